@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs for the draft -> schedule -> verify path.
+
+This module is the only code the HIP path and the CPU oracle's tests share: it draws random
+inputs and holds none of the method's arithmetic.  Everything is numpy (PCG64), seeded per
+config, per operand and per request, so any subset of requests can be regenerated on its
+own, bit for bit.
+
+The shapes and value laws are the five workloads the path is exercised on (the pages
+measure on public benchmarks with trained models; these synthetic tensors stand in for the
+backbone's outputs U_k, h_k, the head's weights and the target model):
+
+  c1  tiny Markov cycle, fp32     R=4   gamma=4  V=1024   r=16  d=64
+  c2  Markov mid-size, bf16       R=64  gamma=8  V=32000  r=256 d=2560
+  c3  Markov headline, bf16       R=256 gamma=8  V=151936 r=256 d=4096
+  c4  scheduler stress, bf16      R=512 gamma=16 V=151936 r=256 d=5120
+  c5  RNN head + async scheduler  R=256 gamma=16 V=129280 r=256 d=4096
+
+bf16 operands are produced as uint16 bit patterns rounded once, to nearest-even, from the
+float32 draw; both sides read exactly those bits.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------------------
+# bf16 helpers (encoding only)
+# --------------------------------------------------------------------------------------
+def bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); returns uint16 bit patterns."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    b = f.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """Widen uint16 bf16 bit patterns to float32 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+# --------------------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    seed: int
+    R: int
+    gamma: int
+    V: int
+    r: int
+    d: int
+    dtype: str             # "f32" or "bf16"
+    head: str              # "markov" or "rnn"
+    u_law: str             # "normal", "zipf", "mixed"
+    u_scale: float         # std of U for "normal"
+    weight_std: float | None  # W1, W2 (and W_gco) std; None = 1/sqrt(r) (W_gco: 1/sqrt(2r+d))
+    h_std: float
+    w_std: float | None    # confidence weights std; None = sqrt(1/(d+r))
+    target_noise: float    # std of the target's deviation from the draft logits
+    sps_kind: str          # "c1", "smooth", "staircase"
+    sps_alpha: float
+    sps_B0: int
+    sps_B1: int            # inclusive
+    sched_mode: int        # 0 sync+break, 1 global, 2 async lag-2
+
+    @property
+    def is_bf16(self) -> bool:
+        return self.dtype == "bf16"
+
+
+CONFIGS = {
+    "c1": Config("c1", 1, 4, 4, 1024, 16, 64, "f32", "markov", "normal", 1.5, 0.1, 1.0, 0.05,
+                 0.5, "smooth", 0.02, 1, 20, 0),
+    "c2": Config("c2", 2, 64, 8, 32000, 256, 2560, "bf16", "markov", "normal", 2.0, None, 1.0,
+                 None, 0.7, "smooth", 0.004, 64, 576, 0),
+    "c3": Config("c3", 3, 256, 8, 151936, 256, 4096, "bf16", "markov", "zipf", 1.0, None, 1.0,
+                 None, 0.6, "smooth", 0.002, 256, 2304, 0),
+    "c4": Config("c4", 4, 512, 16, 151936, 256, 5120, "bf16", "markov", "mixed", 1.0, None,
+                 1.0, None, 0.0, "staircase", 0.0005, 512, 8704, 1),
+    "c5": Config("c5", 5, 256, 16, 129280, 256, 4096, "bf16", "rnn", "zipf", 1.0, None, 1.0,
+                 None, 0.6, "staircase", 0.0005, 256, 4352, 2),
+}
+
+
+def scaled(cfg: Config, **kw) -> Config:
+    """The same value laws at other sizes (tests use small and ragged shapes)."""
+    return dataclasses.replace(cfg, **kw)
+
+
+def _rng(*key) -> np.random.Generator:
+    return np.random.default_rng([int(k) for k in key])
+
+
+def _encode(cfg: Config, x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return bf16_bits(x) if cfg.is_bf16 else x
+
+
+def _wstd(cfg: Config) -> float:
+    return cfg.weight_std if cfg.weight_std is not None else 1.0 / math.sqrt(cfg.r)
+
+
+def _u_row_law(cfg: Config, req: int):
+    """(kind, scale) of request req's U rows; "mixed" interleaves two regimes."""
+    if cfg.u_law == "mixed":
+        return ("normal", 4.0) if req % 2 == 0 else ("normal", 1.0)
+    return (cfg.u_law, cfg.u_scale)
+
+
+def _u_rows(cfg: Config, rng: np.random.Generator, req: int, n: int) -> np.ndarray:
+    kind, scale = _u_row_law(cfg, req)
+    if kind == "zipf":
+        # Zipf(1.1)-ranked logits: -1.1 ln(rank), ranks a fresh random permutation per row
+        base = (-1.1 * np.log(np.arange(1, cfg.V + 1, dtype=np.float64))).astype(np.float32)
+        out = np.empty((n, cfg.V), np.float32)
+        for i in range(n):
+            out[i] = base[rng.permutation(cfg.V)]
+        out += rng.standard_normal((n, cfg.V), dtype=np.float32)
+        return out
+    return rng.standard_normal((n, cfg.V), dtype=np.float32) * np.float32(scale)
+
+
+def anchors(cfg: Config) -> np.ndarray:
+    return _rng(cfg.seed, 0).integers(0, cfg.V, cfg.R).astype(np.int32)
+
+
+def U_rows(cfg: Config, reqs) -> np.ndarray:
+    """U[reqs] as [len(reqs)][gamma][V] (encoded)."""
+    out = [_u_rows(cfg, _rng(cfg.seed, 1, q), q, cfg.gamma) for q in reqs]
+    return _encode(cfg, np.stack(out) if out else np.zeros((0, cfg.gamma, cfg.V), np.float32))
+
+
+def h_rows(cfg: Config, reqs) -> np.ndarray:
+    out = [_rng(cfg.seed, 2, q).standard_normal((cfg.gamma, cfg.d), dtype=np.float32)
+           * np.float32(cfg.h_std) for q in reqs]
+    return _encode(cfg, np.stack(out) if out else np.zeros((0, cfg.gamma, cfg.d), np.float32))
+
+
+def weights(cfg: Config) -> dict:
+    """W1 [V][r], W2 [r][V] (the pages' layout), w [d+r] fp32, W_gco [3r][2r+d] (rnn)."""
+    s = np.float32(_wstd(cfg))
+    W1 = _rng(cfg.seed, 3).standard_normal((cfg.V, cfg.r), dtype=np.float32) * s
+    W2 = _rng(cfg.seed, 4).standard_normal((cfg.r, cfg.V), dtype=np.float32) * s
+    wstd = cfg.w_std if cfg.w_std is not None else math.sqrt(1.0 / (cfg.d + cfg.r))
+    w = _rng(cfg.seed, 5).standard_normal(cfg.d + cfg.r, dtype=np.float32) * np.float32(wstd)
+    out = dict(W1=_encode(cfg, W1), W2=_encode(cfg, W2), w=w)
+    if cfg.head == "rnn":
+        K = 2 * cfg.r + cfg.d
+        gs = np.float32(cfg.weight_std if cfg.weight_std is not None else 1.0 / math.sqrt(K))
+        out["W_gco"] = _encode(cfg, _rng(cfg.seed, 6).standard_normal((3 * cfg.r, K),
+                                                                      dtype=np.float32) * gs)
+    return out
+
+
+def sps_table(cfg: Config) -> np.ndarray:
+    """SPS(B) for B = sps_B0 .. sps_B1 (float32): engine steps/s against verify batch."""
+    B = np.arange(cfg.sps_B0, cfg.sps_B1 + 1, dtype=np.float64)
+    if cfg.sps_kind == "staircase":
+        v = 1.0 / (1.0 + cfg.sps_alpha * B + 0.02 * np.floor((B + 64) / 128))
+    else:
+        v = 1.0 / (1.0 + cfg.sps_alpha * B)
+    return v.astype(np.float32)
+
+
+def inputs(cfg: Config) -> dict:
+    """All draft inputs of a config (numpy, encoded)."""
+    reqs = range(cfg.R)
+    out = dict(U=U_rows(cfg, reqs), h=h_rows(cfg, reqs), x0=anchors(cfg), sps=sps_table(cfg))
+    out.update(weights(cfg))
+    return out
+
+
+def target_noise_std(cfg: Config, req: int) -> float:
+    if cfg.u_law == "mixed":
+        return 0.3 if req % 2 == 0 else 1.0
+    return cfg.target_noise
+
+
+def target_parts(cfg: Config, reqs, cycle: int):
+    """Pieces of the synthetic target-model stand-in for one cycle.
+
+    Returns (noise [n][gamma+1][V] float32, fresh [n][V] float32): target row j (1..gamma)
+    is the draft's logits at position j plus noise[:, j-1]; the bonus row gamma+1 is
+    fresh + noise[:, gamma] (a new U-law row, no head bias).  The caller adds and encodes.
+    """
+    noise, fresh = [], []
+    for q in reqs:
+        g = _rng(cfg.seed, 10, cycle, q)
+        noise.append(g.standard_normal((cfg.gamma + 1, cfg.V), dtype=np.float32)
+                     * np.float32(target_noise_std(cfg, q)))
+        fresh.append(_u_rows(cfg, _rng(cfg.seed, 11, cycle, q), q, 1)[0])
+    n = len(noise)
+    return (np.stack(noise) if n else np.zeros((0, cfg.gamma + 1, cfg.V), np.float32),
+            np.stack(fresh) if n else np.zeros((0, cfg.V), np.float32))
+
+
+def encode(cfg: Config, x) -> np.ndarray:
+    """Encode float values in the config's operand type (bf16 bits or float32)."""
+    return _encode(cfg, x)
+
+
+def decode(cfg: Config, a) -> np.ndarray:
+    """Operand values as float32 (bf16 widened exactly)."""
+    return bf16_to_f32(a) if cfg.is_bf16 else np.ascontiguousarray(a, dtype=np.float32)

@@ -1,0 +1,228 @@
+"""Python access to the plain CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU-baseline leg
+may import this package; the HIP library and its binding never do.  It shares no code with
+the GPU path.  Arrays are numpy; bf16 operands are passed as their uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+SYNC_BREAK, GLOBAL, ASYNC_LAG2 = 0, 1, 2
+S_DRAFT_BLK, S_DRAFT_IN, S_ACCEPT, S_RESID_BLK, S_RESID_IN, S_BONUS_BLK, S_BONUS_IN = range(7)
+VB = 64
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (fp64, IEEE, OpenMP over requests)."""
+    subprocess.check_call(
+        ["gcc", "-O2", "-std=c99", "-Wall", "-fopenmp", "-fPIC", "-shared", "oracle.c",
+         "-o", "liboracle.so", "-lm"], cwd=_HERE)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = C.CDLL(_LIB_PATH)
+        vp, i32p, f32p, f64p, i64p = (C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_float),
+                                      C.POINTER(C.c_double), C.POINTER(C.c_int64))
+        u32p = C.POINTER(C.c_uint32)
+        L.ora_philox4x32_10.argtypes = [u32p, u32p, u32p]
+        L.ora_rand_word.argtypes = [C.c_uint64, C.c_uint64, C.c_int, C.c_uint32, C.c_uint32,
+                                    C.c_uint32]
+        L.ora_rand_word.restype = C.c_uint32
+        for f in (L.ora_uniform, L.ora_gumbel):
+            f.argtypes = L.ora_rand_word.argtypes
+            f.restype = C.c_double
+        L.ora_sample_two_level.argtypes = [C.c_int, f64p, C.c_uint64, C.c_uint64, C.c_int,
+                                           C.c_int, C.c_uint32, C.c_uint32, f64p, f64p]
+        L.ora_sample_two_level.restype = C.c_int
+        L.ora_sample_trials.argtypes = [C.c_int, f64p, C.c_uint64, C.c_uint64, C.c_int,
+                                        C.c_int, C.c_long, i64p]
+        common = [C.c_int] * 6 + [vp, vp, vp, vp]
+        outs = [i32p, f64p, f64p, f64p, f64p, f64p, f64p]
+        L.ora_draft_markov.argtypes = common + [f32p, i32p, C.c_uint64, C.c_uint64] + outs
+        L.ora_draft_rnn.argtypes = common + [vp, f32p, i32p, C.c_uint64, C.c_uint64] + outs
+        L.ora_draft_markov.restype = L.ora_draft_rnn.restype = C.c_int
+        L.ora_schedule.argtypes = [C.c_int, C.c_int, f32p, f32p, C.c_int, f32p, C.c_int,
+                                   C.c_int, C.c_int, i32p, f32p, f64p, f64p]
+        L.ora_schedule.restype = C.c_int
+        L.ora_verify.argtypes = ([C.c_int] * 5 + [vp, vp, vp, f64p, i32p, i32p, C.c_uint64,
+                                 C.c_uint64, i32p, i32p, f64p, f64p, f64p, f64p, f64p])
+        L.ora_verify.restype = C.c_int
+        L.ora_num_threads.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a, ct):
+    return None if a is None else a.ctypes.data_as(C.POINTER(ct))
+
+
+def _vp(a):
+    return None if a is None else C.c_void_p(a.ctypes.data)
+
+
+def _dt_of(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError(f"operand dtype must be uint16 (bf16 bits) or float32, got {a.dtype}")
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return lib().ora_num_threads()
+
+
+def philox(ctr, key) -> np.ndarray:
+    c = _c(ctr, np.uint32)
+    k = _c(key, np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().ora_philox4x32_10(_p(c, C.c_uint32), _p(k, C.c_uint32), _p(out, C.c_uint32))
+    return out
+
+
+def rand_word(seed, cycle, stream, r, k, i) -> int:
+    return int(lib().ora_rand_word(seed, cycle, stream, r, k, i))
+
+
+def uniform(seed, cycle, stream, r, k, i) -> float:
+    return float(lib().ora_uniform(seed, cycle, stream, r, k, i))
+
+
+def gumbel(seed, cycle, stream, r, k, i) -> float:
+    return float(lib().ora_gumbel(seed, cycle, stream, r, k, i))
+
+
+def sample_two_level(l, seed, cycle, stream_blk, stream_in, r, k):
+    l = _c(l, np.float64)
+    gb, gi = C.c_double(), C.c_double()
+    x = lib().ora_sample_two_level(l.size, _p(l, C.c_double), seed, cycle, stream_blk,
+                                   stream_in, r, k, C.byref(gb), C.byref(gi))
+    return x, gb.value, gi.value
+
+
+def sample_trials(l, seed, cycle, stream_blk, stream_in, ntrials) -> np.ndarray:
+    l = _c(l, np.float64)
+    counts = np.zeros(l.size, np.int64)
+    lib().ora_sample_trials(l.size, _p(l, C.c_double), seed, cycle, stream_blk, stream_in,
+                            ntrials, _p(counts, C.c_int64))
+    return counts
+
+
+def _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=None):
+    U, h, W1, W2 = (np.ascontiguousarray(a) for a in (U, h, W1, W2))
+    dt = _dt_of(U)
+    for a in (h, W1, W2) + ((W_gco,) if W_gco is not None else ()):
+        if _dt_of(a) != dt:
+            raise TypeError("all big operands must share one dtype")
+    R, gamma, V = U.shape
+    rank = W1.shape[1]
+    d = h.shape[2]
+    assert W1.shape == (V, rank) and W2.shape == (rank, V) and h.shape[:2] == (R, gamma)
+    w = _c(w, np.float32)
+    assert w.shape == (d + rank,)
+    x0 = _c(x0, np.int32)
+    x = np.zeros((R, gamma), np.int32)
+    c, lse, logit_x, gb, gi = (np.zeros((R, gamma)) for _ in range(5))
+    bias_rows = np.zeros((R, gamma, rank))
+    args = [R, gamma, V, rank, d, dt, _vp(U), _vp(h), _vp(W1), _vp(W2)]
+    tail = [_p(w, C.c_float), _p(x0, C.c_int32), seed, cycle, _p(x, C.c_int32),
+            _p(c, C.c_double), _p(lse, C.c_double), _p(logit_x, C.c_double),
+            _p(bias_rows, C.c_double), _p(gb, C.c_double), _p(gi, C.c_double)]
+    if W_gco is None:
+        rc = lib().ora_draft_markov(*args, *tail)
+    else:
+        W_gco = np.ascontiguousarray(W_gco)
+        assert W_gco.shape == (3 * rank, 2 * rank + d)
+        rc = lib().ora_draft_rnn(*args, _vp(W_gco), *tail)
+    if rc != 0:
+        raise ValueError(f"oracle draft rejected its arguments (rc={rc})")
+    return dict(x=x, c=c, lse=lse, logit_x=logit_x, bias_rows=bias_rows, gap_blk=gb,
+                gap_in=gi)
+
+
+def draft_markov(U, h, W1, W2, w, x0, seed=0, cycle=0):
+    """Markov-head draft (eqs. 4, 5, 7).  W2 is [rank][V] as on the pages."""
+    return _draft(U, h, W1, W2, w, x0, seed, cycle)
+
+
+def draft_rnn(U, h, W1, W2, W_gco, w, x0, seed=0, cycle=0):
+    """RNN-head draft (eq. 6, confidence eq. 7)."""
+    return _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=W_gco)
+
+
+def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, trace=False):
+    """Prefix scheduler.  Returns dict(ell, a, stats=(B, tau, Theta, n_adm), theta)."""
+    c = _c(c, np.float32)
+    R, gamma = c.shape
+    sps = _c(sps, np.float32)
+    cl = None if c_lag is None else _c(c_lag, np.float32)
+    R_lag = 0 if cl is None else cl.shape[0]
+    ell = np.zeros(R, np.int32)
+    a = np.zeros((R, gamma), np.float32)
+    stats = np.zeros(4)
+    theta = np.zeros(R * gamma + 1) if trace else None
+    rc = lib().ora_schedule(R, gamma, _p(c, C.c_float), _p(cl, C.c_float), R_lag,
+                            _p(sps, C.c_float), sps_B0, sps.size, mode, _p(ell, C.c_int32),
+                            _p(a, C.c_float), _p(stats, C.c_double), _p(theta, C.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle schedule rejected its arguments (rc={rc})")
+    return dict(ell=ell, a=a, stats=stats, theta=theta)
+
+
+def schedule_rc(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None) -> int:
+    """Return code only (error-path tests)."""
+    c = _c(c, np.float32)
+    R, gamma = c.shape
+    sps = _c(sps, np.float32)
+    cl = None if c_lag is None else _c(c_lag, np.float32)
+    ell = np.zeros(R, np.int32)
+    return lib().ora_schedule(R, gamma, _p(c, C.c_float), _p(cl, C.c_float),
+                              0 if cl is None else cl.shape[0], _p(sps, C.c_float), sps_B0,
+                              sps.size, mode, _p(ell, C.c_int32), None, None, None)
+
+
+def verify(target, U, W2, bias_rows, x, ell, seed=0, cycle=0):
+    """Rejection-sampling verification (returns dict of n_acc, y, c_star, ...)."""
+    target, U, W2 = (np.ascontiguousarray(a) for a in (target, U, W2))
+    dt = _dt_of(U)
+    if _dt_of(target) != dt or _dt_of(W2) != dt:
+        raise TypeError("target, U and W2 must share one dtype")
+    R, gamma, V = U.shape
+    rank = W2.shape[0]
+    assert target.shape == (R, gamma + 1, V) and W2.shape == (rank, V)
+    bias_rows = _c(bias_rows, np.float64)
+    assert bias_rows.shape == (R, gamma, rank)
+    x = _c(x, np.int32)
+    ell = _c(ell, np.int32)
+    n_acc = np.zeros(R, np.int32)
+    y = np.zeros((R, gamma + 1), np.int32)
+    c_star, pq, ua = (np.zeros((R, gamma)) for _ in range(3))
+    gb, gi = np.zeros(R), np.zeros(R)
+    rc = lib().ora_verify(R, gamma, V, rank, dt, _vp(target), _vp(U), _vp(W2),
+                          _p(bias_rows, C.c_double), _p(x, C.c_int32), _p(ell, C.c_int32),
+                          seed, cycle, _p(n_acc, C.c_int32), _p(y, C.c_int32),
+                          _p(c_star, C.c_double), _p(pq, C.c_double), _p(ua, C.c_double),
+                          _p(gb, C.c_double), _p(gi, C.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle verify rejected its arguments (rc={rc})")
+    return dict(n_acc=n_acc, y=y, c_star=c_star, pq_ratio=pq, u_acc=ua, gap_blk=gb,
+                gap_in=gi)
