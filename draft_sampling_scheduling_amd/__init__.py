@@ -1,0 +1,246 @@
+"""DSpark draft -> schedule -> verify hot path on MI355X: Python binding of libdspark.so.
+
+Thin ctypes layer over the C ABI in include/dspark.h: it checks shapes and dtypes,
+allocates outputs and workspaces with PyTorch (device memory only) and passes raw device
+pointers plus torch's current HIP stream.  Every step of the path runs in the library's
+HIP kernels; there is no fallback: if the library is missing the calls raise.
+
+Operand dtypes: torch.bfloat16 or torch.float32 for U, h, W1, W2t, W_gco and the target
+logits (all of one call share one dtype); float32 for w and the confidences; int32 tokens.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdspark.so")
+
+F32, BF16 = 0, 1
+SYNC_BREAK, GLOBAL, ASYNC_LAG2 = 0, 1, 2
+OK, EINVAL, ERANGE, EWORKSPACE, EDEVICE = 0, -1, -2, -3, -4
+FAULT_TOKEN, FAULT_CONF, FAULT_LEN = 1, 2, 4
+EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov",
+           "dspark_draft_rnn_workspace_bytes", "dspark_draft_rnn",
+           "dspark_schedule_workspace_bytes", "dspark_schedule",
+           "dspark_verify_workspace_bytes", "dspark_verify", "dspark_version")
+
+_lib = None
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, fn: str, rc: int):
+        names = {EINVAL: "EINVAL", ERANGE: "ERANGE", EWORKSPACE: "EWORKSPACE",
+                 EDEVICE: "EDEVICE"}
+        super().__init__(f"{fn} returned {names.get(rc, rc)}")
+        self.rc = rc
+
+
+def lib():
+    """Load libdspark.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python __graft_entry__.py` "
+                               "(or draft_sampling_scheduling_amd.build.build())")
+        L = C.CDLL(LIB_PATH)
+        i, u64, sz, vp = C.c_int, C.c_uint64, C.c_size_t, C.c_void_p
+        L.dspark_draft_workspace_bytes.argtypes = [i] * 5
+        L.dspark_draft_workspace_bytes.restype = sz
+        L.dspark_draft_rnn_workspace_bytes.argtypes = [i] * 5
+        L.dspark_draft_rnn_workspace_bytes.restype = sz
+        L.dspark_draft_markov.argtypes = ([i] * 6 + [vp] * 6 + [u64, u64] + [vp] * 6 +
+                                          [vp, sz, vp])
+        L.dspark_draft_markov.restype = i
+        L.dspark_draft_rnn.argtypes = ([i] * 6 + [vp] * 7 + [u64, u64] + [vp] * 6 +
+                                       [vp, sz, vp])
+        L.dspark_draft_rnn.restype = i
+        L.dspark_schedule_workspace_bytes.argtypes = [i, i]
+        L.dspark_schedule_workspace_bytes.restype = sz
+        L.dspark_schedule.argtypes = [i, i, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+        L.dspark_schedule.restype = i
+        L.dspark_verify_workspace_bytes.argtypes = [i] * 4
+        L.dspark_verify_workspace_bytes.restype = sz
+        L.dspark_verify.argtypes = ([i] * 5 + [vp] * 4 + [i] + [vp] * 4 + [u64, u64] +
+                                    [vp] * 4 + [vp, sz, vp])
+        L.dspark_verify.restype = i
+        L.dspark_version.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def version() -> str:
+    return lib().dspark_version().decode()
+
+
+# ----------------------------------------------------------------------------------------
+# torch plumbing
+# ----------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"operand dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _chk(t, name, shape=None, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _ws(nbytes: int, device, ws=None):
+    torch = _torch()
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return ws
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _raise(fn, rc):
+    if rc != OK:
+        raise DsparkError(fn, rc)
+
+
+# ----------------------------------------------------------------------------------------
+# entry points (same names as the C ABI without the prefix)
+# ----------------------------------------------------------------------------------------
+def draft_workspace_bytes(R, gamma, V, r, d) -> int:
+    return int(lib().dspark_draft_workspace_bytes(R, gamma, V, r, d))
+
+
+def draft_rnn_workspace_bytes(R, gamma, V, r, d) -> int:
+    return int(lib().dspark_draft_rnn_workspace_bytes(R, gamma, V, r, d))
+
+
+def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, out=None, ws=None, status=None):
+    torch = _torch()
+    _chk(U, "U")
+    R, gamma, V = U.shape
+    dt = _dt(U)
+    r = W1.shape[1]
+    d = h.shape[2]
+    _chk(h, "h", (R, gamma, d), U.dtype)
+    _chk(W1, "W1", (V, r), U.dtype)
+    _chk(W2t, "W2t", (V, r), U.dtype)
+    _chk(w, "w", (d + r,), torch.float32)
+    _chk(x0, "x0", (R,), torch.int32)
+    if rnn:
+        _chk(W_gco, "W_gco", (3 * r, 2 * r + d), U.dtype)
+    dev = U.device
+    if out is None:
+        out = dict(
+            x=torch.empty((R, gamma), dtype=torch.int32, device=dev),
+            c=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+            lse=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+            logit_x=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+            bias_rows=torch.empty((R, gamma, r), dtype=torch.float32 if rnn else U.dtype,
+                                  device=dev))
+    nbytes = (draft_rnn_workspace_bytes if rnn else draft_workspace_bytes)(R, gamma, V, r, d)
+    if nbytes == 0 and R > 0:
+        raise DsparkError("dspark_draft_workspace_bytes", EINVAL)
+    ws = _ws(nbytes, dev, ws)
+    args = [R, gamma, V, r, d, dt, _p(U), _p(h), _p(W1), _p(W2t)]
+    if rnn:
+        args.append(_p(W_gco))
+    args += [_p(w), _p(x0), seed, cycle, _p(out["x"]), _p(out["c"]), _p(out["lse"]),
+             _p(out["logit_x"]), _p(out["bias_rows"]), _p(status), _p(ws),
+             ws.numel() * ws.element_size(), _stream()]
+    fn = "dspark_draft_rnn" if rnn else "dspark_draft_markov"
+    _raise(fn, getattr(lib(), fn)(*args))
+    return out
+
+
+def draft_markov(U, h, W1, W2t, w, x0, seed=0, cycle=0, *, out=None, ws=None, status=None):
+    """Markov-head draft; returns dict(x, c, lse, logit_x, bias_rows) (device tensors)."""
+    return _draft(False, U, h, W1, W2t, w, x0, seed, cycle, out=out, ws=ws, status=status)
+
+
+def draft_rnn(U, h, W1, W2t, W_gco, w, x0, seed=0, cycle=0, *, out=None, ws=None, status=None):
+    """RNN-head draft; bias_rows is float32."""
+    return _draft(True, U, h, W1, W2t, w, x0, seed, cycle, W_gco=W_gco, out=out, ws=ws,
+                  status=status)
+
+
+def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, *, out=None, status=None):
+    """Prefix scheduler; returns dict(ell, a, stats) (device tensors)."""
+    torch = _torch()
+    _chk(c, "c", dtype=torch.float32)
+    R, gamma = c.shape
+    _chk(sps, "sps", dtype=torch.float32)
+    R_lag = 0
+    if c_lag is not None:
+        _chk(c_lag, "c_lag", dtype=torch.float32)
+        R_lag = c_lag.shape[0]
+    dev = c.device
+    if out is None:
+        out = dict(ell=torch.empty(R, dtype=torch.int32, device=dev),
+                   a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+                   stats=torch.empty(4, dtype=torch.float64, device=dev))
+    rc = lib().dspark_schedule(R, gamma, _p(c), _p(c_lag), R_lag, _p(sps), sps_B0,
+                               sps.numel(), mode, _p(out["ell"]), _p(out["a"]),
+                               _p(out["stats"]), _p(status), None, 0, _stream())
+    _raise("dspark_schedule", rc)
+    return out
+
+
+def verify_workspace_bytes(R, gamma, V, r) -> int:
+    return int(lib().dspark_verify_workspace_bytes(R, gamma, V, r))
+
+
+def verify(target, U, W2t, bias_rows, x, lse, logit_x, ell, seed=0, cycle=0, *, out=None,
+           ws=None, status=None):
+    """Verification; returns dict(n_acc, y, c_star) (device tensors)."""
+    torch = _torch()
+    _chk(U, "U")
+    R, gamma, V = U.shape
+    dt = _dt(U)
+    r = W2t.shape[1]
+    _chk(target, "target", (R, gamma + 1, V), U.dtype)
+    _chk(W2t, "W2t", (V, r), U.dtype)
+    _chk(bias_rows, "bias_rows", (R, gamma, r))
+    bdt = _dt(bias_rows)
+    _chk(x, "x", (R, gamma), torch.int32)
+    _chk(lse, "lse", (R, gamma), torch.float32)
+    _chk(logit_x, "logit_x", (R, gamma), torch.float32)
+    _chk(ell, "ell", (R,), torch.int32)
+    dev = U.device
+    if out is None:
+        out = dict(n_acc=torch.empty(R, dtype=torch.int32, device=dev),
+                   y=torch.empty((R, gamma + 1), dtype=torch.int32, device=dev),
+                   c_star=torch.empty((R, gamma), dtype=torch.float32, device=dev))
+    nbytes = verify_workspace_bytes(R, gamma, V, r)
+    if nbytes == 0 and R > 0:
+        raise DsparkError("dspark_verify_workspace_bytes", EINVAL)
+    ws = _ws(nbytes, dev, ws)
+    rc = lib().dspark_verify(R, gamma, V, r, dt, _p(target), _p(U), _p(W2t), _p(bias_rows),
+                             bdt, _p(x), _p(lse), _p(logit_x), _p(ell), seed, cycle,
+                             _p(out["n_acc"]), _p(out["y"]), _p(out["c_star"]), _p(status),
+                             _p(ws), ws.numel() * ws.element_size(), _stream())
+    _raise("dspark_verify", rc)
+    return out

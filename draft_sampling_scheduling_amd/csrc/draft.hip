@@ -1,0 +1,591 @@
+// draft.hip -- the sequential block's draft loop (Markov head eq. (5), RNN head eq. (6)),
+// the confidence head (eq. (7)) and the two-level Gumbel-max sampler.
+//
+// One draft position k costs two launches:
+//   sweep   (matrix cores, see sweep.h): per request and per vocabulary range, the running
+//           normaliser (max, sum exp) of l = U_k + bias_k and the best block score
+//           LSE_b + g_b of the sampler's first level;
+//   combine (one wave per request): merge the ranges, take the winning block, recompute its
+//           64 logits, draw x_k inside it (second level), and write lse, l(x_k), c_k and
+//           the bias row.
+// The position-independent half of the confidence, w_h . h_k, is computed for all k by one
+// launch up front; the RNN head adds one state-update launch per position and one
+// h-projection launch up front.
+#include "dev.h"
+#include "host.h"
+#include "sweep.h"
+
+namespace dspark {
+
+// ---------------------------------------------------------------------------------------
+// w_h . h_k for every (request, position): one wave per row of h
+// ---------------------------------------------------------------------------------------
+template <class T>
+__global__ void __launch_bounds__(256) conf_h_kernel(int rows, int d, const T* __restrict__ h,
+                                                     const float* __restrict__ w,
+                                                     float* __restrict__ zh) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const T* hr = h + (size_t)row * d;
+  float acc = 0.0f;
+  for (int i = lane * 8; i < d; i += 64 * 8) {
+    float x[8];
+    ld8<T>(hr + i, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = fmaf(w[i + j], x[j], acc);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) zh[row] = acc;
+}
+
+// ---------------------------------------------------------------------------------------
+// sweep epilogue of a draft step
+// ---------------------------------------------------------------------------------------
+struct DraftSweepParams {
+  const uint16_t* U;     // U + (k-1)*V; row q at U + q*ustride  (bf16)
+  size_t ustride;        // gamma * V
+  int V, R;
+  const int32_t* prev;   // x_{k-1} of row q at prev[q * prev_stride]
+  int prev_stride;
+  const uint16_t* W1;    // Markov B rows: W1[x_{k-1}]
+  const float* orow;     // RNN B rows: tanh(W_o z_k), [R][r] float
+  int r;
+  uint32_t k;            // position, 1-based
+  uint64_t seed, cycle;
+  float4* partials;      // [R][nranges]: (max, sum exp, best G, best block)
+  int nranges;
+  int32_t* status;
+};
+
+template <bool RNN>
+struct DraftEpi {
+  using Params = DraftSweepParams;
+  struct State {
+    float M, S, G;
+    int B;
+    int grp;
+    uint4 words;
+  };
+  struct Pre {
+    uint4 u[2][2][2];  // [nt][mt][chunk]
+  };
+  __device__ static bool group_live(const Params& p, int row0) { return row0 < p.R; }
+  __device__ static int nrows(const Params& p) { return p.R; }
+  __device__ static const void* brow(const Params& p, int row) {
+    if (RNN) return p.orow + (size_t)row * p.r;
+    const int32_t t = checked_token(p.prev[(size_t)row * p.prev_stride], p.V, p.status);
+    return p.W1 + (size_t)t * p.r;
+  }
+  __device__ static void init(const Params&, State& s, int) {
+    s.M = -INFINITY;
+    s.S = 0.0f;
+    s.G = -INFINITY;
+    s.B = 0x7fffffff;
+    s.grp = -1;
+    s.words = make_uint4(0, 0, 0, 0);
+  }
+  template <int NT>
+  __device__ static void prefetch(const Params& p, Pre& pre, int b, int rowbase) {
+    const int lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int row = rowbase + 32 * nt + n;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int v = b * kVB + 32 * mt + 16 * h;
+        const bool ok = row < p.R && v < p.V;
+        const uint16_t* src = p.U + (size_t)row * p.ustride + v;
+        pre.u[nt][mt][0] = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+        pre.u[nt][mt][1] =
+            (ok && v + 8 < p.V) ? *reinterpret_cast<const uint4*>(src + 8) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  template <int NT>
+  __device__ static void block(const Params& p, State& s, const Pre& pre,
+                               const f32x16 (&acc)[NT][2], int b, int rowbase, int myrow) {
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    float mb[NT], sb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float l[32];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int v0 = b * kVB + 32 * mt + 16 * h;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint4 u = pre.u[nt][mt][c];
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = 8 * c + e;
+            const float uv = (e & 1) ? bf16hi(w4[e >> 1]) : bf16lo(w4[e >> 1]);
+            l[16 * mt + j] = (v0 + j < p.V) ? acc[nt][mt][j] + uv : -INFINITY;
+          }
+        }
+      }
+      float m = l[0];
+#pragma unroll
+      for (int j = 1; j < 32; ++j) m = fmaxf(m, l[j]);
+      float sum = 0.0f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) sum += __expf(l[j] - m);
+      }
+      const float m2 = __shfl_xor(m, 32, kWave);
+      const float s2 = __shfl_xor(sum, 32, kWave);
+      lse_merge(m, sum, m2, s2);
+      mb[nt] = m;
+      sb[nt] = sum;
+    }
+    if (myrow < 0 || myrow >= p.R) return;
+    const int mine = (NT == 2) ? h : 0;
+    const float m = mb[mine], sum = sb[mine];
+    lse_merge(s.M, s.S, m, sum);
+    const float lse_b = m + __logf(sum);
+    const int grp = b >> 2;
+    if (grp != s.grp) {
+      s.grp = grp;
+      s.words = Rng(p.seed, p.cycle).block(kStreamDraftBlk, (uint32_t)myrow, p.k, (uint32_t)grp);
+    }
+    const float G = lse_b + gumbel_of(pick_word(s.words, (uint32_t)b & 3u));
+    if (G > s.G) {
+      s.G = G;
+      s.B = b;
+    }
+  }
+  __device__ static void finish(const Params& p, const State& s, int myrow, int range) {
+    if (myrow < 0 || myrow >= p.R) return;
+    p.partials[(size_t)myrow * p.nranges + range] = make_float4(s.M, s.S, s.G, __int_as_float(s.B));
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// the same step for float operands: plain VALU, one wave per (request, range); lane = id
+// inside a 64-id block.  Used by the float workload only.
+// ---------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) draft_sweep_f32_kernel(
+    int R, int V, int r, const float* __restrict__ U, size_t ustride, const int32_t* prev,
+    int prev_stride, const float* __restrict__ W1, const float* __restrict__ orow,
+    const float* __restrict__ W2t, uint32_t k, uint64_t seed, uint64_t cycle, float4* partials,
+    int nranges, int nblocks, int32_t* status) {
+  const int q = blockIdx.y, range = blockIdx.x, lane = threadIdx.x;
+  const int per = (nblocks + nranges - 1) / nranges;
+  const int b0 = range * per, b1 = min(nblocks, b0 + per);
+  const float* e;
+  if (orow) {
+    e = orow + (size_t)q * r;
+  } else {
+    const int32_t t = checked_token(prev[(size_t)q * prev_stride], V, status);
+    e = W1 + (size_t)t * r;
+  }
+  const Rng rng(seed, cycle);
+  float M = -INFINITY, S = 0.0f, G = -INFINITY;
+  int Bk = 0x7fffffff;
+  for (int b = b0; b < b1; ++b) {
+    const int v = b * kVB + lane;
+    float l = -INFINITY;
+    if (v < V) {
+      float acc = 0.0f;
+      for (int i = 0; i < r; ++i) acc = fmaf(e[i], W2t[(size_t)v * r + i], acc);
+      l = U[(size_t)q * ustride + v] + acc;
+    }
+    const float m = wave_max(l);
+    const float sum = wave_sum(l == -INFINITY ? 0.0f : __expf(l - m));
+    lse_merge(M, S, m, sum);
+    const float g = gumbel_of(rng.word(kStreamDraftBlk, (uint32_t)q, k, (uint32_t)b));
+    const float Gb = m + __logf(sum) + g;
+    if (Gb > G) {
+      G = Gb;
+      Bk = b;
+    }
+  }
+  if (lane == 0) partials[(size_t)q * nranges + range] = make_float4(M, S, G, __int_as_float(Bk));
+}
+
+// ---------------------------------------------------------------------------------------
+// combine: one wave per request
+// ---------------------------------------------------------------------------------------
+template <class T, bool RNN>
+__global__ void __launch_bounds__(64) draft_combine_kernel(
+    int R, int gamma, int V, int r, int d, const T* __restrict__ U, const T* __restrict__ W1,
+    const T* __restrict__ W2t, const float* __restrict__ w, const float* __restrict__ zh,
+    const int32_t* prev, int prev_stride, const float* __restrict__ orow,
+    const float4* __restrict__ partials, int nranges, uint32_t k, uint64_t seed, uint64_t cycle,
+    int32_t* x, float* c, float* lse, float* logit_x, void* bias_rows, int32_t* status) {
+  const int q = blockIdx.x, lane = threadIdx.x;
+  float M = -INFINITY, S = 0.0f, G = -INFINITY;
+  int Bk = 0x7fffffff;
+  for (int i = lane; i < nranges; i += 64) {
+    const float4 pr = partials[(size_t)q * nranges + i];
+    const int pb = __float_as_int(pr.w);
+    if (pb == 0x7fffffff) continue;
+    lse_merge(M, S, pr.x, pr.y);
+    if (pr.z > G || (pr.z == G && pb < Bk)) {
+      G = pr.z;
+      Bk = pb;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
+    lse_merge(M, S, m2, s2);
+  }
+  wave_argmax(G, Bk);
+  const int nblocks = (V + kVB - 1) / kVB;
+  if (Bk < 0 || Bk >= nblocks) Bk = 0;  // only if every partial was empty (cannot happen)
+  const float row_lse = M + __logf(S);
+
+  const int32_t tprev = checked_token(prev[(size_t)q * prev_stride], V, status);
+  const T* e = W1 + (size_t)tprev * r;
+  const size_t rk = (size_t)q * gamma + (k - 1);
+
+  // second level: recompute the winning block's logits and draw inside it
+  const int v = Bk * kVB + lane;
+  float l = -INFINITY;
+  if (v < V) {
+    float acc = 0.0f;
+    const T* wr = W2t + (size_t)v * r;
+    for (int i = 0; i < r; i += 8) {
+      float a[8], bv[8];
+      ld8<T>(wr + i, a);
+      if (RNN) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] = orow[(size_t)q * r + i + j];
+      } else {
+        ld8<T>(e + i, bv);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = fmaf(bv[j], a[j], acc);
+    }
+    l = ld<T>(U, (size_t)q * gamma * V + (size_t)(k - 1) * V + v) + acc;
+  }
+  const Rng rng(seed, cycle);
+  float score = (v < V) ? l + gumbel_of(rng.word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v))
+                        : -INFINITY;
+  int idx = v;
+  wave_argmax(score, idx);
+  const float lx = __shfl(l, idx - Bk * kVB, kWave);
+
+  // confidence head: sigmoid(w_h . h_k + w_e . W1[x_{k-1}])
+  float ze = 0.0f;
+  for (int i = lane; i < r; i += 64) ze = fmaf(w[d + i], ld<T>(e, i), ze);
+  ze = wave_sum(ze);
+  const float z = zh[rk] + ze;
+
+  if (lane == 0) {
+    x[rk] = idx;
+    c[rk] = 1.0f / (1.0f + __expf(-z));
+    lse[rk] = row_lse;
+    logit_x[rk] = lx;
+  }
+  if (RNN) {
+    float* br = static_cast<float*>(bias_rows) + rk * r;
+    for (int i = lane; i < r; i += 64) br[i] = orow[(size_t)q * r + i];
+  } else {
+    T* br = static_cast<T*>(bias_rows) + rk * r;
+    for (int i = lane; i < r; i += 64) br[i] = e[i];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// RNN head (eq. (6)).  Gh[q][k][o] = sum_i W_gco[o][2r + i] h_k[i] for all k up front;
+// per step: G = W_gco[:, :2r] [s; e] + Gh, gate/candidate/output nonlinearities, s update.
+// ---------------------------------------------------------------------------------------
+// Gh = h W_h^T: [rows][d] x [3r][d]^T -> [rows][3r] fp32.  One wave per 32x32 tile on the
+// matrix cores, fragments straight from global memory (K-contiguous rows on both sides).
+__global__ void __launch_bounds__(64) rnn_hproj_bf16_kernel(int rows, int d, int r3, int ldw,
+                                                            const uint16_t* __restrict__ h,
+                                                            const uint16_t* __restrict__ Wh,
+                                                            float* __restrict__ Gh) {
+  const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;  // m: output unit, n: row
+  const int orow = m0 + n, hrow = n0 + n;
+  f32x16 acc;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+  for (int k0 = 0; k0 < d; k0 += 16) {
+    const bool kin = k0 + 8 * hh < d;  // d % 8 == 0: an 8-wide chunk is wholly in or out
+    const uint4 a = (orow < r3 && kin)
+                        ? *reinterpret_cast<const uint4*>(Wh + (size_t)orow * ldw + k0 + 8 * hh)
+                        : make_uint4(0, 0, 0, 0);
+    const uint4 bq = (hrow < rows && kin)
+                         ? *reinterpret_cast<const uint4*>(h + (size_t)hrow * d + k0 + 8 * hh)
+                         : make_uint4(0, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bq), acc, 0, 0, 0);
+  }
+  // accumulator: row m = 8(j/4) + 4*hh + (j%4) (output unit), column n (h row)
+  if (hrow < rows) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int m = m0 + 8 * (j >> 2) + 4 * hh + (j & 3);
+      if (m < r3) Gh[(size_t)hrow * r3 + m] = acc[j];
+    }
+  }
+}
+
+template <class T>
+__global__ void __launch_bounds__(64) rnn_hproj_f32_kernel(int rows, int d, int r3, int ldw,
+                                                           const T* __restrict__ h,
+                                                           const T* __restrict__ Wh,
+                                                           float* __restrict__ Gh) {
+  const int row = blockIdx.y, o = blockIdx.x * 64 + threadIdx.x;
+  if (row >= rows || o >= r3) return;
+  float acc = 0.0f;
+  for (int i = 0; i < d; ++i) acc = fmaf(ld<T>(Wh, (size_t)o * ldw + i), ld<T>(h, (size_t)row * d + i), acc);
+  Gh[(size_t)row * r3 + o] = acc;
+}
+
+// one workgroup per request: z_se = [s_{k-1}; W1[x_{k-1}]] in LDS, 3r dot products of
+// length 2r, then the nonlinearities.  Writes o_k (float) and s_k in place.
+template <class T>
+__global__ void __launch_bounds__(256) rnn_step_kernel(int R, int gamma, int V, int r, int d,
+                                                       const T* __restrict__ W1,
+                                                       const T* __restrict__ Wg,
+                                                       const float* __restrict__ Gh,
+                                                       const int32_t* prev, int prev_stride,
+                                                       uint32_t k, float* s, float* orow,
+                                                       int32_t* status) {
+  extern __shared__ float zs[];  // [2r] then G [3r]
+  const int q = blockIdx.x;
+  float* G = zs + 2 * r;
+  const int32_t t = checked_token(prev[(size_t)q * prev_stride], V, status);
+  for (int i = threadIdx.x; i < r; i += blockDim.x) {
+    zs[i] = s[(size_t)q * r + i];
+    zs[r + i] = ld<T>(W1, (size_t)t * r + i);
+  }
+  __syncthreads();
+  const int K = 2 * r + d;
+  const float* gh = Gh + ((size_t)q * gamma + (k - 1)) * 3 * r;
+  for (int o = threadIdx.x; o < 3 * r; o += blockDim.x) {
+    float acc = gh[o];
+    const T* wr = Wg + (size_t)o * K;
+    for (int i = 0; i < 2 * r; i += 8) {
+      float a[8];
+      ld8<T>(wr + i, a);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = fmaf(a[j], zs[i + j], acc);
+    }
+    G[o] = acc;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < r; i += blockDim.x) {
+    const float g = 1.0f / (1.0f + expf(-G[i]));
+    const float cand = tanhf(G[r + i]);
+    const float out = tanhf(G[2 * r + i]);
+    orow[(size_t)q * r + i] = out;
+    s[(size_t)q * r + i] = g * zs[i] + (1.0f - g) * cand;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// host
+// ---------------------------------------------------------------------------------------
+static int nranges_for(int V, int ngroups) {
+  const int nblocks = (V + kVB - 1) / kVB;
+  int nr = device_cus() / (ngroups > 0 ? ngroups : 1);
+  if (nr < 1) nr = 1;
+  if (nr > nblocks) nr = nblocks;
+  if (nr > kMaxRanges) nr = kMaxRanges;
+  return nr;
+}
+
+struct DraftWs {
+  float* zh;
+  float4* partials;
+  float* Gh;
+  float* s;
+  float* orow;
+  size_t bytes;
+};
+
+static DraftWs carve_draft(void* ws, int R, int gamma, int V, int r, int d, bool rnn) {
+  Carve cv(ws);
+  DraftWs w{};
+  w.zh = cv.take<float>((size_t)R * gamma);
+  const int nblocks = (V + kVB - 1) / kVB;
+  w.partials = cv.take<float4>((size_t)R * (nblocks < kMaxRanges ? nblocks : kMaxRanges));
+  if (rnn) {
+    w.Gh = cv.take<float>((size_t)R * gamma * 3 * r);
+    w.s = cv.take<float>((size_t)R * r);
+    w.orow = cv.take<float>((size_t)R * r);
+  }
+  (void)d;
+  w.bytes = cv.bytes();
+  return w;
+}
+
+template <class T>
+static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void* U_,
+                     const void* h_, const void* W1_, const void* W2t_, const void* Wg_,
+                     const float* w, const int32_t* x0, uint64_t seed, uint64_t cycle, int32_t* x,
+                     float* c, float* lse, float* logit_x, void* bias_rows, int32_t* status,
+                     const DraftWs& ws, hipStream_t stream) {
+  const T* U = static_cast<const T*>(U_);
+  const T* h = static_cast<const T*>(h_);
+  const T* W1 = static_cast<const T*>(W1_);
+  const T* W2t = static_cast<const T*>(W2t_);
+  const T* Wg = static_cast<const T*>(Wg_);
+  constexpr bool BF = sizeof(T) == 2;
+  const int rows = R * gamma;
+
+  if (d > 0) {
+    conf_h_kernel<T><<<(rows + 3) / 4, 256, 0, stream>>>(rows, d, h, w, ws.zh);
+  } else {
+    fill_kernel<<<(rows + 255) / 256, 256, 0, stream>>>(ws.zh, (size_t)rows, 0.0f);
+  }
+  if (rnn) {
+    const int r3 = 3 * r, K = 2 * r + d;
+    if (d > 0) {
+      if (BF) {
+        dim3 grid((rows + 31) / 32, (r3 + 31) / 32);
+        rnn_hproj_bf16_kernel<<<grid, 64, 0, stream>>>(
+            rows, d, r3, K, reinterpret_cast<const uint16_t*>(h),
+            reinterpret_cast<const uint16_t*>(Wg) + 2 * r, ws.Gh);
+      } else {
+        dim3 grid((r3 + 63) / 64, rows);
+        rnn_hproj_f32_kernel<T><<<grid, 64, 0, stream>>>(rows, d, r3, K, h, Wg + 2 * r, ws.Gh);
+      }
+    } else {
+      const size_t n3 = (size_t)rows * r3;
+      fill_kernel<<<(unsigned)((n3 + 255) / 256), 256, 0, stream>>>(ws.Gh, n3, 0.0f);
+    }
+    fill_kernel<<<(R * r + 255) / 256, 256, 0, stream>>>(ws.s, (size_t)R * r, 0.0f);  // s_0 = 0
+  }
+
+  const int nt = (R > 128) ? 2 : 1;
+  SweepGeom g{};
+  int nranges;
+  if (BF) {
+    const int rows_per_group = (kSweepThreads / kWave) * nt * 32;
+    const int ngroups = (R + rows_per_group - 1) / rows_per_group;
+    g = make_geom(R, V, r, reinterpret_cast<const uint16_t*>(W2t), nt, device_cus());
+    nranges = g.nranges;
+    (void)ngroups;
+  } else {
+    nranges = nranges_for(V, R);
+    if (nranges > 64) nranges = 64;
+  }
+
+  for (int k = 1; k <= gamma; ++k) {
+    const int32_t* prev = (k == 1) ? x0 : x + (k - 2);
+    const int ps = (k == 1) ? 1 : gamma;
+    if (rnn) {
+      const size_t sh = sizeof(float) * 5 * r;
+      rnn_step_kernel<T><<<R, 256, sh, stream>>>(R, gamma, V, r, d, W1, Wg, ws.Gh, prev, ps,
+                                                 (uint32_t)k, ws.s, ws.orow, status);
+    }
+    if (BF) {
+      DraftSweepParams p{};
+      p.U = reinterpret_cast<const uint16_t*>(U) + (size_t)(k - 1) * V;
+      p.ustride = (size_t)gamma * V;
+      p.V = V;
+      p.R = R;
+      p.prev = prev;
+      p.prev_stride = ps;
+      p.W1 = reinterpret_cast<const uint16_t*>(W1);
+      p.orow = ws.orow;
+      p.r = r;
+      p.k = (uint32_t)k;
+      p.seed = seed;
+      p.cycle = cycle;
+      p.partials = ws.partials;
+      p.nranges = nranges;
+      p.status = status;
+      const size_t sh = sweep_lds_bytes(r);
+      const int ntask = g.nranges * g.ngroups;
+      if (rnn) {
+        if (nt == 2)
+          sweep_kernel<2, true, DraftEpi<true>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
+        else
+          sweep_kernel<1, true, DraftEpi<true>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
+      } else {
+        if (nt == 2)
+          sweep_kernel<2, false, DraftEpi<false>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
+        else
+          sweep_kernel<1, false, DraftEpi<false>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
+      }
+    } else {
+      const int nblocks = (V + kVB - 1) / kVB;
+      dim3 grid(nranges, R);
+      draft_sweep_f32_kernel<<<grid, 64, 0, stream>>>(
+          R, V, r, reinterpret_cast<const float*>(U) + (size_t)(k - 1) * V, (size_t)gamma * V,
+          prev, ps, reinterpret_cast<const float*>(W1), rnn ? ws.orow : nullptr,
+          reinterpret_cast<const float*>(W2t), (uint32_t)k, seed, cycle, ws.partials, nranges,
+          nblocks, status);
+    }
+    if (rnn)
+      draft_combine_kernel<T, true><<<R, 64, 0, stream>>>(
+          R, gamma, V, r, d, U, W1, W2t, w, ws.zh, prev, ps, ws.orow, ws.partials, nranges,
+          (uint32_t)k, seed, cycle, x, c, lse, logit_x, bias_rows, status);
+    else
+      draft_combine_kernel<T, false><<<R, 64, 0, stream>>>(
+          R, gamma, V, r, d, U, W1, W2t, w, ws.zh, prev, ps, nullptr, ws.partials, nranges,
+          (uint32_t)k, seed, cycle, x, c, lse, logit_x, bias_rows, status);
+  }
+  return launch_status();
+}
+
+static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_dtype dt,
+                       const void* U, const void* h, const void* W1, const void* W2t,
+                       const void* Wg, const float* w, const int32_t* x0, uint64_t seed,
+                       uint64_t cycle, int32_t* x, float* c, float* lse, float* logit_x,
+                       void* bias_rows, int32_t* status, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  if (!dims_ok(R, gamma, V, r, d) || (dt != DSPARK_F32 && dt != DSPARK_BF16)) return DSPARK_EINVAL;
+  if (cycle >= ((uint64_t)1 << 28)) return DSPARK_EINVAL;
+  if (R == 0) return DSPARK_OK;
+  if (!U || !W1 || !W2t || !w || !x0 || !x || !c || !lse || !logit_x || !bias_rows || !ws)
+    return DSPARK_EINVAL;
+  if (d > 0 && !h) return DSPARK_EINVAL;
+  if (rnn && !Wg) return DSPARK_EINVAL;
+  if (!aligned16(U) || !aligned16(h) || !aligned16(W1) || !aligned16(W2t) || !aligned16(Wg) ||
+      !aligned16(bias_rows) || !aligned16(w))
+    return DSPARK_EINVAL;
+  const DraftWs probe = carve_draft(nullptr, R, gamma, V, r, d, rnn);
+  if (ws_bytes < probe.bytes) return DSPARK_EWORKSPACE;
+  if (!aligned16(ws)) return DSPARK_EINVAL;
+  const DraftWs lay = carve_draft(ws, R, gamma, V, r, d, rnn);
+  if (dt == DSPARK_BF16)
+    return draft_run<uint16_t>(rnn, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, x0, seed, cycle, x,
+                               c, lse, logit_x, bias_rows, status, lay, stream);
+  return draft_run<float>(rnn, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, x0, seed, cycle, x, c,
+                          lse, logit_x, bias_rows, status, lay, stream);
+}
+
+}  // namespace dspark
+
+extern "C" {
+
+size_t dspark_draft_workspace_bytes(int R, int gamma, int V, int r, int d) {
+  if (!dspark::dims_ok(R, gamma, V, r, d)) return 0;
+  return dspark::carve_draft(nullptr, R, gamma, V, r, d, false).bytes;
+}
+
+size_t dspark_draft_rnn_workspace_bytes(int R, int gamma, int V, int r, int d) {
+  if (!dspark::dims_ok(R, gamma, V, r, d)) return 0;
+  return dspark::carve_draft(nullptr, R, gamma, V, r, d, true).bytes;
+}
+
+int dspark_draft_markov(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void* U,
+                        const void* h, const void* W1, const void* W2t, const float* w,
+                        const int32_t* x0, uint64_t seed, uint64_t cycle, int32_t* x, float* c,
+                        float* lse, float* logit_x, void* bias_rows, int32_t* dev_status,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  return dspark::draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, x0, seed,
+                             cycle, x, c, lse, logit_x, bias_rows, dev_status, ws, ws_bytes,
+                             stream);
+}
+
+int dspark_draft_rnn(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void* U,
+                     const void* h, const void* W1, const void* W2t, const void* W_gco,
+                     const float* w, const int32_t* x0, uint64_t seed, uint64_t cycle,
+                     int32_t* x, float* c, float* lse, float* logit_x, float* bias_rows,
+                     int32_t* dev_status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return dspark::draft_entry(true, R, gamma, V, r, d, dt, U, h, W1, W2t, W_gco, w, x0, seed,
+                             cycle, x, c, lse, logit_x, bias_rows, dev_status, ws, ws_bytes,
+                             stream);
+}
+
+}  // extern "C"

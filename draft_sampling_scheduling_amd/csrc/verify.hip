@@ -1,0 +1,624 @@
+// verify.hip -- lossless verification of the scheduled prefixes (digest page, overall cycle
+// step 3; explainer page, section 06 single-token rule; eq. (8) for the analytic
+// acceptance c*).
+//
+// Rows are flattened the way the digest's production section describes variable-length
+// verification: the scheduled positions of all requests form one ragged list, so no row
+// is padded.  Launches:
+//   prep    one workgroup: exclusive scans of ell; list A = (q, j) for j = 1..ell_q + 1
+//           (every row whose target normaliser is needed, the bonus row included), list B
+//           = (q, j) for j = 1..ell_q (every verified position);
+//   lse     one workgroup per list-A row: log-sum-exp of the target row; on the bonus row
+//           also the first level of the bonus sample (streams 5);
+//   decide  one thread per request: the acceptance tests u < p_j(x_j)/q_j(x_j) in order
+//           (stream 2), the first rejection j*, the accepted tokens;
+//   sweep   matrix cores over list B (sweep.h): q_j recomputed from U_j + bias_j W2 and
+//           normalised by the drafted lse; sum |p - q| per row, and on the row j* the
+//           residual max(0, p - q) per 64-id block with its first-level Gumbel score
+//           (stream 3);
+//   final   one wave per request: c* for every verified row, then the second level of
+//           the correction (stream 4) or of the bonus (stream 6).
+#include "dev.h"
+#include "host.h"
+#include "sweep.h"
+
+namespace dspark {
+
+struct VerifyWs {
+  int* hdr;        // [0] = |A|, [1] = |B|
+  int* offA;       // [R]
+  int* offB;       // [R]
+  int2* rowA;      // [R*(gamma+1)] (q, j)
+  int2* rowB;      // [R*gamma]
+  float* lset;     // [R*(gamma+1)] target log-sum-exp of list-A rows
+  float2* bonus;   // [R] (best G, block) of the bonus row
+  int* jstar;      // [R] first rejected position, 0 = none
+  float4* partials;  // [R*gamma][nranges]: (sum |p-q|, best G, block, residual mass)
+  size_t bytes;
+};
+
+static VerifyWs carve_verify(void* ws, int R, int gamma, int V) {
+  Carve cv(ws);
+  VerifyWs w{};
+  w.hdr = cv.take<int>(4);
+  w.offA = cv.take<int>((size_t)R);
+  w.offB = cv.take<int>((size_t)R);
+  w.rowA = cv.take<int2>((size_t)R * (gamma + 1));
+  w.rowB = cv.take<int2>((size_t)R * gamma);
+  w.lset = cv.take<float>((size_t)R * (gamma + 1));
+  w.bonus = cv.take<float2>((size_t)R);
+  w.jstar = cv.take<int>((size_t)R);
+  const int nblocks = (V + kVB - 1) / kVB;
+  w.partials = cv.take<float4>((size_t)R * gamma * (nblocks < kMaxRanges ? nblocks : kMaxRanges));
+  w.bytes = cv.bytes();
+  return w;
+}
+
+// ---------------------------------------------------------------------------------------
+// prep: ragged row lists from ell
+// ---------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) verify_prep_kernel(int R, int gamma, const int32_t* ell_in,
+                                                           VerifyWs ws, int32_t* status) {
+  __shared__ int totA[1024], totB[1024];
+  const int per = (R + 1023) / 1024;
+  const int lo = threadIdx.x * per, hi = min(R, lo + per);
+  int sa = 0, sb = 0;
+  for (int q = lo; q < hi; ++q) {
+    int L = ell_in[q];
+    if (L < 0 || L > gamma) {
+      raise_fault(status, DSPARK_FAULT_LEN);
+      L = L < 0 ? 0 : gamma;
+    }
+    sa += L + 1;
+    sb += L;
+  }
+  totA[threadIdx.x] = sa;
+  totB[threadIdx.x] = sb;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int va = threadIdx.x >= off ? totA[threadIdx.x - off] : 0;
+    const int vb = threadIdx.x >= off ? totB[threadIdx.x - off] : 0;
+    __syncthreads();
+    totA[threadIdx.x] += va;
+    totB[threadIdx.x] += vb;
+    __syncthreads();
+  }
+  int oa = threadIdx.x > 0 ? totA[threadIdx.x - 1] : 0;
+  int ob = threadIdx.x > 0 ? totB[threadIdx.x - 1] : 0;
+  for (int q = lo; q < hi; ++q) {
+    int L = ell_in[q];
+    L = L < 0 ? 0 : (L > gamma ? gamma : L);
+    ws.offA[q] = oa;
+    ws.offB[q] = ob;
+    for (int j = 1; j <= L + 1; ++j) ws.rowA[oa + j - 1] = make_int2(q, j);
+    for (int j = 1; j <= L; ++j) ws.rowB[ob + j - 1] = make_int2(q, j);
+    oa += L + 1;
+    ob += L;
+  }
+  if (threadIdx.x == 1023) {
+    ws.hdr[0] = totA[1023];
+    ws.hdr[1] = totB[1023];
+  }
+}
+
+__device__ __forceinline__ int clamp_len(int L, int gamma) { return L < 0 ? 0 : (L > gamma ? gamma : L); }
+
+// ---------------------------------------------------------------------------------------
+// lse: target normaliser per list-A row (+ first level of the bonus sample)
+// ---------------------------------------------------------------------------------------
+template <class T>
+__global__ void __launch_bounds__(256) verify_lse_kernel(int R, int gamma, int V,
+                                                         const T* __restrict__ target,
+                                                         const int32_t* ell, VerifyWs ws,
+                                                         uint64_t seed, uint64_t cycle) {
+  __shared__ float sm[4], ss[4], sg[4];
+  __shared__ int sb[4];
+  const int i = blockIdx.x;
+  if (i >= ws.hdr[0]) return;
+  const int2 qj = ws.rowA[i];
+  const int q = qj.x, j = qj.y;
+  const int L = clamp_len(ell[q], gamma);
+  const bool bonus = (j == L + 1);
+  const T* row = target + ((size_t)q * (gamma + 1) + (j - 1)) * V;
+  const Rng rng(seed, cycle);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float M = -INFINITY, S = 0.0f, G = -INFINITY;
+  int Bk = 0x7fffffff;
+  const int nch = (V + 7) / 8;  // V % 8 == 0: whole chunks
+  for (int base = 0; base < nch; base += 256) {
+    const int ci = base + threadIdx.x;
+    float x[8];
+    float m = -INFINITY;
+    if (ci < nch) {
+      ld8<T>(row + (size_t)ci * 8, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, x[e]);
+    }
+    float s = 0.0f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += __expf(x[e] - m);
+    }
+    if (bonus) {
+      // one 64-id block = 8 consecutive threads (chunks ci & ~7 .. ci | 7)
+      float bm = m, bs = s;
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const float m2 = __shfl_xor(bm, o, kWave), s2 = __shfl_xor(bs, o, kWave);
+        lse_merge(bm, bs, m2, s2);
+      }
+      const int b = ci >> 3;
+      if ((threadIdx.x & 7) == 0 && ci < nch) {
+        const float g = gumbel_of(rng.word(kStreamBonusBlk, (uint32_t)q, (uint32_t)j, (uint32_t)b));
+        const float Gb = bm + __logf(bs) + g;
+        if (Gb > G) {
+          G = Gb;
+          Bk = b;
+        }
+      }
+    }
+    lse_merge(M, S, m, s);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
+    lse_merge(M, S, m2, s2);
+  }
+  wave_argmax(G, Bk);
+  if (lane == 0) {
+    sm[wave] = M;
+    ss[wave] = S;
+    sg[wave] = G;
+    sb[wave] = Bk;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) {
+      lse_merge(M, S, sm[w], ss[w]);
+      if (sg[w] > G || (sg[w] == G && sb[w] < Bk)) {
+        G = sg[w];
+        Bk = sb[w];
+      }
+    }
+    ws.lset[i] = M + __logf(S);
+    if (bonus) ws.bonus[q] = make_float2(G, __int_as_float(Bk));
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// decide: acceptance tests in order
+// ---------------------------------------------------------------------------------------
+template <class T>
+__global__ void __launch_bounds__(256) verify_decide_kernel(
+    int R, int gamma, int V, const T* __restrict__ target, const int32_t* __restrict__ x,
+    const float* __restrict__ lse, const float* __restrict__ logit_x, const int32_t* ell,
+    VerifyWs ws, uint64_t seed, uint64_t cycle, int32_t* n_acc, int32_t* y, int32_t* status) {
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= R) return;
+  const int L = clamp_len(ell[q], gamma);
+  const Rng rng(seed, cycle);
+  int js = 0;
+  for (int j = 1; j <= L; ++j) {
+    const size_t rj = (size_t)q * gamma + (j - 1);
+    const int xj = checked_token(x[rj], V, status);
+    const float t = ld<T>(target, ((size_t)q * (gamma + 1) + (j - 1)) * V + xj);
+    const float lp = t - ws.lset[ws.offA[q] + j - 1];  // log p_j(x_j)
+    const float lq = logit_x[rj] - lse[rj];             // log q_j(x_j)
+    const float ratio = __expf(lp - lq);
+    const float u = uniform_of(rng.word(kStreamAccept, (uint32_t)q, (uint32_t)j, 0u));
+    if (!(u < ratio)) {
+      js = j;
+      break;
+    }
+  }
+  ws.jstar[q] = js;
+  const int na = js ? js - 1 : L;
+  n_acc[q] = na;
+  int32_t* yq = y + (size_t)q * (gamma + 1);
+  for (int j = 0; j < na; ++j) yq[j] = checked_token(x[(size_t)q * gamma + j], V, status);
+  for (int j = na; j <= gamma; ++j) yq[j] = -1;
+}
+
+// ---------------------------------------------------------------------------------------
+// sweep epilogue over list B
+// ---------------------------------------------------------------------------------------
+struct VerifySweepParams {
+  const uint16_t* U;        // [R][gamma][V]
+  const uint16_t* target;   // [R][gamma+1][V]
+  const void* brows;        // [R][gamma][r] bf16 or float
+  const float* lse;         // [R][gamma]
+  int R, gamma, V, r;
+  VerifyWs ws;
+  uint64_t seed, cycle;
+  int nranges;
+};
+
+template <bool SPLIT>
+struct VerifyEpi {
+  using Params = VerifySweepParams;
+  struct State {
+    float tv;          // sum |p - q| over this range
+    float G, mass;     // residual: best block score, total mass
+    int B;
+    int q, j, resid;   // this lane's row
+    float lq, lp;      // normalisers (draft lse, target lse)
+    int grp;
+    uint4 words;
+  };
+  struct Pre {
+    uint4 u[2][2][2];
+    uint4 t[2][2][2];
+  };
+  __device__ static bool group_live(const Params& p, int row0) { return row0 < p.ws.hdr[1]; }
+  __device__ static int nrows(const Params& p) { return p.ws.hdr[1]; }
+  __device__ static const void* brow(const Params& p, int row) {
+    const int2 qj = p.ws.rowB[row];
+    const size_t off = ((size_t)qj.x * p.gamma + (qj.y - 1)) * p.r;
+    if (SPLIT) return static_cast<const float*>(p.brows) + off;
+    return static_cast<const uint16_t*>(p.brows) + off;
+  }
+  __device__ static void init(const Params& p, State& s, int myrow) {
+    s.tv = 0.0f;
+    s.G = -INFINITY;
+    s.mass = 0.0f;
+    s.B = 0x7fffffff;
+    s.grp = -1;
+    s.words = make_uint4(0, 0, 0, 0);
+    s.q = s.j = s.resid = 0;
+    s.lq = s.lp = 0.0f;
+    if (myrow >= 0 && myrow < p.ws.hdr[1]) {
+      const int2 qj = p.ws.rowB[myrow];
+      s.q = qj.x;
+      s.j = qj.y;
+      s.resid = (p.ws.jstar[qj.x] == qj.y);
+      s.lq = p.lse[(size_t)qj.x * p.gamma + (qj.y - 1)];
+      s.lp = p.ws.lset[p.ws.offA[qj.x] + qj.y - 1];
+    }
+  }
+  template <int NT>
+  __device__ static void prefetch(const Params& p, Pre& pre, int b, int rowbase) {
+    const int lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5;
+    const int nB = p.ws.hdr[1];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int row = rowbase + 32 * nt + n;
+      int2 qj = make_int2(0, 1);
+      if (row < nB) qj = p.ws.rowB[row];
+      const uint16_t* ur = p.U + ((size_t)qj.x * p.gamma + (qj.y - 1)) * p.V;
+      const uint16_t* tr = p.target + ((size_t)qj.x * (p.gamma + 1) + (qj.y - 1)) * p.V;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int v = b * kVB + 32 * mt + 16 * h;
+        const bool ok = row < nB && v < p.V;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bool okc = ok && (v + 8 * c) < p.V;
+          pre.u[nt][mt][c] = okc ? *reinterpret_cast<const uint4*>(ur + v + 8 * c) : make_uint4(0, 0, 0, 0);
+          pre.t[nt][mt][c] = okc ? *reinterpret_cast<const uint4*>(tr + v + 8 * c) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  }
+  template <int NT>
+  __device__ static void block(const Params& p, State& s, const Pre& pre,
+                               const f32x16 (&acc)[NT][2], int b, int rowbase, int myrow) {
+    const int lane = threadIdx.x & 63, h = lane >> 5, n = lane & 31;
+    const int nB = p.ws.hdr[1];
+    float tvp[NT], rm[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      // normalisers of this lane's row in n-tile nt, kept by lane n + 32*nt
+      const int row = rowbase + 32 * nt + n;
+      const float lq = __shfl(s.lq, n + 32 * nt, kWave);
+      const float lp = __shfl(s.lp, n + 32 * nt, kWave);
+      float tv = 0.0f, rho = 0.0f;
+      if (row < nB) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int v0 = b * kVB + 32 * mt + 16 * h;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const uint4 u = pre.u[nt][mt][c], t = pre.t[nt][mt][c];
+            const uint32_t uw[4] = {u.x, u.y, u.z, u.w}, tw[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int jj = 8 * c + e;
+              if (v0 + jj < p.V) {
+                const float uv = (e & 1) ? bf16hi(uw[e >> 1]) : bf16lo(uw[e >> 1]);
+                const float tt = (e & 1) ? bf16hi(tw[e >> 1]) : bf16lo(tw[e >> 1]);
+                const float qv = __expf(acc[nt][mt][jj] + uv - lq);
+                const float pv = __expf(tt - lp);
+                tv += fabsf(pv - qv);
+                rho += fmaxf(pv - qv, 0.0f);
+              }
+            }
+          }
+        }
+      }
+      tvp[nt] = tv + __shfl_xor(tv, 32, kWave);
+      rm[nt] = rho + __shfl_xor(rho, 32, kWave);
+    }
+    if (myrow < 0 || myrow >= nB) return;
+    const int mine = (NT == 2) ? h : 0;
+    s.tv += tvp[mine];
+    if (s.resid) {
+      const float mass = rm[mine];
+      s.mass += mass;
+      if (mass > 0.0f) {
+        const int grp = b >> 2;
+        if (grp != s.grp) {
+          s.grp = grp;
+          s.words = Rng(p.seed, p.cycle).block(kStreamResidBlk, (uint32_t)s.q, (uint32_t)s.j,
+                                               (uint32_t)grp);
+        }
+        const float G = __logf(mass) + gumbel_of(pick_word(s.words, (uint32_t)b & 3u));
+        if (G > s.G) {
+          s.G = G;
+          s.B = b;
+        }
+      }
+    }
+  }
+  __device__ static void finish(const Params& p, const State& s, int myrow, int range) {
+    if (myrow < 0 || myrow >= p.ws.hdr[1]) return;
+    p.ws.partials[(size_t)myrow * p.nranges + range] = make_float4(s.tv, s.G, __int_as_float(s.B), s.mass);
+  }
+};
+
+// float operands: one wave per (list-B row, range), VALU only
+__global__ void __launch_bounds__(64) verify_sweep_f32_kernel(
+    int gamma, int V, int r, const float* __restrict__ U, const float* __restrict__ target,
+    const float* __restrict__ W2t, const float* __restrict__ brows,
+    const float* __restrict__ lse, VerifyWs ws, uint64_t seed, uint64_t cycle, int nranges,
+    int nblocks) {
+  const int row = blockIdx.y, range = blockIdx.x, lane = threadIdx.x;
+  if (row >= ws.hdr[1]) return;
+  const int2 qj = ws.rowB[row];
+  const int q = qj.x, j = qj.y;
+  const size_t rj = (size_t)q * gamma + (j - 1);
+  const float* e = brows + rj * r;
+  const float* trow = target + ((size_t)q * (gamma + 1) + (j - 1)) * V;
+  const float lq = lse[rj], lp = ws.lset[ws.offA[q] + j - 1];
+  const bool resid = ws.jstar[q] == j;
+  const int per = (nblocks + nranges - 1) / nranges;
+  const int b0 = range * per, b1 = min(nblocks, b0 + per);
+  const Rng rng(seed, cycle);
+  float tv = 0.0f, G = -INFINITY, mass = 0.0f;
+  int Bk = 0x7fffffff;
+  for (int b = b0; b < b1; ++b) {
+    const int v = b * kVB + lane;
+    float d = 0.0f, rho = 0.0f;
+    if (v < V) {
+      float acc = 0.0f;
+      for (int i = 0; i < r; ++i) acc = fmaf(e[i], W2t[(size_t)v * r + i], acc);
+      const float qv = __expf(U[rj * V + v] + acc - lq);
+      const float pv = __expf(trow[v] - lp);
+      d = fabsf(pv - qv);
+      rho = fmaxf(pv - qv, 0.0f);
+    }
+    tv += wave_sum(d);
+    const float m = wave_sum(rho);
+    if (resid) {
+      mass += m;
+      if (m > 0.0f) {
+        const float Gb = __logf(m) + gumbel_of(rng.word(kStreamResidBlk, (uint32_t)q, (uint32_t)j, (uint32_t)b));
+        if (Gb > G) {
+          G = Gb;
+          Bk = b;
+        }
+      }
+    }
+  }
+  if (lane == 0) ws.partials[(size_t)row * nranges + range] = make_float4(tv, G, __int_as_float(Bk), mass);
+}
+
+// two-level Gumbel-max over a whole row of logits, one wave (fallback of the correction
+// when the residual mass is zero in floating point)
+template <class T>
+__device__ int sample_row_wave(const T* row, int V, const Rng& rng, uint32_t sblk, uint32_t sin,
+                               uint32_t q, uint32_t k) {
+  const int lane = threadIdx.x & 63;
+  const int nblocks = (V + kVB - 1) / kVB;
+  float G = -INFINITY;
+  int Bk = 0;
+  for (int b = 0; b < nblocks; ++b) {
+    const int v = b * kVB + lane;
+    const float l = v < V ? ld<T>(row, v) : -INFINITY;
+    const float m = wave_max(l);
+    const float s = wave_sum(l == -INFINITY ? 0.0f : __expf(l - m));
+    const float Gb = m + __logf(s) + gumbel_of(rng.word(sblk, q, k, (uint32_t)b));
+    if (Gb > G) {
+      G = Gb;
+      Bk = b;
+    }
+  }
+  const int v = Bk * kVB + lane;
+  float score = v < V ? ld<T>(row, v) + gumbel_of(rng.word(sin, q, k, (uint32_t)v)) : -INFINITY;
+  int idx = v;
+  wave_argmax(score, idx);
+  return idx;
+}
+
+// ---------------------------------------------------------------------------------------
+// final: c* of every verified row, then the correction or the bonus token
+// ---------------------------------------------------------------------------------------
+template <class T, class BT>
+__global__ void __launch_bounds__(64) verify_final_kernel(
+    int R, int gamma, int V, int r, const T* __restrict__ target, const T* __restrict__ U,
+    const T* __restrict__ W2t, const BT* __restrict__ brows, const float* __restrict__ lse,
+    const int32_t* ell, VerifyWs ws, int nranges, uint64_t seed, uint64_t cycle,
+    const int32_t* n_acc, int32_t* y, float* c_star) {
+  const int q = blockIdx.x, lane = threadIdx.x;
+  const int L = clamp_len(ell[q], gamma);
+  for (int j = 1; j <= gamma; ++j) {
+    float cs = __int_as_float(0x7fc00000);  // NaN past the scheduled length
+    if (j <= L) {
+      const size_t row = (size_t)ws.offB[q] + j - 1;
+      float s = 0.0f;
+      for (int i = lane; i < nranges; i += 64) s += ws.partials[row * nranges + i].x;
+      s = wave_sum(s);
+      cs = 1.0f - 0.5f * s;
+    }
+    if (lane == 0) c_star[(size_t)q * gamma + (j - 1)] = cs;
+  }
+  const Rng rng(seed, cycle);
+  const int js = ws.jstar[q];
+  int token;
+  if (js > 0) {
+    const size_t row = (size_t)ws.offB[q] + js - 1;
+    float G = -INFINITY, mass = 0.0f;
+    int Bk = 0x7fffffff;
+    for (int i = lane; i < nranges; i += 64) {
+      const float4 pr = ws.partials[row * nranges + i];
+      const int pb = __float_as_int(pr.z);
+      mass += pr.w;
+      if (pr.y > G || (pr.y == G && pb < Bk)) {
+        G = pr.y;
+        Bk = pb;
+      }
+    }
+    mass = wave_sum(mass);
+    wave_argmax(G, Bk);
+    const size_t rj = (size_t)q * gamma + (js - 1);
+    const T* trow = target + ((size_t)q * (gamma + 1) + (js - 1)) * V;
+    const int nblocks = (V + kVB - 1) / kVB;
+    if (mass > 0.0f && Bk >= 0 && Bk < nblocks) {
+      const float lq = lse[rj], lp = ws.lset[ws.offA[q] + js - 1];
+      const int v = Bk * kVB + lane;
+      float score = -INFINITY;
+      if (v < V) {
+        float acc = 0.0f;
+        const BT* e = brows + rj * r;
+        for (int i = 0; i < r; ++i) acc = fmaf(ld<BT>(e, i), ld<T>(W2t, (size_t)v * r + i), acc);
+        const float qv = __expf(ld<T>(U, rj * V + v) + acc - lq);
+        const float pv = __expf(ld<T>(trow, v) - lp);
+        const float rho = pv - qv;
+        if (rho > 0.0f)
+          score = __logf(rho) + gumbel_of(rng.word(kStreamResidIn, (uint32_t)q, (uint32_t)js, (uint32_t)v));
+      }
+      int idx = v;
+      wave_argmax(score, idx);
+      token = idx;
+    } else {
+      token = sample_row_wave<T>(trow, V, rng, kStreamResidBlk, kStreamResidIn, (uint32_t)q,
+                                 (uint32_t)js);
+    }
+  } else {
+    const int j = L + 1;
+    const T* trow = target + ((size_t)q * (gamma + 1) + L) * V;
+    const int nblocks = (V + kVB - 1) / kVB;
+    int Bk = __float_as_int(ws.bonus[q].y);
+    if (Bk < 0 || Bk >= nblocks) Bk = 0;
+    const int v = Bk * kVB + lane;
+    float score = v < V ? ld<T>(trow, v) + gumbel_of(rng.word(kStreamBonusIn, (uint32_t)q, (uint32_t)j, (uint32_t)v))
+                        : -INFINITY;
+    int idx = v;
+    wave_argmax(score, idx);
+    token = idx;
+  }
+  if (lane == 0) y[(size_t)q * (gamma + 1) + n_acc[q]] = token;
+}
+
+// ---------------------------------------------------------------------------------------
+// host
+// ---------------------------------------------------------------------------------------
+template <class T, class BT>
+static int verify_run(int R, int gamma, int V, int r, const void* target_, const void* U_,
+                      const void* W2t_, const void* brows_, const int32_t* x, const float* lse,
+                      const float* logit_x, const int32_t* ell, uint64_t seed, uint64_t cycle,
+                      int32_t* n_acc, int32_t* y, float* c_star, int32_t* status,
+                      const VerifyWs& ws, hipStream_t stream) {
+  const T* target = static_cast<const T*>(target_);
+  const T* U = static_cast<const T*>(U_);
+  const T* W2t = static_cast<const T*>(W2t_);
+  const BT* brows = static_cast<const BT*>(brows_);
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr bool SPLIT = BF && sizeof(BT) == 4;
+
+  verify_prep_kernel<<<1, 1024, 0, stream>>>(R, gamma, ell, ws, status);
+  verify_lse_kernel<T><<<R * (gamma + 1), 256, 0, stream>>>(R, gamma, V, target, ell, ws, seed, cycle);
+  verify_decide_kernel<T><<<(R + 255) / 256, 256, 0, stream>>>(
+      R, gamma, V, target, x, lse, logit_x, ell, ws, seed, cycle, n_acc, y, status);
+
+  const int rows_max = R * gamma;
+  int nranges;
+  if (BF) {
+    const int nt = rows_max > 128 ? 2 : 1;
+    SweepGeom g = make_geom(rows_max, V, r, reinterpret_cast<const uint16_t*>(W2t), nt, device_cus());
+    nranges = g.nranges;
+    VerifySweepParams p{};
+    p.U = reinterpret_cast<const uint16_t*>(U);
+    p.target = reinterpret_cast<const uint16_t*>(target);
+    p.brows = brows;
+    p.lse = lse;
+    p.R = R;
+    p.gamma = gamma;
+    p.V = V;
+    p.r = r;
+    p.ws = ws;
+    p.seed = seed;
+    p.cycle = cycle;
+    p.nranges = nranges;
+    const size_t sh = sweep_lds_bytes(r);
+    const int ntask = g.nranges * g.ngroups;
+    if (nt == 2)
+      sweep_kernel<2, SPLIT, VerifyEpi<SPLIT>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
+    else
+      sweep_kernel<1, SPLIT, VerifyEpi<SPLIT>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
+  } else {
+    const int nblocks = (V + kVB - 1) / kVB;
+    nranges = nblocks < 64 ? nblocks : 64;
+    dim3 grid(nranges, rows_max);
+    verify_sweep_f32_kernel<<<grid, 64, 0, stream>>>(
+        gamma, V, r, reinterpret_cast<const float*>(U), reinterpret_cast<const float*>(target),
+        reinterpret_cast<const float*>(W2t), reinterpret_cast<const float*>(brows), lse, ws,
+        seed, cycle, nranges, nblocks);
+  }
+  verify_final_kernel<T, BT><<<R, 64, 0, stream>>>(R, gamma, V, r, target, U, W2t, brows, lse,
+                                                    ell, ws, nranges, seed, cycle, n_acc, y, c_star);
+  return launch_status();
+}
+
+}  // namespace dspark
+
+extern "C" {
+
+size_t dspark_verify_workspace_bytes(int R, int gamma, int V, int r) {
+  if (!dspark::dims_ok(R, gamma, V, r, 0)) return 0;
+  return dspark::carve_verify(nullptr, R, gamma, V).bytes;
+}
+
+int dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, const void* target,
+                  const void* U, const void* W2t, const void* bias_rows, dspark_dtype bias_dt,
+                  const int32_t* x, const float* lse, const float* logit_x, const int32_t* ell,
+                  uint64_t seed, uint64_t cycle, int32_t* n_acc, int32_t* y, float* c_star,
+                  int32_t* dev_status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  using namespace dspark;
+  if (!dims_ok(R, gamma, V, r, 0) || (dt != DSPARK_F32 && dt != DSPARK_BF16)) return DSPARK_EINVAL;
+  if (bias_dt != DSPARK_F32 && bias_dt != dt) return DSPARK_EINVAL;
+  if (cycle >= ((uint64_t)1 << 28)) return DSPARK_EINVAL;
+  if (R == 0) return DSPARK_OK;
+  if ((long)R * (gamma + 1) > (long)0x7fffffff / 2) return DSPARK_EINVAL;
+  if (!target || !U || !W2t || !bias_rows || !x || !lse || !logit_x || !ell || !n_acc || !y ||
+      !c_star || !ws)
+    return DSPARK_EINVAL;
+  if (!aligned16(target) || !aligned16(U) || !aligned16(W2t) || !aligned16(bias_rows))
+    return DSPARK_EINVAL;
+  if (ws_bytes < carve_verify(nullptr, R, gamma, V).bytes) return DSPARK_EWORKSPACE;
+  if (!aligned16(ws)) return DSPARK_EINVAL;
+  const VerifyWs lay = carve_verify(ws, R, gamma, V);
+  if (dt == DSPARK_BF16) {
+    if (bias_dt == DSPARK_BF16)
+      return verify_run<uint16_t, uint16_t>(R, gamma, V, r, target, U, W2t, bias_rows, x, lse,
+                                            logit_x, ell, seed, cycle, n_acc, y, c_star,
+                                            dev_status, lay, stream);
+    return verify_run<uint16_t, float>(R, gamma, V, r, target, U, W2t, bias_rows, x, lse,
+                                       logit_x, ell, seed, cycle, n_acc, y, c_star, dev_status,
+                                       lay, stream);
+  }
+  return verify_run<float, float>(R, gamma, V, r, target, U, W2t, bias_rows, x, lse, logit_x,
+                                  ell, seed, cycle, n_acc, y, c_star, dev_status, lay, stream);
+}
+
+const char* dspark_version(void) { return "dspark-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

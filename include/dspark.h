@@ -1,0 +1,183 @@
+/*
+ * dspark.h -- C ABI of the DSpark draft -> schedule -> verify hot path on MI355X (gfx950).
+ *
+ * The method ("DSpark: confidence-scheduled speculative decoding"; the technical digest
+ * page, the interactive explainer page): a parallel backbone gives base logits U_k and
+ * hidden states h_k for draft positions k = 1..gamma; a light sequential head adds a
+ * prefix-dependent bias to U_k, samples x_k from one exact softmax and emits a confidence
+ * c_k; a hardware-aware scheduler picks how many drafted tokens of each request the target
+ * verifies; rejection sampling keeps the target's distribution exactly.
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer unless its comment says otherwise.  The
+ *     caller owns all memory; the library never allocates, frees, retains a pointer or
+ *     synchronises.  All work is enqueued on `stream` and the call returns at once.
+ *   - Arrays are dense and row-major with the shapes given; element type "dt" means the
+ *     dtype argument (DSPARK_F32: float, DSPARK_BF16: bfloat16 bit patterns).
+ *   - A negative return value means the call was rejected on the host before anything was
+ *     enqueued (DSPARK_EINVAL bad scalar, shape or null pointer; DSPARK_ERANGE a table that
+ *     does not cover what the call needs; DSPARK_EWORKSPACE ws_bytes below the matching
+ *     *_workspace_bytes(); DSPARK_EDEVICE a HIP error when launching).
+ *   - Faults in device data (a token outside [0,V), a confidence that is NaN or outside
+ *     [0,1], a length outside [0,gamma]) OR bits into *dev_status (nullable); the
+ *     offending value is clamped so every access stays in bounds, and the outputs of that
+ *     call are then unspecified.
+ *   - Randomness is Philox4x32-10 keyed by `seed` (64 bits), with the counter
+ *     (i >> 2, request, position, cycle << 4 | stream) and word i & 3; `cycle` < 2^28.
+ *     Same inputs + (seed, cycle) give bit-identical outputs.
+ *   - Sampling from softmax(l) is Gumbel-max taken in two levels: the block of 64
+ *     consecutive ids with the largest log-sum-exp + Gumbel noise, then the id inside it
+ *     with the largest l + Gumbel noise (exact in distribution).
+ *   - Size limits (DSPARK_EINVAL otherwise): V % 8 == 0; r in {16,32,64,128,256};
+ *     d % 8 == 0; 1 <= gamma <= 64; R >= 0 (R == 0 is a no-op); R*gamma <= 8192 for the
+ *     scheduler.
+ *   - Thread safety: no global mutable state; concurrent calls on different streams with
+ *     disjoint outputs and workspaces are safe.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+typedef enum {
+  /* Algorithm 1 as printed on the digest page (Module E): admit candidates in descending
+   * prefix survival while Theta = tau * SPS(B) rises, stop at the first one that does not */
+  DSPARK_SCHED_SYNC_BREAK = 0,
+  /* the production variant without the break: the admitted count is the first one that
+   * reaches the largest Theta over all prefixes of the sorted order (digest, production
+   * deployment, first conflict) */
+  DSPARK_SCHED_GLOBAL = 1,
+  /* the asynchronous variant: the batch capacity comes from a GLOBAL search over the
+   * confidences of two cycles before, the candidates are ranked by the current ones and
+   * the top K = capacity - R are admitted (digest, production deployment, second conflict) */
+  DSPARK_SCHED_ASYNC_LAG2 = 2
+} dspark_sched_mode;
+
+enum {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = -1,
+  DSPARK_ERANGE = -2,
+  DSPARK_EWORKSPACE = -3,
+  DSPARK_EDEVICE = -4
+};
+
+/* bits OR-ed into *dev_status */
+enum { DSPARK_FAULT_TOKEN = 1, DSPARK_FAULT_CONF = 2, DSPARK_FAULT_LEN = 4 };
+
+/* ------------------------------------------------------------------------------------
+ * Draft (digest, Module B eq. (4) with the Markov head of eq. (5) or the RNN head of
+ * eq. (6); confidence head eq. (7)).
+ *
+ * For every request q and k = 1..gamma (x_{q,0} = x0[q], the anchor, which is the first
+ * predicted position per Module A):
+ *   e            = W1[x_{q,k-1}]                                     (gather, r values)
+ *   bias row     = e (Markov)  |  tanh(W_o z_k), z_k = [s_{k-1}; e; h_k] (RNN)
+ *   l(v)         = U_k(v) + sum_i biasrow[i] * W2[i][v]              (never stored)
+ *   lse[q][k]    = log sum_v exp l(v);   q_k = softmax(l)
+ *   x[q][k]      = two-level Gumbel-max sample of q_k (streams 0, 1)
+ *   logit_x      = l(x_k);  so q_k(x_k) = exp(logit_x - lse)
+ *   c[q][k]      = sigmoid( sum_i w[i] h_k[i] + sum_i w[d+i] e[i] )   (no bias term)
+ *
+ * Inputs
+ *   U   [R][gamma][V] dt   base logits U_1..U_gamma of the parallel backbone
+ *   h   [R][gamma][d] dt   hidden states h_1..h_gamma
+ *   W1  [V][r] dt          token embedding table (the low-rank factor W_1)
+ *   W2t [V][r] dt          W_2 transposed: row v holds column v of W_2 in R^{r x V}
+ *                          (the usual storage of an output projection)
+ *   w   [d + r] float      confidence weights, ordered [h part ; W1-row part]
+ *   x0  [R] int32          anchors
+ * Outputs
+ *   x, c, lse, logit_x [R][gamma] (int32, float, float, float)
+ *   bias_rows [R][gamma][r]: the vector that multiplied W2 at each step, for verify;
+ *     Markov: type dt (exact copy of W1 rows);  RNN: float.
+ * Workspace: ws_bytes >= dspark_draft_workspace_bytes(...), any 256-byte aligned buffer.
+ * ------------------------------------------------------------------------------------ */
+size_t dspark_draft_workspace_bytes(int R, int gamma, int V, int r, int d);
+
+int dspark_draft_markov(int R, int gamma, int V, int r, int d, dspark_dtype dt,
+                        const void *U, const void *h, const void *W1, const void *W2t,
+                        const float *w, const int32_t *x0, uint64_t seed, uint64_t cycle,
+                        int32_t *x, float *c, float *lse, float *logit_x, void *bias_rows,
+                        int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* RNN head, eq. (6): W_gco [3r][2r + d] dt stacks the gate, candidate and output
+ * projections (row blocks in that order; columns ordered [s ; W1 row ; h]; no biases);
+ * s_0 = 0.  The bias row of step k is tanh(W_o z_k) with z_k holding s_{k-1}; c uses eq.
+ * (7) with W1[x_{k-1}] unchanged.  bias_rows is float [R][gamma][r]. */
+size_t dspark_draft_rnn_workspace_bytes(int R, int gamma, int V, int r, int d);
+
+int dspark_draft_rnn(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void *U,
+                     const void *h, const void *W1, const void *W2t, const void *W_gco,
+                     const float *w, const int32_t *x0, uint64_t seed, uint64_t cycle,
+                     int32_t *x, float *c, float *lse, float *logit_x, float *bias_rows,
+                     int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Schedule (digest, Module E and Algorithm 1; production deployment for the variants).
+ *   a[q][j]   = c[q][1] * ... * c[q][j] in float, left to right (prefix survival)
+ *   E         = {(q,j) : a[q][j] > 0} in descending a (ties: q, then j, ascending)
+ *   admitting the first n entries of E gives B_n = R + n and
+ *   tau_n     = R + sum of their a, kept exactly as floor(a * 2^32) integer increments,
+ *   Theta_n   = double(tau_fx_n) * 2^-32 * double(SPS(B_n)), one rounding.
+ *   SYNC_BREAK: n = (first n >= 1 with Theta_n <= Theta_{n-1}) - 1, or |E|;
+ *   GLOBAL: the smallest n with the largest Theta_n;
+ *   ASYNC_LAG2: cap = R_lag + n_GLOBAL(c_lag); n = min(max(cap - R, 0), |E|).
+ *   ell[q] = number of q's entries among the first n (always a prefix 1..ell[q]).
+ * Inputs
+ *   c [R][gamma] float in [0,1]; c_lag [R_lag][gamma] float (ASYNC_LAG2 only, else NULL)
+ *   sps: DEVICE float table, SPS(B) = sps[B - sps_B0]; it must cover B = R .. R(1+gamma)
+ *   (and R_lag .. R_lag(1+gamma) in ASYNC_LAG2), else DSPARK_ERANGE.
+ * Outputs: ell [R] int32; a [R][gamma] float (nullable);
+ *   stats [4] double (nullable) = {B, tau, Theta, n admitted}.
+ * ------------------------------------------------------------------------------------ */
+size_t dspark_schedule_workspace_bytes(int R, int gamma);
+
+int dspark_schedule(int R, int gamma, const float *c, const float *c_lag, int R_lag,
+                    const float *sps, int sps_B0, int sps_len, dspark_sched_mode mode,
+                    int32_t *ell, float *a, double *stats, int32_t *dev_status, void *ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Verify (digest, overall cycle step 3; explainer, section 06; eq. (8) for c*).
+ * For each request q with scheduled length L = ell[q] and positions j = 1..L:
+ *   p_j = softmax(target row j); q_j = softmax(U_j + bias_j W2) normalised by lse
+ *   c_star[q][j] = 1 - 1/2 sum_v |p_j(v) - q_j(v)|   (NaN for j > L)
+ *   x_j is accepted iff u < p_j(x_j) / q_j(x_j), u uniform (stream 2, index 0),
+ *   with q_j(x_j) = exp(logit_x - lse) as drafted; the first rejection j* stops it.
+ * If some j* <= L is rejected: emit x_1..x_{j*-1}, then a two-level Gumbel sample of
+ *   max(0, p_j* - q_j*) (streams 3, 4; if that mass is 0 in floating point, of p_j*).
+ * Otherwise: emit x_1..x_L, then a sample of target row L+1 (the bonus; streams 5, 6).
+ * Inputs
+ *   target [R][gamma+1][V] dt   target logits for positions 1..gamma+1
+ *   U [R][gamma][V] dt, W2t [V][r] dt      as in draft
+ *   bias_rows [R][gamma][r] of type bias_dt (as the draft wrote them)
+ *   x, lse, logit_x [R][gamma]              draft outputs
+ *   ell [R] int32                           schedule output (or any lengths in [0,gamma])
+ * Outputs: n_acc [R] int32; y [R][gamma+1] int32 (first n_acc+1 valid, rest -1);
+ *   c_star [R][gamma] float.
+ * ------------------------------------------------------------------------------------ */
+size_t dspark_verify_workspace_bytes(int R, int gamma, int V, int r);
+
+int dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, const void *target,
+                  const void *U, const void *W2t, const void *bias_rows,
+                  dspark_dtype bias_dt, const int32_t *x, const float *lse,
+                  const float *logit_x, const int32_t *ell, uint64_t seed, uint64_t cycle,
+                  int32_t *n_acc, int32_t *y, float *c_star, int32_t *dev_status, void *ws,
+                  size_t ws_bytes, hipStream_t stream);
+
+/* Library version string (static storage). */
+const char *dspark_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

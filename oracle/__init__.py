@@ -53,13 +53,13 @@ def lib():
                                         C.c_int, C.c_long, i64p]
         common = [C.c_int] * 6 + [vp, vp, vp, vp]
         outs = [i32p, f64p, f64p, f64p, f64p, f64p, f64p]
-        L.ora_draft_markov.argtypes = common + [f32p, i32p, C.c_uint64, C.c_uint64] + outs
-        L.ora_draft_rnn.argtypes = common + [vp, f32p, i32p, C.c_uint64, C.c_uint64] + outs
+        L.ora_draft_markov.argtypes = common + [f32p, i32p, i32p, C.c_uint64, C.c_uint64] + outs
+        L.ora_draft_rnn.argtypes = common + [vp, f32p, i32p, i32p, C.c_uint64, C.c_uint64] + outs
         L.ora_draft_markov.restype = L.ora_draft_rnn.restype = C.c_int
         L.ora_schedule.argtypes = [C.c_int, C.c_int, f32p, f32p, C.c_int, f32p, C.c_int,
                                    C.c_int, C.c_int, i32p, f32p, f64p, f64p]
         L.ora_schedule.restype = C.c_int
-        L.ora_verify.argtypes = ([C.c_int] * 5 + [vp, vp, vp, f64p, i32p, i32p, C.c_uint64,
+        L.ora_verify.argtypes = ([C.c_int] * 5 + [vp, vp, vp, f64p, i32p, i32p, i32p, C.c_uint64,
                                  C.c_uint64, i32p, i32p, f64p, f64p, f64p, f64p, f64p])
         L.ora_verify.restype = C.c_int
         L.ora_num_threads.restype = C.c_int
@@ -127,7 +127,7 @@ def sample_trials(l, seed, cycle, stream_blk, stream_in, ntrials) -> np.ndarray:
     return counts
 
 
-def _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=None):
+def _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=None, req_ids=None):
     U, h, W1, W2 = (np.ascontiguousarray(a) for a in (U, h, W1, W2))
     dt = _dt_of(U)
     for a in (h, W1, W2) + ((W_gco,) if W_gco is not None else ()):
@@ -140,11 +140,14 @@ def _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=None):
     w = _c(w, np.float32)
     assert w.shape == (d + rank,)
     x0 = _c(x0, np.int32)
+    rid = None if req_ids is None else _c(req_ids, np.int32)
+    assert rid is None or rid.shape == (R,)
     x = np.zeros((R, gamma), np.int32)
     c, lse, logit_x, gb, gi = (np.zeros((R, gamma)) for _ in range(5))
     bias_rows = np.zeros((R, gamma, rank))
     args = [R, gamma, V, rank, d, dt, _vp(U), _vp(h), _vp(W1), _vp(W2)]
-    tail = [_p(w, C.c_float), _p(x0, C.c_int32), seed, cycle, _p(x, C.c_int32),
+    tail = [_p(w, C.c_float), _p(x0, C.c_int32), _p(rid, C.c_int32), seed, cycle,
+            _p(x, C.c_int32),
             _p(c, C.c_double), _p(lse, C.c_double), _p(logit_x, C.c_double),
             _p(bias_rows, C.c_double), _p(gb, C.c_double), _p(gi, C.c_double)]
     if W_gco is None:
@@ -159,14 +162,14 @@ def _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=None):
                 gap_in=gi)
 
 
-def draft_markov(U, h, W1, W2, w, x0, seed=0, cycle=0):
+def draft_markov(U, h, W1, W2, w, x0, seed=0, cycle=0, req_ids=None):
     """Markov-head draft (eqs. 4, 5, 7).  W2 is [rank][V] as on the pages."""
-    return _draft(U, h, W1, W2, w, x0, seed, cycle)
+    return _draft(U, h, W1, W2, w, x0, seed, cycle, req_ids=req_ids)
 
 
-def draft_rnn(U, h, W1, W2, W_gco, w, x0, seed=0, cycle=0):
+def draft_rnn(U, h, W1, W2, W_gco, w, x0, seed=0, cycle=0, req_ids=None):
     """RNN-head draft (eq. 6, confidence eq. 7)."""
-    return _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=W_gco)
+    return _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=W_gco, req_ids=req_ids)
 
 
 def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, trace=False):
@@ -200,7 +203,7 @@ def schedule_rc(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None) -> int:
                               sps.size, mode, _p(ell, C.c_int32), None, None, None)
 
 
-def verify(target, U, W2, bias_rows, x, ell, seed=0, cycle=0):
+def verify(target, U, W2, bias_rows, x, ell, seed=0, cycle=0, req_ids=None):
     """Rejection-sampling verification (returns dict of n_acc, y, c_star, ...)."""
     target, U, W2 = (np.ascontiguousarray(a) for a in (target, U, W2))
     dt = _dt_of(U)
@@ -213,13 +216,14 @@ def verify(target, U, W2, bias_rows, x, ell, seed=0, cycle=0):
     assert bias_rows.shape == (R, gamma, rank)
     x = _c(x, np.int32)
     ell = _c(ell, np.int32)
+    rid = None if req_ids is None else _c(req_ids, np.int32)
     n_acc = np.zeros(R, np.int32)
     y = np.zeros((R, gamma + 1), np.int32)
     c_star, pq, ua = (np.zeros((R, gamma)) for _ in range(3))
     gb, gi = np.zeros(R), np.zeros(R)
     rc = lib().ora_verify(R, gamma, V, rank, dt, _vp(target), _vp(U), _vp(W2),
                           _p(bias_rows, C.c_double), _p(x, C.c_int32), _p(ell, C.c_int32),
-                          seed, cycle, _p(n_acc, C.c_int32), _p(y, C.c_int32),
+                          _p(rid, C.c_int32), seed, cycle, _p(n_acc, C.c_int32), _p(y, C.c_int32),
                           _p(c_star, C.c_double), _p(pq, C.c_double), _p(ua, C.c_double),
                           _p(gb, C.c_double), _p(gi, C.c_double))
     if rc != 0:

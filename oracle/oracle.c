@@ -208,9 +208,9 @@ static int check_dims(int R, int gamma, int V, int rank, int d, int dt) {
  * ------------------------------------------------------------------------------------ */
 static int draft_common(int R, int gamma, int V, int rank, int d, int dt, const void *U,
                         const void *h, const void *W1, const void *W2, const void *W_gco,
-                        const float *w, const int32_t *x0, uint64_t seed, uint64_t cycle,
-                        int32_t *x, double *c, double *lse, double *logit_x,
-                        double *bias_rows, double *gap_blk, double *gap_in) {
+                        const float *w, const int32_t *x0, const int32_t *req_ids,
+                        uint64_t seed, uint64_t cycle, int32_t *x, double *c, double *lse,
+                        double *logit_x, double *bias_rows, double *gap_blk, double *gap_in) {
   if (check_dims(R, gamma, V, rank, d, dt)) return -1;
   int bad = 0;
   for (int r = 0; r < R; ++r)
@@ -252,8 +252,9 @@ static int draft_common(int R, int gamma, int V, int rank, int d, int dt, const 
       logits_row(V, rank, dt, U, rk * (size_t)V, W2, vec, l);
       double L = log_sum_exp(V, l);
       double gb = INFINITY, gi = INFINITY;
-      int xk = ora_sample_two_level(V, l, seed, cycle, ORA_S_DRAFT_BLK, ORA_S_DRAFT_IN,
-                                    (uint32_t)r, (uint32_t)k, &gb, &gi);
+      uint32_t rid = req_ids ? (uint32_t)req_ids[r] : (uint32_t)r;
+      int xk = ora_sample_two_level(V, l, seed, cycle, ORA_S_DRAFT_BLK, ORA_S_DRAFT_IN, rid,
+                                    (uint32_t)k, &gb, &gi);
       x[rk] = xk;
       c[rk] = confidence(d, rank, dt, h, rk * (size_t)d, w, e);
       lse[rk] = L;
@@ -270,21 +271,21 @@ static int draft_common(int R, int gamma, int V, int rank, int d, int dt, const 
 
 int ora_draft_markov(int R, int gamma, int V, int rank, int d, int dt, const void *U,
                      const void *h, const void *W1, const void *W2, const float *w,
-                     const int32_t *x0, uint64_t seed, uint64_t cycle, int32_t *x,
-                     double *c, double *lse, double *logit_x, double *bias_rows,
+                     const int32_t *x0, const int32_t *req_ids, uint64_t seed, uint64_t cycle,
+                     int32_t *x, double *c, double *lse, double *logit_x, double *bias_rows,
                      double *gap_blk, double *gap_in) {
-  return draft_common(R, gamma, V, rank, d, dt, U, h, W1, W2, NULL, w, x0, seed, cycle, x,
-                      c, lse, logit_x, bias_rows, gap_blk, gap_in);
+  return draft_common(R, gamma, V, rank, d, dt, U, h, W1, W2, NULL, w, x0, req_ids, seed,
+                      cycle, x, c, lse, logit_x, bias_rows, gap_blk, gap_in);
 }
 
 int ora_draft_rnn(int R, int gamma, int V, int rank, int d, int dt, const void *U,
                   const void *h, const void *W1, const void *W2, const void *W_gco,
-                  const float *w, const int32_t *x0, uint64_t seed, uint64_t cycle,
-                  int32_t *x, double *c, double *lse, double *logit_x, double *bias_rows,
-                  double *gap_blk, double *gap_in) {
+                  const float *w, const int32_t *x0, const int32_t *req_ids, uint64_t seed,
+                  uint64_t cycle, int32_t *x, double *c, double *lse, double *logit_x,
+                  double *bias_rows, double *gap_blk, double *gap_in) {
   if (!W_gco) return -1;
-  return draft_common(R, gamma, V, rank, d, dt, U, h, W1, W2, W_gco, w, x0, seed, cycle, x,
-                      c, lse, logit_x, bias_rows, gap_blk, gap_in);
+  return draft_common(R, gamma, V, rank, d, dt, U, h, W1, W2, W_gco, w, x0, req_ids, seed,
+                      cycle, x, c, lse, logit_x, bias_rows, gap_blk, gap_in);
 }
 
 /* ------------------------------------------------------------------------------------
@@ -454,7 +455,8 @@ int ora_schedule(int R, int gamma, const float *c, const float *c_lag, int R_lag
  * ------------------------------------------------------------------------------------ */
 int ora_verify(int R, int gamma, int V, int rank, int dt, const void *target,
                const void *U, const void *W2, const double *bias_rows, const int32_t *x,
-               const int32_t *ell, uint64_t seed, uint64_t cycle, int32_t *n_acc,
+               const int32_t *ell, const int32_t *req_ids, uint64_t seed, uint64_t cycle,
+               int32_t *n_acc,
                int32_t *y, double *c_star, double *pq_ratio, double *u_acc,
                double *gap_blk, double *gap_in) {
   if (check_dims(R, gamma, V, rank, 0, dt)) return -1;
@@ -472,6 +474,7 @@ int ora_verify(int R, int gamma, int V, int rank, int dt, const void *target,
     double *q = (double *)malloc(sizeof(double) * (size_t)V);
     double *wk = (double *)malloc(sizeof(double) * (size_t)V);
     const int l = ell[r];
+    const uint32_t rid = req_ids ? (uint32_t)req_ids[r] : (uint32_t)r;
     int jstar = 0; /* first rejected position, 0 = none */
     int32_t last = -1;
     double gb = INFINITY, gi = INFINITY;
@@ -496,7 +499,7 @@ int ora_verify(int R, int gamma, int V, int rank, int dt, const void *target,
       if (jstar) continue;
       int32_t xj = x[rj];
       double ratio = p[xj] / q[xj];
-      double u = ora_uniform(seed, cycle, ORA_S_ACCEPT, (uint32_t)r, (uint32_t)j, 0u);
+      double u = ora_uniform(seed, cycle, ORA_S_ACCEPT, rid, (uint32_t)j, 0u);
       if (pq_ratio) pq_ratio[rj] = ratio;
       if (u_acc) u_acc[rj] = u;
       if (u < ratio) continue; /* accepted */
@@ -514,15 +517,15 @@ int ora_verify(int R, int gamma, int V, int rank, int dt, const void *target,
       }
       if (!(mass > 0.0)) /* degenerate in floating point: fall back to p */
         for (int v = 0; v < V; ++v) wk[v] = t[v];
-      last = ora_sample_two_level(V, wk, seed, cycle, ORA_S_RESID_BLK, ORA_S_RESID_IN,
-                                  (uint32_t)r, (uint32_t)j, &gb, &gi);
+      last = ora_sample_two_level(V, wk, seed, cycle, ORA_S_RESID_BLK, ORA_S_RESID_IN, rid,
+                                  (uint32_t)j, &gb, &gi);
     }
     int na = jstar ? jstar - 1 : l;
     if (!jstar) {
       size_t trow = ((size_t)r * G1 + (size_t)l) * (size_t)V; /* row l+1 */
       for (int v = 0; v < V; ++v) t[v] = elem(target, dt, trow + (size_t)v);
-      last = ora_sample_two_level(V, t, seed, cycle, ORA_S_BONUS_BLK, ORA_S_BONUS_IN,
-                                  (uint32_t)r, (uint32_t)(l + 1), &gb, &gi);
+      last = ora_sample_two_level(V, t, seed, cycle, ORA_S_BONUS_BLK, ORA_S_BONUS_IN, rid,
+                                  (uint32_t)(l + 1), &gb, &gi);
     }
     n_acc[r] = na;
     for (size_t j = 0; j < G1; ++j) y[(size_t)r * G1 + j] = -1;

@@ -83,14 +83,16 @@ void ora_sample_trials(int n, const double *l, uint64_t seed, uint64_t cycle, in
 /* Markov-head draft, eqs. (4), (5), (7).  Layouts (row-major):
  *   U [R][gamma][V], h [R][gamma][d], W1 [V][rank], W2 [rank][V]   (dt)
  *   w [d + rank] fp32, order [h-part ; W1-row part]; x0 [R]
+ *   req_ids [R] (nullable): the request index each row uses in the random counters
+ *     (default: its position 0..R-1), so a subset of a batch can be checked alone
  * Outputs: x [R][gamma], c, lse, logit_x [R][gamma] (double),
  *   bias_rows [R][gamma][rank] (double): the vector that multiplies W2 at step k,
  *   gap_blk, gap_in [R][gamma] (nullable).
  * Returns 0, or -1 on a bad argument / token out of range. */
 int ora_draft_markov(int R, int gamma, int V, int rank, int d, int dt, const void *U,
                      const void *h, const void *W1, const void *W2, const float *w,
-                     const int32_t *x0, uint64_t seed, uint64_t cycle, int32_t *x,
-                     double *c, double *lse, double *logit_x, double *bias_rows,
+                     const int32_t *x0, const int32_t *req_ids, uint64_t seed, uint64_t cycle,
+                     int32_t *x, double *c, double *lse, double *logit_x, double *bias_rows,
                      double *gap_blk, double *gap_in);
 
 /* RNN-head draft, eq. (6) with eq. (7) for c.  W_gco [3*rank][2*rank + d] (dt): rows
@@ -99,9 +101,9 @@ int ora_draft_markov(int R, int gamma, int V, int rank, int d, int dt, const voi
  * ora_draft_markov. */
 int ora_draft_rnn(int R, int gamma, int V, int rank, int d, int dt, const void *U,
                   const void *h, const void *W1, const void *W2, const void *W_gco,
-                  const float *w, const int32_t *x0, uint64_t seed, uint64_t cycle,
-                  int32_t *x, double *c, double *lse, double *logit_x, double *bias_rows,
-                  double *gap_blk, double *gap_in);
+                  const float *w, const int32_t *x0, const int32_t *req_ids, uint64_t seed,
+                  uint64_t cycle, int32_t *x, double *c, double *lse, double *logit_x,
+                  double *bias_rows, double *gap_blk, double *gap_in);
 
 /* Prefix scheduler (Module E, Algorithm 1 and the production variants).
  *   c [R][gamma] fp32; c_lag [R_lag][gamma] (ASYNC_LAG2 only, else NULL)
@@ -120,7 +122,7 @@ int ora_schedule(int R, int gamma, const float *c, const float *c_lag, int R_lag
  *     bonus position gamma+1 (row l_r + 1 gives the bonus distribution).
  *   U [R][gamma][V] (dt), W2 [rank][V] (dt), bias_rows [R][gamma][rank] (double):
  *     q_j is recomputed from them as softmax(U_j + bias_j W2).
- *   x [R][gamma] drafted tokens, ell [R] scheduled lengths.
+ *   x [R][gamma] drafted tokens, ell [R] scheduled lengths, req_ids as in the draft.
  * Outputs: n_acc [R]; y [R][gamma+1] emitted tokens (n_acc+1 valid, rest -1);
  *   c_star [R][gamma] (NaN for j > ell); pq_ratio [R][gamma] p_j(x_j)/q_j(x_j) and
  *   u_acc [R][gamma] the acceptance uniforms (both nullable, NaN where not tested);
@@ -128,8 +130,8 @@ int ora_schedule(int R, int gamma, const float *c, const float *c_lag, int R_lag
  * Returns 0 or -1. */
 int ora_verify(int R, int gamma, int V, int rank, int dt, const void *target,
                const void *U, const void *W2, const double *bias_rows, const int32_t *x,
-               const int32_t *ell, uint64_t seed, uint64_t cycle, int32_t *n_acc,
-               int32_t *y, double *c_star, double *pq_ratio, double *u_acc,
+               const int32_t *ell, const int32_t *req_ids, uint64_t seed, uint64_t cycle,
+               int32_t *n_acc, int32_t *y, double *c_star, double *pq_ratio, double *u_acc,
                double *gap_blk, double *gap_in);
 
 /* Number of OpenMP threads the oracle uses (1 when built without OpenMP). */

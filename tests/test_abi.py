@@ -1,0 +1,94 @@
+"""Host-side checks of the C ABI: the library builds, loads and exports every declared
+symbol, and rejects bad arguments before touching a device (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def ds():
+    import draft_sampling_scheduling_amd as ds
+    if not os.path.exists(ds.LIB_PATH):
+        from draft_sampling_scheduling_amd import build
+        build.build()
+    ds.lib()
+    return ds
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dspark.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(ds):
+    names = _declared()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(ds.lib(), n), n
+    assert set(names) == set(ds.EXPORTS)
+    assert "gfx950" in ds.version()
+
+
+def test_workspace_sizes(ds):
+    a = ds.draft_workspace_bytes(256, 8, 151936, 256, 4096)
+    b = ds.draft_rnn_workspace_bytes(256, 8, 151936, 256, 4096)
+    assert 0 < a < b
+    assert ds.verify_workspace_bytes(256, 8, 151936, 256) > 0
+    assert ds.draft_workspace_bytes(4, 4, 1001, 16, 64) == 0   # V % 8 != 0
+    assert ds.draft_workspace_bytes(4, 4, 1024, 48, 64) == 0   # r not a power of two
+    assert ds.draft_workspace_bytes(4, 0, 1024, 16, 64) == 0   # gamma < 1
+
+
+FAKE = C.c_void_p(0x1000)  # never dereferenced: these calls return before any launch
+
+
+def test_draft_rejects_bad_arguments(ds):
+    L = ds.lib()
+    ws = ds.draft_workspace_bytes(4, 4, 1024, 16, 64)
+
+    def call(R=4, gamma=4, V=1024, r=16, d=64, dt=ds.F32, U=FAKE, ws_bytes=ws, cycle=0):
+        return L.dspark_draft_markov(R, gamma, V, r, d, dt, U, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                                     cycle, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_bytes,
+                                     None)
+
+    assert call(V=1001) == ds.EINVAL
+    assert call(r=24) == ds.EINVAL
+    assert call(dt=7) == ds.EINVAL
+    assert call(U=None) == ds.EINVAL
+    assert call(ws_bytes=ws - 1) == ds.EWORKSPACE
+    assert call(cycle=1 << 28) == ds.EINVAL
+    assert call(R=0) == ds.OK  # empty batch: nothing to do
+
+
+def test_schedule_rejects_bad_arguments(ds):
+    L = ds.lib()
+
+    def call(R=4, gamma=3, sps_B0=4, sps_len=13, mode=ds.SYNC_BREAK, c_lag=None, R_lag=0):
+        return L.dspark_schedule(R, gamma, FAKE, c_lag, R_lag, FAKE, sps_B0, sps_len, mode,
+                                 FAKE, None, None, None, None, 0, None)
+
+    assert call(sps_len=12) == ds.ERANGE      # must reach R(1+gamma) = 16
+    assert call(sps_B0=5, sps_len=20) == ds.ERANGE
+    assert call(mode=5) == ds.EINVAL
+    assert call(mode=ds.ASYNC_LAG2) == ds.EINVAL  # no lagged confidences
+    assert call(mode=ds.ASYNC_LAG2, c_lag=FAKE, R_lag=8) == ds.ERANGE  # 8*(1+3) > 16
+    assert call(R=1024, gamma=9, sps_B0=1, sps_len=20000) == ds.EINVAL  # R*gamma > 8192
+    assert call(gamma=0) == ds.EINVAL
+
+
+def test_verify_rejects_bad_arguments(ds):
+    L = ds.lib()
+    ws = ds.verify_workspace_bytes(4, 4, 1024, 16)
+
+    def call(dt=ds.BF16, bdt=ds.BF16, ws_bytes=ws, V=1024):
+        return L.dspark_verify(4, 4, V, 16, dt, FAKE, FAKE, FAKE, FAKE, bdt, FAKE, FAKE, FAKE,
+                               FAKE, 0, 0, FAKE, FAKE, FAKE, None, FAKE, ws_bytes, None)
+
+    assert call(dt=ds.F32, bdt=ds.BF16) == ds.EINVAL  # bias rows must be float or dt
+    assert call(ws_bytes=ws - 1) == ds.EWORKSPACE
+    assert call(V=1020) == ds.EINVAL

@@ -1,0 +1,95 @@
+"""GPU draft (dspark_draft_markov / dspark_draft_rnn) against the oracle on the same seeded
+inputs: tokens identical except counted near-ties, confidences and probabilities within
+1e-4, bias rows exact."""
+import numpy as np
+import pytest
+
+from draft_sampling_scheduling_amd import synth
+from tests.gpu_util import N, T, compare_draft, excuse_budget
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(ora, ds, cfg, seed=0, cycle=0, rnn=False):
+    I = synth.inputs(cfg)
+    W2t = np.ascontiguousarray(I["W2"].T)
+    if rnn:
+        o = ora.draft_rnn(I["U"], I["h"], I["W1"], I["W2"], I["W_gco"], I["w"], I["x0"], seed, cycle)
+        g = ds.draft_rnn(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["W_gco"]), T(I["w"]),
+                         T(I["x0"]), seed, cycle)
+    else:
+        o = ora.draft_markov(I["U"], I["h"], I["W1"], I["W2"], I["w"], I["x0"], seed, cycle)
+        g = ds.draft_markov(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(I["x0"]),
+                            seed, cycle)
+    g = {k: N(v) for k, v in g.items()}
+    if g["bias_rows"].dtype == np.uint16:
+        g["bias_rows"] = synth.bf16_to_f32(g["bias_rows"])
+    return I, o, g
+
+
+@pytest.fixture(scope="module")
+def ds():
+    import draft_sampling_scheduling_amd as ds
+    ds.lib()
+    return ds
+
+
+CASES = [
+    # name, base config, overrides
+    ("c1", "c1", {}),
+    ("c1-ragged", "c1", dict(R=5, V=1000, gamma=3)),
+    ("c2-R64", "c2", dict(gamma=4)),
+    ("c2-R37-V5000", "c2", dict(R=37, gamma=3, V=5000, d=512)),
+    ("c2-R150-r64", "c2", dict(R=150, gamma=3, V=3000, r=64, d=256)),
+    ("c2-R300-r128", "c2", dict(R=300, gamma=2, V=2056, r=128, d=128)),
+    ("c3-law-R20", "c3", dict(R=20, gamma=4, V=8192, d=512)),
+    ("c2-r16", "c2", dict(R=70, gamma=3, V=1024, r=16, d=64)),
+]
+
+
+@pytest.mark.parametrize("name,base,kw", CASES, ids=[c[0] for c in CASES])
+def test_markov_parity(ora, ds, name, base, kw):
+    cfg = synth.scaled(synth.CONFIGS[base], **kw)
+    I, o, g = _run(ora, ds, cfg, seed=7, cycle=3)
+    compared, excused = compare_draft(o, g, name)
+    print(f"{name}: compared {compared}, near-tie mismatches {excused}")
+    assert excused <= excuse_budget(compared)
+
+
+RNN_CASES = [
+    ("rnn-f32", "c5", dict(R=6, gamma=4, V=1024, r=16, d=64, dtype="f32")),
+    ("rnn-bf16", "c5", dict(R=40, gamma=4, V=4096, r=64, d=128)),
+    ("rnn-bf16-r256", "c5", dict(R=140, gamma=3, V=2048, r=256, d=256)),
+]
+
+
+@pytest.mark.parametrize("name,base,kw", RNN_CASES, ids=[c[0] for c in RNN_CASES])
+def test_rnn_parity(ora, ds, name, base, kw):
+    cfg = synth.scaled(synth.CONFIGS[base], **kw)
+    I, o, g = _run(ora, ds, cfg, seed=1, cycle=5, rnn=True)
+    compared, excused = compare_draft(o, g, name)
+    print(f"{name}: compared {compared}, near-tie mismatches {excused}")
+    assert excused <= excuse_budget(compared)
+
+
+def test_deterministic(ds):
+    cfg = synth.scaled(synth.CONFIGS["c2"], R=100, gamma=3, V=4096, d=256)
+    I = synth.inputs(cfg)
+    W2t = np.ascontiguousarray(I["W2"].T)
+    args = [T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(I["x0"])]
+    runs = [{k: N(v) for k, v in ds.draft_markov(*args, 3, 9).items()} for _ in range(3)]
+    for r in runs[1:]:
+        for k in r:
+            assert np.array_equal(r[k].view(np.uint8), runs[0][k].view(np.uint8)), k
+
+
+def test_bad_anchor_sets_fault_bit(ds):
+    import torch
+    cfg = synth.scaled(synth.CONFIGS["c2"], R=8, gamma=2, V=1024, d=64)
+    I = synth.inputs(cfg)
+    x0 = I["x0"].copy()
+    x0[3] = cfg.V + 5
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    W2t = np.ascontiguousarray(I["W2"].T)
+    ds.draft_markov(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(x0), status=status)
+    assert int(N(status)[0]) & ds.FAULT_TOKEN

@@ -1,0 +1,78 @@
+"""GPU scheduler (dspark_schedule) against the oracle: ell, a and stats bit-exact in every
+mode, on workload-shaped and adversarial confidences."""
+import numpy as np
+import pytest
+
+from draft_sampling_scheduling_amd import synth
+from tests.gpu_util import N, T
+
+pytestmark = pytest.mark.gpu
+MODES = (0, 1, 2)
+
+
+@pytest.fixture(scope="module")
+def ds():
+    import draft_sampling_scheduling_amd as ds
+    ds.lib()
+    return ds
+
+
+def _conf_sets():
+    rng = np.random.default_rng(42)
+    out = []
+    out.append(("beta-c3", rng.beta(6, 1.6, (256, 8)).astype(np.float32), 1, "c3"))
+    c = rng.choice(np.array([1.0, 1.0, 1.0, 0.5, 0.0, 0.999], np.float32), (100, 8))
+    out.append(("exact-ones-zeros", c, 1, "smooth"))
+    c = np.full((64, 16), 0.02, np.float32)
+    c[::3] = 1e-10  # subnormal running products
+    out.append(("subnormal", c, 1, "smooth"))
+    out.append(("all-equal", np.full((300, 5), 0.9, np.float32), 1, "smooth"))
+    c = rng.beta(8, 1.5, (512, 16)).astype(np.float32)
+    c[1::2] = rng.beta(2, 2, (256, 16))
+    out.append(("c4-size", c, 1, "c4"))
+    out.append(("R1", np.array([[0.8, 0.9]], np.float32), 1, "appendix"))
+    out.append(("ragged-37x7", rng.uniform(0, 1, (37, 7)).astype(np.float32), 1, "smooth"))
+    return out
+
+
+def _sps(kind, R, gamma):
+    B = np.arange(1, R * (gamma + 1) + 1, dtype=np.float64)
+    if kind == "appendix":
+        return np.array([1.0, 0.5, 0.45], np.float32), 1
+    if kind == "c4":
+        cfg = synth.CONFIGS["c4"]
+        return synth.sps_table(cfg), cfg.sps_B0
+    if kind == "c3":
+        cfg = synth.CONFIGS["c3"]
+        return synth.sps_table(cfg), cfg.sps_B0
+    return (1.0 / (1.0 + 0.01 * B + 0.03 * np.floor(B / 37))).astype(np.float32), 1
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", range(7))
+def test_schedule_bit_exact(ora, ds, mode, case):
+    name, c, _, kind = _conf_sets()[case]
+    R, gamma = c.shape
+    sps, B0 = _sps(kind, R, gamma)
+    c_lag = None
+    if mode == 2:
+        rng = np.random.default_rng(case)
+        # the lagged batch must lie inside the table: workload tables start at B = R
+        Rl = R if kind in ("c3", "c4") else max(1, R - 3)
+        c_lag = np.clip(c[:Rl] + rng.normal(0, 0.05, (Rl, gamma)), 0, 1).astype(np.float32)
+    o = ora.schedule(c, sps, B0, mode, c_lag=c_lag)
+    g = ds.schedule(T(c), T(sps), B0, mode, c_lag=None if c_lag is None else T(c_lag))
+    g = {k: N(v) for k, v in g.items()}
+    assert np.array_equal(g["a"].view(np.uint32), o["a"].view(np.uint32)), name
+    assert np.array_equal(g["ell"], o["ell"]), (name, np.nonzero(g["ell"] != o["ell"]))
+    assert np.array_equal(g["stats"].view(np.uint64), o["stats"].view(np.uint64)), (name, g["stats"], o["stats"])
+
+
+def test_confidence_fault_bit(ds):
+    import torch
+    c = np.full((4, 3), 0.5, np.float32)
+    c[2, 1] = np.nan
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    sps = np.ones(16, np.float32)
+    ds.schedule(T(c), T(sps), 1, 0, status=status)
+    assert int(N(status)[0]) & ds.FAULT_CONF

@@ -1,0 +1,119 @@
+"""GPU verification (dspark_verify) against the oracle on inputs the oracle drafted:
+accepted counts and emitted tokens identical except counted near-ties, c* within 1e-4."""
+import numpy as np
+import pytest
+
+from draft_sampling_scheduling_amd import synth
+from tests.gpu_util import ACC_EXCUSE, N, T, TIE_GAP, TOL_P, excuse_budget
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ds():
+    import draft_sampling_scheduling_amd as ds
+    ds.lib()
+    return ds
+
+
+def _inputs(ora, cfg, cycle, ell_kind, rnn=False):
+    I = synth.inputs(cfg)
+    if rnn:
+        d = ora.draft_rnn(I["U"], I["h"], I["W1"], I["W2"], I["W_gco"], I["w"], I["x0"], 0, cycle)
+    else:
+        d = ora.draft_markov(I["U"], I["h"], I["W1"], I["W2"], I["w"], I["x0"], 0, cycle)
+    # synthetic target-model stand-in: the drafted logits plus noise; bonus row fresh
+    U = synth.decode(cfg, I["U"]).astype(np.float64)
+    W2 = synth.decode(cfg, I["W2"]).astype(np.float64)
+    logits = U + np.einsum("qkr,rv->qkv", d["bias_rows"], W2)
+    noise, fresh = synth.target_parts(cfg, range(cfg.R), cycle)
+    tgt = np.concatenate([logits, fresh[:, None, :]], axis=1) + noise
+    target = synth.encode(cfg, tgt.astype(np.float32))
+    rng = np.random.default_rng(cycle)
+    if ell_kind == "sched":
+        s = ora.schedule(d["c"].astype(np.float32), synth.sps_table(cfg), cfg.sps_B0, 0)
+        ell = s["ell"]
+    elif ell_kind == "full":
+        ell = np.full(cfg.R, cfg.gamma, np.int32)
+    else:
+        ell = rng.integers(0, cfg.gamma + 1, cfg.R).astype(np.int32)
+        ell[0] = 0
+        ell[-1] = cfg.gamma
+    return I, d, target, ell
+
+
+def _compare(o, g, d, ell, gamma, label):
+    excused = 0
+    R = len(ell)
+    for q in range(R):
+        L = ell[q]
+        np.testing.assert_allclose(g["c_star"][q, :L], o["c_star"][q, :L], atol=TOL_P, err_msg=label)
+        assert np.all(np.isnan(g["c_star"][q, L:])), (label, q)
+        if g["n_acc"][q] != o["n_acc"][q]:
+            j = min(g["n_acc"][q], o["n_acc"][q])  # first differing acceptance test (0-based)
+            gap = abs(o["u_acc"][q, j] - o["pq_ratio"][q, j])
+            assert gap < ACC_EXCUSE, (label, "acceptance differs off a near-tie", q, j, gap)
+            excused += 1
+            continue
+        na = o["n_acc"][q]
+        assert np.array_equal(g["y"][q, :na], o["y"][q, :na]), (label, q)
+        assert np.all(g["y"][q, na + 1:] == -1), (label, q)
+        if g["y"][q, na] != o["y"][q, na]:
+            assert min(o["gap_blk"][q], o["gap_in"][q]) < TIE_GAP, (label, "final token differs", q)
+            excused += 1
+    return excused
+
+
+CASES = [
+    ("c1-sched", "c1", {}, "sched"),
+    ("c1-random", "c1", dict(R=9, V=1000), "random"),
+    ("c2-random", "c2", dict(R=48, gamma=5, V=6000, d=256), "random"),
+    ("c2-full", "c2", dict(R=33, gamma=4, V=4096, d=128, r=128), "full"),
+    ("c2-sched", "c2", dict(R=64, gamma=4, V=8192, d=256), "sched"),
+    ("c3-law", "c3", dict(R=40, gamma=6, V=16384, d=256), "random"),
+]
+
+
+@pytest.mark.parametrize("name,base,kw,ell_kind", CASES, ids=[c[0] for c in CASES])
+def test_verify_parity(ora, ds, name, base, kw, ell_kind):
+    cfg = synth.scaled(synth.CONFIGS[base], **kw)
+    cycle = 4
+    I, d, target, ell = _inputs(ora, cfg, cycle, ell_kind)
+    o = ora.verify(target, I["U"], I["W2"], d["bias_rows"], d["x"], ell, seed=0, cycle=cycle)
+    brows = synth.encode(cfg, d["bias_rows"].astype(np.float32))  # exact: rows of W1
+    W2t = np.ascontiguousarray(I["W2"].T)
+    g = ds.verify(T(target), T(I["U"]), T(W2t), T(brows), T(d["x"]),
+                  T(d["lse"].astype(np.float32)), T(d["logit_x"].astype(np.float32)), T(ell),
+                  seed=0, cycle=cycle)
+    g = {k: N(v) for k, v in g.items()}
+    excused = _compare(o, g, d, ell, cfg.gamma, name)
+    print(f"{name}: rows {int(ell.sum())}, accepted {int(o['n_acc'].sum())}, excused {excused}")
+    assert excused <= excuse_budget(int(ell.sum()) + cfg.R)
+
+
+def test_verify_rnn_float_bias_rows(ora, ds):
+    cfg = synth.scaled(synth.CONFIGS["c5"], R=24, gamma=4, V=4096, r=64, d=128)
+    cycle = 2
+    I, d, target, ell = _inputs(ora, cfg, cycle, "random", rnn=True)
+    o = ora.verify(target, I["U"], I["W2"], d["bias_rows"], d["x"], ell, seed=0, cycle=cycle)
+    W2t = np.ascontiguousarray(I["W2"].T)
+    g = ds.verify(T(target), T(I["U"]), T(W2t), T(d["bias_rows"].astype(np.float32)), T(d["x"]),
+                  T(d["lse"].astype(np.float32)), T(d["logit_x"].astype(np.float32)), T(ell),
+                  seed=0, cycle=cycle)
+    g = {k: N(v) for k, v in g.items()}
+    excused = _compare(o, g, d, ell, cfg.gamma, "rnn")
+    assert excused <= excuse_budget(int(ell.sum()) + cfg.R)
+
+
+def test_length_fault_bit(ora, ds):
+    import torch
+    cfg = synth.scaled(synth.CONFIGS["c2"], R=4, gamma=3, V=1024, d=64)
+    I, d, target, ell = _inputs(ora, cfg, 0, "random")
+    ell = ell.copy()
+    ell[1] = 9
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    W2t = np.ascontiguousarray(I["W2"].T)
+    brows = synth.encode(cfg, d["bias_rows"].astype(np.float32))
+    ds.verify(T(target), T(I["U"]), T(W2t), T(brows), T(d["x"]), T(d["lse"].astype(np.float32)),
+              T(d["logit_x"].astype(np.float32)), T(ell), status=status)
+    assert int(N(status)[0]) & ds.FAULT_LEN
