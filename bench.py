@@ -1,0 +1,297 @@
+#!/usr/bin/env python
+"""Throughput of one DSpark decode cycle (draft -> schedule -> verify) on one MI355X.
+
+A step is one whole cycle of the hot path on the headline workload (R=256 requests, gamma=8
+draft positions, V=151936, r=256, d=4096, bf16 operands with fp32 softmax):
+  dspark_draft_markov  (gamma vocabulary sweeps + combines)
+  dspark_schedule      (Algorithm 1 with the early-stop break)
+  dspark_verify        (rejection sampling of the scheduled prefixes, c*)
+All inputs are seeded synthetic tensors already resident in device memory.  The target
+logits that verification reads are a synthetic stand-in for the target model (the drafted
+logits plus noise, plus a fresh bonus row), built once before timing for the cycle's drafted
+tokens; every timed step redoes the whole cycle on the same inputs and seed, so the drafted
+tokens and the target stay consistent.
+
+Printed: one JSON line with the metric, the roofline of the dominant kernel (the draft
+sweep, timed live with HIP events around each of its launches), and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "draft+verify tokens/s at R=256 γ=8 V=151936; % of HBM roofline"
+SEED = 0
+CYCLE = 1
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c3", help="workload: c3 (headline) or c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def hip_events(n):
+    hip = C.CDLL("libamdhip64.so.7")  # the runtime PyTorch already loaded
+    hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+    arr = (C.c_void_p * n)()
+    for i in range(n):
+        ev = C.c_void_p()
+        if hip.hipEventCreate(C.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        arr[i] = ev
+    return hip, arr
+
+
+def elapsed_ms(hip, a, b) -> float:
+    ms = C.c_float()
+    if hip.hipEventElapsedTime(C.byref(ms), a, b) != 0:
+        raise RuntimeError("hipEventElapsedTime failed")
+    return ms.value
+
+
+def make_target(torch, cfg, U, W2t, d, gen):
+    """Synthetic target-model stand-in: drafted logits + N(0, s^2) noise for rows 1..gamma,
+    a fresh Zipf-ranked row + noise for the bonus row (built on the device, untimed)."""
+    R, G, V = cfg.R, cfg.gamma, cfg.V
+    noise = cfg.target_noise
+    tgt = torch.empty((R, G + 1, V), dtype=torch.bfloat16, device=U.device)
+    W2f = W2t.float().t().contiguous()  # [r][V]
+    base = -1.1 * torch.log(torch.arange(1, V + 1, device=U.device, dtype=torch.float32))
+    for q0 in range(0, R, 32):
+        q1 = min(R, q0 + 32)
+        br = d["bias_rows"][q0:q1].float()                          # [n, G, r]
+        logits = U[q0:q1].float() + torch.matmul(br, W2f)           # [n, G, V]
+        logits += noise * torch.randn(logits.shape, device=U.device, generator=gen)
+        tgt[q0:q1, :G] = logits.to(torch.bfloat16)
+        fresh = torch.stack([base[torch.randperm(V, device=U.device, generator=gen)]
+                             for _ in range(q1 - q0)])
+        fresh += torch.randn(fresh.shape, device=U.device, generator=gen)
+        fresh += noise * torch.randn(fresh.shape, device=U.device, generator=gen)
+        tgt[q0:q1, G] = fresh.to(torch.bfloat16)
+    return tgt
+
+
+def cpu_baseline(cfg, I, target_seconds):
+    """The oracle, untuned, on the host cores: draft + schedule + verify of a sample of the
+    workload's requests (the first S, same inputs), timed wall-clock."""
+    import numpy as np
+
+    import oracle
+    from draft_sampling_scheduling_amd import synth
+
+    oracle.lib()
+    threads = oracle.num_threads()
+    W2 = I["W2"]
+
+    def run(S):
+        reqs = np.arange(S)
+        U = I["U"][:S]
+        h = I["h"][:S]
+        t0 = time.perf_counter()
+        d = oracle.draft_markov(U, h, I["W1"], W2, I["w"], I["x0"][:S], SEED, CYCLE,
+                                req_ids=reqs)
+        t_draft = time.perf_counter() - t0
+        sps = (1.0 / (1.0 + cfg.sps_alpha * np.arange(S, S * (cfg.gamma + 1) + 1))).astype(np.float32)
+        t0 = time.perf_counter()
+        s = oracle.schedule(d["c"].astype(np.float32), sps, S, oracle.SYNC_BREAK)
+        t_sched = time.perf_counter() - t0
+        # target stand-in for the sample (untimed)
+        logits = synth.decode(cfg, U).astype(np.float64)
+        logits += np.einsum("qkr,rv->qkv", d["bias_rows"], synth.decode(cfg, W2).astype(np.float64))
+        noise, fresh = synth.target_parts(cfg, range(S), CYCLE)
+        tgt = synth.encode(cfg, (np.concatenate([logits, fresh[:, None, :]], axis=1) + noise)
+                           .astype(np.float32))
+        del logits, noise
+        t0 = time.perf_counter()
+        oracle.verify(tgt, U, W2, d["bias_rows"], d["x"], s["ell"], SEED, CYCLE, req_ids=reqs)
+        t_verify = time.perf_counter() - t0
+        return t_draft + t_sched + t_verify, int(s["ell"].sum())
+
+    # calibrate on one request per thread, then size the sample for the target wall time
+    t1, _ = run(threads)
+    S = int(threads * max(1.0, target_seconds / max(t1, 1e-3)))
+    S = max(threads, min(cfg.R, (S // threads) * threads))
+    t, nver = run(S) if S != threads else (t1, None)
+    return dict(value=S * cfg.gamma / t, unit="drafted tokens/s", cores=threads, kind="oracle",
+                sample=f"first {S} of {cfg.R} requests of the same workload: draft (gamma={cfg.gamma}, "
+                       f"V={cfg.V}, fp64), schedule (early stop) and verify; {t:.1f} s wall")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (this build shows one GPU's share of the path); "
+              f"--gpus {args.gpus} / WORLD_SIZE={world} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_sampling_scheduling_amd as ds
+    from draft_sampling_scheduling_amd import synth
+
+    ds.lib()  # fails loudly if the HIP library is missing
+    cfg = synth.CONFIGS[args.config]
+    if cfg.head != "markov" or cfg.dtype != "bf16":
+        raise SystemExit("bench.py times the bf16 Markov-head workloads (c2, c3)")
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    I = synth.inputs(cfg)
+
+    def T(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    U, h, W1, w, x0 = T(I["U"]), T(I["h"]), T(I["W1"]), T(I["w"]), T(I["x0"])
+    W2t = T(np.ascontiguousarray(I["W2"].T))
+    sps = T(synth.sps_table(cfg))
+    R, G, V, r, d = cfg.R, cfg.gamma, cfg.V, cfg.r, cfg.d
+    gen_s = time.perf_counter() - t_gen
+    log(f"inputs of {cfg.name} resident on the device ({gen_s:.1f} s)")
+
+    # outputs and workspaces allocated once
+    dout = dict(x=torch.empty((R, G), dtype=torch.int32, device=dev),
+                c=torch.empty((R, G), dtype=torch.float32, device=dev),
+                lse=torch.empty((R, G), dtype=torch.float32, device=dev),
+                logit_x=torch.empty((R, G), dtype=torch.float32, device=dev),
+                bias_rows=torch.empty((R, G, r), dtype=torch.bfloat16, device=dev))
+    sout = dict(ell=torch.empty(R, dtype=torch.int32, device=dev),
+                a=torch.empty((R, G), dtype=torch.float32, device=dev),
+                stats=torch.empty(4, dtype=torch.float64, device=dev))
+    vout = dict(n_acc=torch.empty(R, dtype=torch.int32, device=dev),
+                y=torch.empty((R, G + 1), dtype=torch.int32, device=dev),
+                c_star=torch.empty((R, G), dtype=torch.float32, device=dev))
+    dws = torch.empty(ds.draft_workspace_bytes(R, G, V, r, d), dtype=torch.uint8, device=dev)
+    vws = torch.empty(ds.verify_workspace_bytes(R, G, V, r), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    # the cycle's drafted tokens, then the target stand-in for them
+    ds.draft_markov(U, h, W1, W2t, w, x0, SEED, CYCLE, out=dout, ws=dws, status=status)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    target = make_target(torch, cfg, U, W2t, dout, gen)
+    torch.cuda.synchronize()
+    log("target stand-in built")
+
+    nsteps = args.warmup + args.steps
+    hip, evs = hip_events(2 * G * nsteps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nsteps)]
+
+    def step(i):
+        e = ev[i]
+        e[0].record()
+        evb = C.cast(C.addressof(evs) + (2 * G * i) * C.sizeof(C.c_void_p), C.POINTER(C.c_void_p))
+        eve = C.cast(C.addressof(evs) + (2 * G * i + G) * C.sizeof(C.c_void_p), C.POINTER(C.c_void_p))
+        ds.draft_markov(U, h, W1, W2t, w, x0, SEED, CYCLE, out=dout, ws=dws, status=status,
+                        events=(evb, eve))
+        e[1].record()
+        ds.schedule(dout["c"], sps, cfg.sps_B0, ds.SYNC_BREAK, out=sout, status=status)
+        e[2].record()
+        ds.verify(target, U, W2t, dout["bias_rows"], dout["x"], dout["lse"], dout["logit_x"],
+                  sout["ell"], SEED, CYCLE, out=vout, ws=vws, status=status)
+        e[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"{args.steps} timed cycles: {wall * 1e3 / args.steps:.3f} ms each")
+    if int(status.item()) != 0:
+        raise SystemExit(f"device fault bits set: {int(status.item())}")
+
+    timed = range(args.warmup, nsteps)
+    t_draft = np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in timed])
+    t_sched = np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in timed])
+    t_ver = np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in timed])
+    sweep_ms = np.mean([elapsed_ms(hip, evs[2 * G * i + k], evs[2 * G * i + G + k])
+                        for i in timed for k in range(G)])
+    ms_per_step = wall * 1000.0 / args.steps
+    n_acc = vout["n_acc"].cpu().numpy()
+    ell = sout["ell"].cpu().numpy()
+    emitted = int(n_acc.sum()) + R
+
+    # algorithmic bytes of one draft sweep launch: U_k rows, all of W2, the gathered W1 rows
+    sweep_bytes = R * V * 2 + V * r * 2 + R * r * 2
+    achieved = sweep_bytes / (sweep_ms * 1e-3) / 1e9
+    n_a, n_b = int(ell.sum()) + R, int(ell.sum())
+    cycle_bytes = (G * sweep_bytes + R * G * d * 2) + (n_a * V * 2 + n_b * V * 2 + V * r * 2)
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "draft_sweep_c3_traffic.json")
+    if args.config == "c3" and os.path.exists(prof):
+        try:
+            tr = json.load(open(prof))
+            if tr.get("kernel_source_sha") == kernel_sha():
+                traffic = tr.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": METRIC,
+        "value": R * G / (ms_per_step * 1e-3),
+        "unit": "drafted tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Markov head R={R} gamma={G} V={V} r={r} d={d}, "
+                               "bf16 operands, fp32 softmax; draft + schedule (early stop) + verify",
+                   "R": R, "gamma": G, "V": V, "r": r, "d": d},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "draft sweep (sweep_kernel<2,false,DraftEpi<false>>)",
+                     "bytes_per_launch": sweep_bytes, "launch_us": sweep_ms * 1e3},
+        "emitted_tokens_per_s": emitted / (ms_per_step * 1e-3),
+        "stage_ms": {"draft": t_draft, "schedule": t_sched, "verify": t_ver},
+        "cycle_hbm_frac": cycle_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "verified_rows": n_b, "accepted": int(n_acc.sum()), "mean_ell": float(ell.mean()),
+        "input_gen_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline(cfg, I, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("dev.h", "sweep.h", "draft.hip"):
+        h.update(open(os.path.join(ROOT, "draft_sampling_scheduling_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -20,7 +20,7 @@ F32, BF16 = 0, 1
 SYNC_BREAK, GLOBAL, ASYNC_LAG2 = 0, 1, 2
 OK, EINVAL, ERANGE, EWORKSPACE, EDEVICE = 0, -1, -2, -3, -4
 FAULT_TOKEN, FAULT_CONF, FAULT_LEN = 1, 2, 4
-EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov",
+EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov", "dspark_draft_markov_timed",
            "dspark_draft_rnn_workspace_bytes", "dspark_draft_rnn",
            "dspark_schedule_workspace_bytes", "dspark_schedule",
            "dspark_verify_workspace_bytes", "dspark_verify", "dspark_version")
@@ -43,6 +43,10 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run `python __graft_entry__.py` "
                                "(or draft_sampling_scheduling_amd.build.build())")
+        # load PyTorch's HIP runtime first: the library then binds to that same runtime
+        # (one libamdhip64.so.7 per process), so torch streams are valid handles for it
+        import torch  # noqa: F401
+
         L = C.CDLL(LIB_PATH)
         i, u64, sz, vp = C.c_int, C.c_uint64, C.c_size_t, C.c_void_p
         L.dspark_draft_workspace_bytes.argtypes = [i] * 5
@@ -52,6 +56,8 @@ def lib():
         L.dspark_draft_markov.argtypes = ([i] * 6 + [vp] * 6 + [u64, u64] + [vp] * 6 +
                                           [vp, sz, vp])
         L.dspark_draft_markov.restype = i
+        L.dspark_draft_markov_timed.argtypes = L.dspark_draft_markov.argtypes + [vp, vp]
+        L.dspark_draft_markov_timed.restype = i
         L.dspark_draft_rnn.argtypes = ([i] * 6 + [vp] * 7 + [u64, u64] + [vp] * 6 +
                                        [vp, sz, vp])
         L.dspark_draft_rnn.restype = i
@@ -138,7 +144,8 @@ def draft_rnn_workspace_bytes(R, gamma, V, r, d) -> int:
     return int(lib().dspark_draft_rnn_workspace_bytes(R, gamma, V, r, d))
 
 
-def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, out=None, ws=None, status=None):
+def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, out=None, ws=None, status=None,
+           events=None):
     torch = _torch()
     _chk(U, "U")
     R, gamma, V = U.shape
@@ -172,13 +179,19 @@ def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, out=None, ws=None
              _p(out["logit_x"]), _p(out["bias_rows"]), _p(status), _p(ws),
              ws.numel() * ws.element_size(), _stream()]
     fn = "dspark_draft_rnn" if rnn else "dspark_draft_markov"
+    if events is not None:  # (begin, end): ctypes arrays of gamma hipEvent_t each
+        fn = "dspark_draft_markov_timed"
+        args += [C.cast(events[0], C.c_void_p), C.cast(events[1], C.c_void_p)]
     _raise(fn, getattr(lib(), fn)(*args))
     return out
 
 
-def draft_markov(U, h, W1, W2t, w, x0, seed=0, cycle=0, *, out=None, ws=None, status=None):
-    """Markov-head draft; returns dict(x, c, lse, logit_x, bias_rows) (device tensors)."""
-    return _draft(False, U, h, W1, W2t, w, x0, seed, cycle, out=out, ws=ws, status=status)
+def draft_markov(U, h, W1, W2t, w, x0, seed=0, cycle=0, *, out=None, ws=None, status=None,
+                 events=None):
+    """Markov-head draft; returns dict(x, c, lse, logit_x, bias_rows) (device tensors).
+    events=(begin, end) arrays of gamma hipEvent_t selects the timed variant."""
+    return _draft(False, U, h, W1, W2t, w, x0, seed, cycle, out=out, ws=ws, status=status,
+                  events=events)
 
 
 def draft_rnn(U, h, W1, W2t, W_gco, w, x0, seed=0, cycle=0, *, out=None, ws=None, status=None):

@@ -73,12 +73,19 @@ __device__ __forceinline__ float uniform_of(uint32_t w) {
   return (float)(2u * (w >> 9) + 1u) * 0x1p-24f;
 }
 
-// g = -ln(-ln u).  -ln u is formed as -log1p(-(1-u)) above 1/2 (1-u is exact there) so
-// that the largest noise values, which decide the argmax, keep full relative accuracy.
+// g = -ln(-ln u), branch-free.  -ln u is taken from the hardware log2 except when
+// e = 1 - u (exact: u is an odd multiple of 2^-24) is below 2^-7, where the series
+// e + e^2/2 + e^3/3 + e^4/4 keeps full relative accuracy for the largest noise values,
+// which decide the argmax.
 __device__ __forceinline__ float gumbel_of(uint32_t w) {
-  const float u = uniform_of(w);
-  const float t = (u > 0.5f) ? -log1pf(-(1.0f - u)) : -logf(u);
-  return -logf(t);
+  constexpr float kLn2 = 0.69314718055994531f;
+  const uint32_t k = w >> 9;
+  const float u = (float)(2u * k + 1u) * 0x1p-24f;
+  const float e = (float)(0xFFFFFFu - 2u * k) * 0x1p-24f;
+  const float t_log = -__builtin_amdgcn_logf(u) * kLn2;
+  const float t_ser = e * (1.0f + e * (0.5f + e * (0.333333343f + e * 0.25f)));
+  const float t = (e < 0x1p-7f) ? t_ser : t_log;
+  return -__builtin_amdgcn_logf(t) * kLn2;
 }
 
 // ----------------------------------------------------------------------------------------
@@ -116,16 +123,11 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// merge of two (max, sum of exp(l - max)) pairs; -inf maxima carry zero mass
+// merge of two (max, sum of exp(l - max)) pairs; -inf maxima carry zero mass (branch-free)
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float mm = fmaxf(m, m2);
-  if (mm == -INFINITY) {
-    m = mm;
-    s = 0.0f;
-    return;
-  }
-  s = ((m == -INFINITY) ? 0.0f : s * __expf(m - mm)) +
-      ((m2 == -INFINITY) ? 0.0f : s2 * __expf(m2 - mm));
+  const float ref = (mm == -INFINITY) ? 0.0f : mm;
+  s = s * __expf(m - ref) + s2 * __expf(m2 - ref);
   m = mm;
 }
 

@@ -60,15 +60,14 @@ struct DraftSweepParams {
 
 template <bool RNN>
 struct DraftEpi {
+  static constexpr int kStreams = 1;  // U_k
   using Params = DraftSweepParams;
   struct State {
-    float M, S, G;
-    int B;
-    int grp;
+    float M, S, G;  // running normaliser (max, sum exp) and best block score of the range
+    int B;          // best block
+    int grp;        // block group (4 blocks) whose random words are cached
     uint4 words;
-  };
-  struct Pre {
-    uint4 u[2][2][2];  // [nt][mt][chunk]
+    float hm, hs;   // (max, sum exp) of the first half of the current block
   };
   __device__ static bool group_live(const Params& p, int row0) { return row0 < p.R; }
   __device__ static int nrows(const Params& p) { return p.R; }
@@ -77,6 +76,10 @@ struct DraftEpi {
     const int32_t t = checked_token(p.prev[(size_t)row * p.prev_stride], p.V, p.status);
     return p.W1 + (size_t)t * p.r;
   }
+  __device__ static const uint16_t* sbase(const Params& p, int) { return p.U; }
+  __device__ static uint32_t srow(const Params& p, int, int row) {
+    return (uint32_t)((size_t)row * p.ustride);
+  }
   __device__ static void init(const Params&, State& s, int) {
     s.M = -INFINITY;
     s.S = 0.0f;
@@ -84,80 +87,60 @@ struct DraftEpi {
     s.B = 0x7fffffff;
     s.grp = -1;
     s.words = make_uint4(0, 0, 0, 0);
+    s.hm = -INFINITY;
+    s.hs = 0.0f;
   }
-  template <int NT>
-  __device__ static void prefetch(const Params& p, Pre& pre, int b, int rowbase) {
-    const int lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int row = rowbase + 32 * nt + n;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int v = b * kVB + 32 * mt + 16 * h;
-        const bool ok = row < p.R && v < p.V;
-        const uint16_t* src = p.U + (size_t)row * p.ustride + v;
-        pre.u[nt][mt][0] = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
-        pre.u[nt][mt][1] =
-            (ok && v + 8 < p.V) ? *reinterpret_cast<const uint4*>(src + 8) : make_uint4(0, 0, 0, 0);
-      }
+  // random words of block b's group of four (uniform value across the wave)
+  __device__ static void refresh(const Params& p, State& s, int b, int row) {
+    if ((b >> 2) != s.grp) {
+      s.grp = b >> 2;
+      s.words = Rng(p.seed, p.cycle).block(kStreamDraftBlk, (uint32_t)row, p.k, (uint32_t)s.grp);
     }
   }
-  template <int NT>
-  __device__ static void block(const Params& p, State& s, const Pre& pre,
-                               const f32x16 (&acc)[NT][2], int b, int rowbase, int myrow) {
-    const int lane = threadIdx.x & 63, h = lane >> 5;
-    float mb[NT], sb[NT];
+  // one 32-id tile (half HALF of block b): the tile's (max, sum exp) joins the other half;
+  // after the second half the block's LSE_b feeds the row normaliser and LSE_b + g_b the
+  // running first-level Gumbel-max.  Branch-free unless MASK.
+  template <int HALF, bool MASK>
+  __device__ static void tile(const Params& p, State& s, const f32x16& acc, const uint4 (&)[2],
+                              int b, int row, bool owner) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const int h = (threadIdx.x & 63) >> 5;
+    float l[16];  // U_k + bias (the accumulator was seeded with U_k)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float l[32];
+    for (int j = 0; j < 16; ++j) l[j] = acc[j];
+    if (MASK) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int v0 = b * kVB + 32 * mt + 16 * h;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint4 u = pre.u[nt][mt][c];
-          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 8 * c + e;
-            const float uv = (e & 1) ? bf16hi(w4[e >> 1]) : bf16lo(w4[e >> 1]);
-            l[16 * mt + j] = (v0 + j < p.V) ? acc[nt][mt][j] + uv : -INFINITY;
-          }
-        }
-      }
-      float m = l[0];
-#pragma unroll
-      for (int j = 1; j < 32; ++j) m = fmaxf(m, l[j]);
-      float sum = 0.0f;
-      if (m != -INFINITY) {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) sum += __expf(l[j] - m);
-      }
-      const float m2 = __shfl_xor(m, 32, kWave);
-      const float s2 = __shfl_xor(sum, 32, kWave);
-      lse_merge(m, sum, m2, s2);
-      mb[nt] = m;
-      sb[nt] = sum;
+      for (int j = 0; j < 16; ++j)
+        if (b * kVB + kTile * HALF + vocab_of_reg(h, j) >= p.V) l[j] = -INFINITY;
     }
-    if (myrow < 0 || myrow >= p.R) return;
-    const int mine = (NT == 2) ? h : 0;
-    const float m = mb[mine], sum = sb[mine];
-    lse_merge(s.M, s.S, m, sum);
-    const float lse_b = m + __logf(sum);
-    const int grp = b >> 2;
-    if (grp != s.grp) {
-      s.grp = grp;
-      s.words = Rng(p.seed, p.cycle).block(kStreamDraftBlk, (uint32_t)myrow, p.k, (uint32_t)grp);
+    float m = fmaxf(fmaxf(l[0], l[1]), l[2]);
+#pragma unroll
+    for (int j = 3; j < 15; j += 2) m = fmaxf(fmaxf(m, l[j]), l[j + 1]);
+    m = fmaxf(m, l[15]);
+    const float ref = (m == -INFINITY) ? 0.0f : m * kLog2e;
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sum += __builtin_amdgcn_exp2f(fmaf(l[j], kLog2e, -ref));
+    half_lse(m, sum);  // both lane halves: the row's 32 ids
+    if (HALF == 0) {
+      s.hm = m;
+      s.hs = sum;
+      return;
     }
-    const float G = lse_b + gumbel_of(pick_word(s.words, (uint32_t)b & 3u));
-    if (G > s.G) {
-      s.G = G;
-      s.B = b;
-    }
+    lse_merge(m, sum, s.hm, s.hs);  // the whole 64-id block
+    float M = s.M, S = s.S;
+    lse_merge(M, S, m, sum);
+    const float G = m + __logf(sum) + gumbel_of(pick_word(s.words, (uint32_t)b & 3u));
+    const bool better = owner && G > s.G;
+    s.M = owner ? M : s.M;
+    s.S = owner ? S : s.S;
+    s.G = better ? G : s.G;
+    s.B = better ? b : s.B;
+    (void)row;
   }
-  __device__ static void finish(const Params& p, const State& s, int myrow, int range) {
-    if (myrow < 0 || myrow >= p.R) return;
-    p.partials[(size_t)myrow * p.nranges + range] = make_float4(s.M, s.S, s.G, __int_as_float(s.B));
+  __device__ static void finish(const Params& p, const State& s, int row, bool owner, int range) {
+    if (!owner) return;
+    p.partials[(size_t)row * p.nranges + range] = make_float4(s.M, s.S, s.G, __int_as_float(s.B));
   }
 };
 
@@ -421,7 +404,7 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
                      const void* h_, const void* W1_, const void* W2t_, const void* Wg_,
                      const float* w, const int32_t* x0, uint64_t seed, uint64_t cycle, int32_t* x,
                      float* c, float* lse, float* logit_x, void* bias_rows, int32_t* status,
-                     const DraftWs& ws, hipStream_t stream) {
+                     const DraftWs& ws, hipStream_t stream, hipEvent_t* evb, hipEvent_t* eve) {
   const T* U = static_cast<const T*>(U_);
   const T* h = static_cast<const T*>(h_);
   const T* W1 = static_cast<const T*>(W1_);
@@ -454,15 +437,13 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
     fill_kernel<<<(R * r + 255) / 256, 256, 0, stream>>>(ws.s, (size_t)R * r, 0.0f);  // s_0 = 0
   }
 
-  const int nt = (R > 128) ? 2 : 1;
   SweepGeom g{};
   int nranges;
   if (BF) {
-    const int rows_per_group = (kSweepThreads / kWave) * nt * 32;
-    const int ngroups = (R + rows_per_group - 1) / rows_per_group;
-    g = make_geom(R, V, r, reinterpret_cast<const uint16_t*>(W2t), nt, device_cus());
+    const int ngroups = (R + kRowsPerGroup - 1) / kRowsPerGroup;
+    g = make_geom(R, V, r, reinterpret_cast<const uint16_t*>(W2t),
+                  device_cus() / (ngroups > 0 ? ngroups : 1));
     nranges = g.nranges;
-    (void)ngroups;
   } else {
     nranges = nranges_for(V, R);
     if (nranges > 64) nranges = 64;
@@ -476,6 +457,7 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
       rnn_step_kernel<T><<<R, 256, sh, stream>>>(R, gamma, V, r, d, W1, Wg, ws.Gh, prev, ps,
                                                  (uint32_t)k, ws.s, ws.orow, status);
     }
+    if (evb) (void)hipEventRecord(evb[k - 1], stream);
     if (BF) {
       DraftSweepParams p{};
       p.U = reinterpret_cast<const uint16_t*>(U) + (size_t)(k - 1) * V;
@@ -493,19 +475,10 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
       p.partials = ws.partials;
       p.nranges = nranges;
       p.status = status;
-      const size_t sh = sweep_lds_bytes(r);
-      const int ntask = g.nranges * g.ngroups;
-      if (rnn) {
-        if (nt == 2)
-          sweep_kernel<2, true, DraftEpi<true>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
-        else
-          sweep_kernel<1, true, DraftEpi<true>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
-      } else {
-        if (nt == 2)
-          sweep_kernel<2, false, DraftEpi<false>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
-        else
-          sweep_kernel<1, false, DraftEpi<false>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
-      }
+      if (rnn)
+        launch_sweep<true, DraftEpi<true>>(g, p, stream);
+      else
+        launch_sweep<false, DraftEpi<false>>(g, p, stream);
     } else {
       const int nblocks = (V + kVB - 1) / kVB;
       dim3 grid(nranges, R);
@@ -515,6 +488,7 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
           reinterpret_cast<const float*>(W2t), (uint32_t)k, seed, cycle, ws.partials, nranges,
           nblocks, status);
     }
+    if (eve) (void)hipEventRecord(eve[k - 1], stream);
     if (rnn)
       draft_combine_kernel<T, true><<<R, 64, 0, stream>>>(
           R, gamma, V, r, d, U, W1, W2t, w, ws.zh, prev, ps, ws.orow, ws.partials, nranges,
@@ -532,7 +506,8 @@ static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_d
                        const void* Wg, const float* w, const int32_t* x0, uint64_t seed,
                        uint64_t cycle, int32_t* x, float* c, float* lse, float* logit_x,
                        void* bias_rows, int32_t* status, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+                       hipStream_t stream, hipEvent_t* evb = nullptr,
+                       hipEvent_t* eve = nullptr) {
   if (!dims_ok(R, gamma, V, r, d) || (dt != DSPARK_F32 && dt != DSPARK_BF16)) return DSPARK_EINVAL;
   if (cycle >= ((uint64_t)1 << 28)) return DSPARK_EINVAL;
   if (R == 0) return DSPARK_OK;
@@ -540,6 +515,8 @@ static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_d
     return DSPARK_EINVAL;
   if (d > 0 && !h) return DSPARK_EINVAL;
   if (rnn && !Wg) return DSPARK_EINVAL;
+  // the bf16 sweep addresses U rows with 32-bit byte offsets
+  if (dt == DSPARK_BF16 && (uint64_t)R * gamma * V * 2 >= ((uint64_t)1 << 32)) return DSPARK_EINVAL;
   if (!aligned16(U) || !aligned16(h) || !aligned16(W1) || !aligned16(W2t) || !aligned16(Wg) ||
       !aligned16(bias_rows) || !aligned16(w))
     return DSPARK_EINVAL;
@@ -549,9 +526,9 @@ static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_d
   const DraftWs lay = carve_draft(ws, R, gamma, V, r, d, rnn);
   if (dt == DSPARK_BF16)
     return draft_run<uint16_t>(rnn, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, x0, seed, cycle, x,
-                               c, lse, logit_x, bias_rows, status, lay, stream);
+                               c, lse, logit_x, bias_rows, status, lay, stream, evb, eve);
   return draft_run<float>(rnn, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, x0, seed, cycle, x, c,
-                          lse, logit_x, bias_rows, status, lay, stream);
+                          lse, logit_x, bias_rows, status, lay, stream, evb, eve);
 }
 
 }  // namespace dspark
@@ -576,6 +553,18 @@ int dspark_draft_markov(int R, int gamma, int V, int r, int d, dspark_dtype dt, 
   return dspark::draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, x0, seed,
                              cycle, x, c, lse, logit_x, bias_rows, dev_status, ws, ws_bytes,
                              stream);
+}
+
+int dspark_draft_markov_timed(int R, int gamma, int V, int r, int d, dspark_dtype dt,
+                              const void* U, const void* h, const void* W1, const void* W2t,
+                              const float* w, const int32_t* x0, uint64_t seed, uint64_t cycle,
+                              int32_t* x, float* c, float* lse, float* logit_x, void* bias_rows,
+                              int32_t* dev_status, void* ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t* ev_begin, hipEvent_t* ev_end) {
+  if (!ev_begin || !ev_end) return DSPARK_EINVAL;
+  return dspark::draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, x0, seed,
+                             cycle, x, c, lse, logit_x, bias_rows, dev_status, ws, ws_bytes,
+                             stream, ev_begin, ev_end);
 }
 
 int dspark_draft_rnn(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void* U,

@@ -1,31 +1,35 @@
 // sweep.h -- the vocabulary sweep shared by the draft step and verification.
 //
-// For a group of rows (requests at one draft position, or verified positions) and a
-// contiguous range of 64-id vocabulary blocks, it forms
-//     l(row, v) = sum_i B[row][i] * W2t[v][i]          (bias = W1[x_{k-1}] W2, eq. (5))
-// on the matrix cores, 64 ids at a time, and hands every 64x(rows) tile of fp32 logits to
-// an epilogue that folds it into per-row running state (normalisers, Gumbel maxima,
+// For a group of up to 256 rows (requests at one draft position, or verified positions)
+// and a contiguous range of 64-id vocabulary blocks, it forms
+//     l(row, v) = sum_i B[row][i] * W2t[v][i] + stream_0[row][v]   (eq. (4) with eq. (5))
+// on the matrix cores, 32 ids at a time, and hands each 32 x 256 tile of fp32 logits to an
+// epilogue that folds it into per-row running state (normalisers, Gumbel maxima,
 // distances), so no V-wide row is ever written to memory.
 //
-// Work split (one workgroup = 4 waves = 256 threads):
-//   - grid = nranges x ngroups tasks; a task owns one vocabulary range and one row group.
-//   - The W2t rows of the current 64-id block are staged in LDS (double-buffered, loaded
-//     with coalesced 16-byte reads: a W2t row is r contiguous bf16), shared by all waves.
-//   - Each wave owns NT*32 rows; their B rows (K = r) live in registers for the whole
-//     sweep, so every LDS fragment of W2t feeds NT MFMAs.
-//   - MFMA 32x32x16 bf16 with A = W2t tile (vocab on M) and B = B^T (rows on N): lane
-//     (n, h) of the accumulator holds row n and 16 vocabulary ids; the tile's vocabulary
-//     order is permuted so that these 16 ids are consecutive (v0 + 16h .. v0 + 16h + 15),
-//     which makes the epilogue's per-row operand loads two 16-byte reads per tile.
+// Work split: one workgroup of 8 waves per task; grid = vocabulary ranges x row groups.
+//   - Each wave owns 32 rows; their B rows (K = r) live in registers for the whole sweep.
+//   - Per 32-id tile the workgroup stages in LDS the tile's W2t rows (32 x r bf16, shared by
+//     all waves) and every wave's 32 x 32 slice of each streamed operand (U, and the target
+//     logits in verification).  Staging is asynchronous: the loads go straight to LDS
+//     (global_load_lds_dwordx4), three stages deep when LDS allows, so each tile's HBM
+//     traffic is issued two tiles ahead of its use and the matrix-core and epilogue work
+//     of the current tile hides the memory latency.  The waits on those loads are explicit
+//     vmcnt waits.
+//   - MFMA 32x32x16 bf16 with A = W2t tile (vocabulary on M) and B = B^T (rows on N):
+//     accumulator lane (n, h) holds row n; its 16 registers are permuted (see
+//     tile_row_of_vocab) to two runs of 8 consecutive ids, which the epilogue matches with
+//     two 16-byte LDS reads per streamed operand.
 #pragma once
 
 #include "dev.h"
 
 namespace dspark {
 
-constexpr int kSweepThreads = 256;
-constexpr int kMaxKS = 16;   // r <= 256
-constexpr int kMaxStage = 8; // 16-byte W2t chunks staged per thread per block (r = 256)
+constexpr int kSweepThreads = 512;  // 8 waves; each wave owns 32 rows of the group
+constexpr int kSweepWaves = kSweepThreads / kWave;
+constexpr int kRowsPerGroup = kSweepWaves * 32;
+constexpr int kTile = 32;           // vocabulary ids per pipeline step (one m-tile)
 
 struct SweepGeom {
   int nrows;      // rows (upper bound; an epilogue may know the exact count on device)
@@ -40,17 +44,35 @@ struct SweepGeom {
   const uint16_t* W2t;  // [V][r] bf16
 };
 
-// position of the 16-byte chunk c of tile row m (0..31) of m-tile mt in an LDS buffer
-__device__ __forceinline__ int lds_pos(const SweepGeom& g, int mt, int m, int c) {
-  const int swz = m & ((g.CH < 16 ? g.CH : 16) - 1);
-  return (mt * 32 + m) * g.CH + (c ^ swz);
+// ---------------------------------------------------------------------------------------
+// LDS layout of one pipeline stage (units of 16-byte chunks)
+//   [W2t tile: 32 rows, row stride CH + 1 (the odd stride puts the 16 rows one
+//    ds_read_b128 phase reads on distinct banks, so every fragment address is a per-lane
+//    base plus an immediate); rounded up to whole 64-chunk copies]
+//   [stream s: 8 waves x 32 rows x 4 chunks] for each streamed operand
+// ---------------------------------------------------------------------------------------
+__host__ __device__ constexpr int w2_copies(int CH) { return (32 * (CH + 1) + 63) / 64; }
+__host__ __device__ constexpr int w2_tile_chunks(int CH) { return 64 * w2_copies(CH); }
+__host__ __device__ constexpr int stream_tile_chunks() { return kSweepWaves * 32 * 4; }
+__host__ __device__ constexpr int stage_chunks(int CH, int nstreams) {
+  return w2_tile_chunks(CH) + nstreams * stream_tile_chunks();
+}
+inline size_t sweep_lds_bytes(int r, int nstreams, int nstage) {
+  return (size_t)16 * nstage * stage_chunks(r / 8, nstreams);
 }
 
-// accumulator row m of a 32x32 tile holds vocabulary offset perm(m) inside the tile:
-// perm(8q + 4h + t) = 16h + 4q + t.  Inverse: v -> 8((v & 15) >> 2) + 4(v >> 4) + (v & 3).
+// 16-byte chunk c (0..3) of row n in a wave's 32 x 32 stream slice; the xor spreads the 16
+// rows of one read phase over the banks
+__device__ __forceinline__ int stream_pos(int n, int c) { return n * 4 + (c ^ ((n >> 2) & 3)); }
+
+// Accumulator row m = 16c + 8a + 4h + t of a 32x32 tile holds vocabulary offset
+// 16c + 8h + 4a + t (bits 2 and 3 swapped; the map is its own inverse), so register
+// j = 8c + e of lane half h is vocabulary offset 16c + 8h + e: chunks h and 2 + h of the
+// row's 32-id slice.
 __device__ __forceinline__ int tile_row_of_vocab(int vv) {
-  return 8 * ((vv & 15) >> 2) + 4 * (vv >> 4) + (vv & 3);
+  return 16 * (vv >> 4) + 8 * ((vv >> 2) & 1) + 4 * ((vv >> 3) & 1) + (vv & 3);
 }
+__device__ __forceinline__ int vocab_of_reg(int h, int j) { return 16 * (j >> 3) + 8 * h + (j & 7); }
 
 __device__ __forceinline__ void task_of(const SweepGeom& g, int& range, int& group) {
   const int ntask = g.nranges * g.ngroups;
@@ -65,36 +87,6 @@ __device__ __forceinline__ void task_of(const SweepGeom& g, int& range, int& gro
 __device__ __forceinline__ void range_blocks(const SweepGeom& g, int range, int& b0, int& b1) {
   b0 = range * g.blocks_lo + (range < g.blocks_extra ? range : g.blocks_extra);
   b1 = b0 + g.blocks_lo + (range < g.blocks_extra ? 1 : 0);
-}
-
-// load the W2t rows of block b into staging registers (zero past V)
-__device__ __forceinline__ void stage_load(const SweepGeom& g, int b, uint4 (&st)[kMaxStage]) {
-  const int total = 64 * g.CH;
-#pragma unroll
-  for (int s = 0; s < kMaxStage; ++s) {
-    const int c = threadIdx.x + s * kSweepThreads;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (c < total) {
-      const int vl = c / g.CH, ch = c - vl * g.CH;
-      const int vocab = b * kVB + vl;
-      if (vocab < g.V)
-        v = *reinterpret_cast<const uint4*>(g.W2t + (size_t)vocab * g.r + ch * 8);
-    }
-    st[s] = v;
-  }
-}
-
-__device__ __forceinline__ void stage_store(const SweepGeom& g, uint4* buf,
-                                            const uint4 (&st)[kMaxStage]) {
-  const int total = 64 * g.CH;
-#pragma unroll
-  for (int s = 0; s < kMaxStage; ++s) {
-    const int c = threadIdx.x + s * kSweepThreads;
-    if (c < total) {
-      const int vl = c / g.CH, ch = c - vl * g.CH;
-      buf[lds_pos(g, vl >> 5, tile_row_of_vocab(vl & 31), ch)] = st[s];
-    }
-  }
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -114,113 +106,289 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint4& hi, uint4& lo
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-// The sweep kernel.  Epi provides:
-//   struct Params; struct State; struct Pre;
-//   static bool group_live(const Params&, int row0)          rows exist in this group
-//   static int  nrows(const Params&)                         exact row count (device)
-//   static const void* brow(const Params&, int row)          B row of a row (bf16 or f32)
-//   static void init(const Params&, State&, int myrow)
-//   template <int NT> static void prefetch(const Params&, Pre&, int b, int rowbase)
-//   static void block(const Params&, State&, const Pre&, const f32x16 (&acc)[NT][2],
-//                     int b, int rowbase, int myrow)
-//   static void finish(const Params&, const State&, int myrow, int range)
+// 8 bf16 of a 16-byte chunk, widened
+__device__ __forceinline__ void widen8(uint4 u, float* o) {
+  o[0] = bf16lo(u.x); o[1] = bf16hi(u.x); o[2] = bf16lo(u.y); o[3] = bf16hi(u.y);
+  o[4] = bf16lo(u.z); o[5] = bf16hi(u.z); o[6] = bf16lo(u.w); o[7] = bf16hi(u.w);
+}
+
+// ---------------------------------------------------------------------------------------
+// Asynchronous global -> LDS copies (global_load_lds_dwordx4): every lane moves 16 bytes to
+// lds_byte_base + 16 * lane.  They are issued as inline assembly so that the compiler's own
+// wait-count bookkeeping does not serialise later LDS reads behind them; the sweep waits
+// for them explicitly (vm_wait) before the barrier that publishes a stage.
+// ---------------------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// the same copy with a scalar base and a per-lane 32-bit byte offset: the per-tile cost is
+// one scalar add per copy
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_byte_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_byte_base)
+      : "memory", "m0");
+}
+
+// x of the lane 32 apart (lane l <-> l ^ 32) combined with op, on both halves: the swap
+// returns (x[0..31], x[0..31]) and (x[32..63], x[32..63]), so op(first, second) is
+// op(x[l], x[l ^ 32]) on every lane when op is commutative
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void half_lse(float& m, float& s) {
+  const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  m = __uint_as_float(rm[0]);
+  s = __uint_as_float(rs[0]);
+  lse_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
+}
+
+// The sweep kernel.  Lane (n, h) of wave w works on row = group*256 + 32w + n; the lanes
+// with h == 0 own the row's running state.  Epi provides:
+//   static constexpr int kStreams;       streamed operands: 1 (U) or 2 (U, target)
+//   struct Params; struct State;
+//   static bool group_live(const Params&, int row0)         rows exist in this group
+//   static int  nrows(const Params&)                        exact row count (device)
+//   static const void* brow(const Params&, int row)         B row of a live row
+//   static const uint16_t* sbase(const Params&, int s)      stream s array
+//   static uint32_t srow(const Params&, int s, int row)     element offset of a live row
+//   static void init(const Params&, State&, int row)        row < 0: not a live row
+//   static void refresh(const Params&, State&, int b, int row)   random words of block b
+//   template <int HALF, bool MASK>
+//   static void tile(const Params&, State&, const f32x16& l, const uint4 (&x)[2], int b,
+//                    int row, bool owner)
+//        l: the 32-id tile (half HALF of block b) of logits U + bias in accumulator
+//        layout; x: stream 1 of the tile (packed bf16, chunks h and 2 + h of the row's
+//        slice) when kStreams == 2; MASK: ids past V may be present (last block only)
+//   static void finish(const Params&, const State&, int row, bool owner, int range)
+// NKS = r / 16 (compile time: the k loop is fully unrolled over register operands).
 // SPLIT: B rows are float and enter as hi + lo bf16 terms (two MFMAs each).
-template <int NT, bool SPLIT, class Epi>
+// Host guarantees: every stream array is smaller than 4 GiB (32-bit byte offsets).
+template <int NKS, bool SPLIT, int NSTAGE, class Epi>
 __global__ void __launch_bounds__(kSweepThreads, 1)
     sweep_kernel(SweepGeom g, typename Epi::Params ep) {
+  constexpr int CH = 2 * NKS;
+  constexpr int RS = CH + 1;                 // W2t tile row stride (chunks)
+  constexpr int NI = w2_copies(CH);          // W2t copies per tile
+  constexpr int W2_MAX = (NI + kSweepWaves - 1) / kSweepWaves;
+  constexpr int NS = Epi::kStreams;
+  constexpr int SCH = stage_chunks(CH, NS);
+  constexpr int D = NSTAGE - 1;              // prefetch distance in tiles
   extern __shared__ uint4 lds[];
+
   int range, group;
   task_of(g, range, group);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int group_row0 = group * (kSweepThreads / kWave) * NT * 32;
+  const int group_row0 = group * kRowsPerGroup;
   if (!Epi::group_live(ep, group_row0)) return;
   const int nrows = Epi::nrows(ep);
-  const int rowbase = group_row0 + wave * NT * 32;
-  // the row this lane keeps running state for: n-tile h (NT == 2) or n-tile 0 (NT == 1)
-  const int myrow = (NT == 2 || h == 0) ? rowbase + (NT == 2 ? 32 * h : 0) + n : -1;
+  const int row = group_row0 + wave * 32 + n;
+  const bool live = row < nrows;
+  const bool owner = live && h == 0;
 
-  // B operand in registers: rows rowbase + 32*nt + n, k = 16*ks + 8*h .. + 8
-  bf16x8 bh[NT][kMaxKS];
-  bf16x8 bl[SPLIT ? NT : 1][SPLIT ? kMaxKS : 1];
+  // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row
+  bf16x8 bh[NKS];
+  bf16x8 bl[SPLIT ? NKS : 1];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = rowbase + 32 * nt + n;
-    const bool live = row < nrows;
-#pragma unroll
-    for (int ks = 0; ks < kMaxKS; ++ks) {
-      uint4 hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
-      if (live && ks < g.nks) {
-        const int k0 = 16 * ks + 8 * h;
-        if (SPLIT) {
-          const float* p = reinterpret_cast<const float*>(Epi::brow(ep, row)) + k0;
-          const float4 a = *reinterpret_cast<const float4*>(p);
-          const float4 c = *reinterpret_cast<const float4*>(p + 4);
-          const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-          split8(x, hi, lo);
-        } else {
-          hi = *reinterpret_cast<const uint4*>(
-              reinterpret_cast<const uint16_t*>(Epi::brow(ep, row)) + k0);
-        }
+  for (int ks = 0; ks < NKS; ++ks) {
+    uint4 hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
+    if (live) {
+      const int k0 = 16 * ks + 8 * h;
+      if (SPLIT) {
+        const float* p = reinterpret_cast<const float*>(Epi::brow(ep, row)) + k0;
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 c = *reinterpret_cast<const float4*>(p + 4);
+        const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        split8(x, hi, lo);
+      } else {
+        hi = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(Epi::brow(ep, row)) + k0);
       }
-      bh[nt][ks] = as_bf16x8(hi);
-      if (SPLIT) bl[SPLIT ? nt : 0][SPLIT ? ks : 0] = as_bf16x8(lo);
     }
+    bh[ks] = as_bf16x8(hi);
+    if (SPLIT) bl[SPLIT ? ks : 0] = as_bf16x8(lo);
   }
-
   typename Epi::State st;
-  Epi::init(ep, st, myrow);
+  Epi::init(ep, st, live ? row : -1);
+
+  // per-lane byte offsets of the copies (constant over tiles)
+  //   W2t copy i (index I = wave + 8i): lane -> padded position P = 64I + lane -> tile row
+  //   m = P / RS, chunk c = P % RS; the pad chunk and positions past the tile read row 0
+  //   stream copy k: lane -> chunk lane & 3 (xor-permuted) of the wave's row 16k + lane/4;
+  //   rows past the end read the last live row
+  uint32_t w2off[W2_MAX];
+#pragma unroll
+  for (int i = 0; i < W2_MAX; ++i) {
+    const int P = 64 * (wave + kSweepWaves * i) + lane;
+    const int m = P / RS, c = P - m * RS;
+    w2off[i] = (m < 32 && c < CH) ? (uint32_t)(tile_row_of_vocab(m) * g.r + 8 * c) * 2u : 0u;
+  }
+  uint32_t soff[NS][2];
+  int sx[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int rl = 16 * k + (lane >> 2);
+    int rr = group_row0 + wave * 32 + rl;
+    if (rr >= nrows) rr = nrows - 1;
+    sx[k] = 8 * ((lane & 3) ^ ((rl >> 2) & 3));  // element offset inside the 32-id slice
+#pragma unroll
+    for (int s = 0; s < NS; ++s) soff[s][k] = (Epi::srow(ep, s, rr) + (uint32_t)sx[k]) * 2u;
+  }
+  const uint16_t* sb[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) sb[s] = Epi::sbase(ep, s);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  // LDS chunk indices this lane reads (stage 0): A fragments at a_idx + 2*ks, stream chunks
+  const int a_idx = n * RS + h;
+  const int s_idx0 = w2_tile_chunks(CH) + wave * 128 + stream_pos(n, h);
+  const int s_idx1 = w2_tile_chunks(CH) + wave * 128 + stream_pos(n, 2 + h);
+
+  // copies of full tile t into stage stg (scalar bases; per-lane offsets fixed)
+  auto issue = [&](int t, int stg) {
+    const uint32_t base = lds0 + 16u * stg * SCH;
+    const uint16_t* w2b = g.W2t + (size_t)kTile * t * g.r;
+#pragma unroll
+    for (int i = 0; i < W2_MAX; ++i) {
+      const int I = wave + kSweepWaves * i;
+      if (I < NI) dma16s(w2b, w2off[i], base + 16u * 64u * I);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        dma16s(sb[s] + kTile * t, soff[s][k],
+               base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
+  };
+  // the same for the short last tile: clamp each lane's source into the arrays
+  auto issue_ragged = [&](int t, int stg) {
+    const uint32_t base = lds0 + 16u * stg * SCH;
+#pragma unroll
+    for (int i = 0; i < W2_MAX; ++i) {
+      const int I = wave + kSweepWaves * i;
+      const int P = 64 * I + lane;
+      const int m = P / RS, c = P - m * RS;
+      int v = kTile * t + (m < 32 ? tile_row_of_vocab(m) : 0);
+      if (v >= g.V) v = g.V - 1;
+      const uint32_t off = (m < 32 && c < CH) ? (uint32_t)(v * g.r + 8 * c) * 2u : 0u;
+      if (I < NI) dma16s(g.W2t, off, base + 16u * 64u * I);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        int v = kTile * t + sx[k];
+        if (v > g.V - 8) v = g.V - 8;
+        dma16s(sb[s], soff[s][k] + (uint32_t)(v - sx[k]) * 2u,
+               base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
+      }
+  };
+  // loads one tile puts in flight for this wave
+  const int ops = (wave < NI - kSweepWaves * (W2_MAX - 1) ? W2_MAX : W2_MAX - 1) + 2 * NS;
+  // wait until at most `left` tiles' copies are still in flight (loads complete in order)
+  auto wait_tiles = [&](int left) {
+    if (left == 0) {
+      vm_wait<0>();
+    } else if (ops == W2_MAX + 2 * NS) {
+      vm_wait<W2_MAX + 2 * NS>();
+    } else {
+      vm_wait<W2_MAX - 1 + 2 * NS>();
+    }
+  };
+
+  // matrix-core chain of the tile in stage stg, seeded with its U slice
+  auto mma = [&](int stg, f32x16& acc, uint4 (&x)[2]) {
+    const uint4* sl = lds + stg * SCH;
+    float u[16];
+    widen8(sl[s_idx0], u);
+    widen8(sl[s_idx1], u + 8);
+    if (NS == 2) {
+      x[0] = sl[s_idx0 + stream_tile_chunks()];
+      x[1] = sl[s_idx1 + stream_tile_chunks()];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = u[j];
+    const uint4* ab = sl + a_idx;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 a = as_bf16x8(ab[2 * ks]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc, 0, 0, 0);
+      if (SPLIT) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[SPLIT ? ks : 0], acc, 0, 0, 0);
+    }
+  };
 
   int b0, b1;
   range_blocks(g, range, b0, b1);
-  const int buf_chunks = 64 * g.CH;
-  uint4 stage[kMaxStage];
-  if (b0 < b1) {
-    stage_load(g, b0, stage);
-    stage_store(g, lds, stage);
-  }
-  for (int b = b0; b < b1; ++b) {
-    uint4* cur = lds + ((b - b0) & 1) * buf_chunks;
-    uint4* nxt = lds + (((b - b0) & 1) ^ 1) * buf_chunks;
-    const bool more = b + 1 < b1;
-    if (more) stage_load(g, b + 1, stage);
-    typename Epi::Pre pre;
-    Epi::template prefetch<NT>(ep, pre, b, rowbase);
-    __syncthreads();  // cur is complete; every wave is past its reads of nxt
+  // the last block of the vocabulary is short when V % 64 != 0: it leaves the pipeline
+  const bool ragged = (b1 * kVB > g.V);
+  const int bp1 = ragged ? b1 - 1 : b1;  // pipelined blocks [b0, bp1)
+  const int t0 = 2 * b0, t1 = 2 * bp1;
 
-    f32x16 acc[NT][2];
+  // a wait the compiler sees: every load issued so far (B rows, epilogue state) has
+  // landed, so none of them is pending at the loop header
+  __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[nt][mt][j] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < kMaxKS; ++ks) {
-      if (ks < g.nks) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 a = as_bf16x8(cur[lds_pos(g, mt, n, 2 * ks + h)]);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[nt][ks], acc[nt][mt],
-                                                                  0, 0, 0);
-            if (SPLIT)
-              acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  a, bl[SPLIT ? nt : 0][SPLIT ? ks : 0], acc[nt][mt], 0, 0, 0);
-          }
-        }
-      }
-    }
-    Epi::template block<NT>(ep, st, pre, acc, b, rowbase, myrow);
-    if (more) stage_store(g, nxt, stage);
+  for (int d = 0; d < D; ++d)
+    if (t0 + d < t1) issue(t0 + d, d);
+  f32x16 accA, accB;
+  uint4 xA[2], xB[2];
+  xA[0] = xA[1] = xB[0] = xB[1] = make_uint4(0, 0, 0, 0);
+  int stg = 0;
+  // one pipeline step: tile t's copies are awaited, tile t+D's issued, tile t's matrix
+  // chain runs, and the epilogue of tile t-1 (HALF = 1 - half of t) overlaps it
+  for (int t = t0; t < t1; t += 2) {
+    const int b = t >> 1;
+    // -- tile t = 2b (half 0); epilogue of tile 2b-1 (half 1 of block b-1)
+    wait_tiles(D == 2 && t + 1 < t1 ? 1 : 0);
+    __syncthreads();
+    if (t + D < t1) issue(t + D, stg + D >= NSTAGE ? stg + D - NSTAGE : stg + D);
+    if (t > t0) Epi::refresh(ep, st, b - 1, row);
+    mma(stg, accA, xA);
+    if (t > t0) Epi::template tile<1, false>(ep, st, accB, xB, b - 1, row, owner);
+    stg = stg + 1 == NSTAGE ? 0 : stg + 1;
+    // -- tile t + 1 (half 1); epilogue of tile t (half 0 of block b)
+    wait_tiles(D == 2 && t + 2 < t1 ? 1 : 0);
+    __syncthreads();
+    if (t + 1 + D < t1) issue(t + 1 + D, stg + D >= NSTAGE ? stg + D - NSTAGE : stg + D);
+    mma(stg, accB, xB);
+    Epi::template tile<0, false>(ep, st, accA, xA, b, row, owner);
+    stg = stg + 1 == NSTAGE ? 0 : stg + 1;
   }
-  Epi::finish(ep, st, myrow, range);
+  if (t1 > t0) {
+    Epi::refresh(ep, st, bp1 - 1, row);
+    Epi::template tile<1, false>(ep, st, accB, xB, bp1 - 1, row, owner);
+  }
+  if (ragged) {  // the short last block, unpipelined
+    const int b = b1 - 1;
+    vm_wait<0>();
+    __syncthreads();
+    issue_ragged(2 * b, 0);
+    issue_ragged(2 * b + 1, 1);
+    vm_wait<0>();
+    __syncthreads();
+    mma(0, accA, xA);
+    Epi::template tile<0, true>(ep, st, accA, xA, b, row, owner);
+    mma(1, accB, xB);
+    Epi::refresh(ep, st, b, row);
+    Epi::template tile<1, true>(ep, st, accB, xB, b, row, owner);
+  }
+  vm_wait<0>();
+  Epi::finish(ep, st, row, owner, range);
 }
 
-// host-side geometry
-inline SweepGeom make_geom(int nrows, int V, int r, const uint16_t* W2t, int nt,
-                           int target_tasks) {
+// host-side geometry: row groups of 256, target_ranges vocabulary ranges per group
+inline SweepGeom make_geom(int nrows, int V, int r, const uint16_t* W2t, int target_ranges) {
   SweepGeom g{};
   g.nrows = nrows;
   g.V = V;
@@ -228,10 +396,9 @@ inline SweepGeom make_geom(int nrows, int V, int r, const uint16_t* W2t, int nt,
   g.CH = r / 8;
   g.nks = r / 16;
   g.nblocks = (V + kVB - 1) / kVB;
-  const int rows_per_group = (kSweepThreads / kWave) * nt * 32;
-  g.ngroups = (nrows + rows_per_group - 1) / rows_per_group;
+  g.ngroups = (nrows + kRowsPerGroup - 1) / kRowsPerGroup;
   if (g.ngroups < 1) g.ngroups = 1;
-  int nr = target_tasks / g.ngroups;
+  int nr = target_ranges;
   if (nr < 1) nr = 1;
   if (nr > g.nblocks) nr = g.nblocks;
   g.nranges = nr;
@@ -241,6 +408,55 @@ inline SweepGeom make_geom(int nrows, int V, int r, const uint16_t* W2t, int nt,
   return g;
 }
 
-inline size_t sweep_lds_bytes(int r) { return (size_t)2 * 64 * (r / 8) * 16; }
+// LDS the device allows one workgroup (cached per device)
+inline size_t device_max_lds() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        v <= 0)
+      v = 65536;
+    cache[dev] = v;
+  }
+  return (size_t)cache[dev];
+}
+
+template <int NKS, bool SPLIT, int NSTAGE, class Epi>
+inline void launch_sweep_nks(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s) {
+  auto kern = sweep_kernel<NKS, SPLIT, NSTAGE, Epi>;
+  const size_t sh = sweep_lds_bytes(g.r, Epi::kStreams, NSTAGE);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+    attr = true;
+  }
+  kern<<<g.nranges * g.ngroups, kSweepThreads, sh, s>>>(g, p);
+}
+
+// launch with NKS = r / 16 fixed at compile time (r in {16, 32, 64, 128, 256}) and three
+// pipeline stages when the device's LDS allows them, else two
+template <bool SPLIT, class Epi>
+inline void launch_sweep(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s) {
+  const bool three = sweep_lds_bytes(g.r, Epi::kStreams, 3) <= device_max_lds();
+  switch (g.nks) {
+    case 1:
+      three ? launch_sweep_nks<1, SPLIT, 3, Epi>(g, p, s) : launch_sweep_nks<1, SPLIT, 2, Epi>(g, p, s);
+      break;
+    case 2:
+      three ? launch_sweep_nks<2, SPLIT, 3, Epi>(g, p, s) : launch_sweep_nks<2, SPLIT, 2, Epi>(g, p, s);
+      break;
+    case 4:
+      three ? launch_sweep_nks<4, SPLIT, 3, Epi>(g, p, s) : launch_sweep_nks<4, SPLIT, 2, Epi>(g, p, s);
+      break;
+    case 8:
+      three ? launch_sweep_nks<8, SPLIT, 3, Epi>(g, p, s) : launch_sweep_nks<8, SPLIT, 2, Epi>(g, p, s);
+      break;
+    default:
+      three ? launch_sweep_nks<16, SPLIT, 3, Epi>(g, p, s) : launch_sweep_nks<16, SPLIT, 2, Epi>(g, p, s);
+  }
+}
 
 }  // namespace dspark

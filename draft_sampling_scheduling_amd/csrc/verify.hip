@@ -234,6 +234,7 @@ struct VerifySweepParams {
 
 template <bool SPLIT>
 struct VerifyEpi {
+  static constexpr int kStreams = 2;  // U_j, target row j
   using Params = VerifySweepParams;
   struct State {
     float tv;          // sum |p - q| over this range
@@ -241,12 +242,9 @@ struct VerifyEpi {
     int B;
     int q, j, resid;   // this lane's row
     float lq, lp;      // normalisers (draft lse, target lse)
+    float hr;          // residual mass of the first half of the current block
     int grp;
     uint4 words;
-  };
-  struct Pre {
-    uint4 u[2][2][2];
-    uint4 t[2][2][2];
   };
   __device__ static bool group_live(const Params& p, int row0) { return row0 < p.ws.hdr[1]; }
   __device__ static int nrows(const Params& p) { return p.ws.hdr[1]; }
@@ -256,17 +254,26 @@ struct VerifyEpi {
     if (SPLIT) return static_cast<const float*>(p.brows) + off;
     return static_cast<const uint16_t*>(p.brows) + off;
   }
-  __device__ static void init(const Params& p, State& s, int myrow) {
+  __device__ static const uint16_t* sbase(const Params& p, int s) { return s == 0 ? p.U : p.target; }
+  __device__ static uint32_t srow(const Params& p, int s, int row) {
+    const int2 qj = p.ws.rowB[row];
+    if (s == 0) return (uint32_t)(((size_t)qj.x * p.gamma + (qj.y - 1)) * p.V);
+    return (uint32_t)(((size_t)qj.x * (p.gamma + 1) + (qj.y - 1)) * p.V);
+  }
+  __device__ static void init(const Params& p, State& s, int row) {
     s.tv = 0.0f;
     s.G = -INFINITY;
     s.mass = 0.0f;
     s.B = 0x7fffffff;
     s.grp = -1;
     s.words = make_uint4(0, 0, 0, 0);
-    s.q = s.j = s.resid = 0;
+    s.q = 0;
+    s.j = 1;
+    s.resid = 0;
     s.lq = s.lp = 0.0f;
-    if (myrow >= 0 && myrow < p.ws.hdr[1]) {
-      const int2 qj = p.ws.rowB[myrow];
+    s.hr = 0.0f;
+    if (row >= 0) {
+      const int2 qj = p.ws.rowB[row];
       s.q = qj.x;
       s.j = qj.y;
       s.resid = (p.ws.jstar[qj.x] == qj.y);
@@ -274,93 +281,51 @@ struct VerifyEpi {
       s.lp = p.ws.lset[p.ws.offA[qj.x] + qj.y - 1];
     }
   }
-  template <int NT>
-  __device__ static void prefetch(const Params& p, Pre& pre, int b, int rowbase) {
-    const int lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5;
-    const int nB = p.ws.hdr[1];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int row = rowbase + 32 * nt + n;
-      int2 qj = make_int2(0, 1);
-      if (row < nB) qj = p.ws.rowB[row];
-      const uint16_t* ur = p.U + ((size_t)qj.x * p.gamma + (qj.y - 1)) * p.V;
-      const uint16_t* tr = p.target + ((size_t)qj.x * (p.gamma + 1) + (qj.y - 1)) * p.V;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int v = b * kVB + 32 * mt + 16 * h;
-        const bool ok = row < nB && v < p.V;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const bool okc = ok && (v + 8 * c) < p.V;
-          pre.u[nt][mt][c] = okc ? *reinterpret_cast<const uint4*>(ur + v + 8 * c) : make_uint4(0, 0, 0, 0);
-          pre.t[nt][mt][c] = okc ? *reinterpret_cast<const uint4*>(tr + v + 8 * c) : make_uint4(0, 0, 0, 0);
-        }
-      }
+  __device__ static void refresh(const Params& p, State& s, int b, int) {
+    if (s.resid && (b >> 2) != s.grp) {
+      s.grp = b >> 2;
+      s.words = Rng(p.seed, p.cycle).block(kStreamResidBlk, (uint32_t)s.q, (uint32_t)s.j,
+                                           (uint32_t)s.grp);
     }
   }
-  template <int NT>
-  __device__ static void block(const Params& p, State& s, const Pre& pre,
-                               const f32x16 (&acc)[NT][2], int b, int rowbase, int myrow) {
-    const int lane = threadIdx.x & 63, h = lane >> 5, n = lane & 31;
-    const int nB = p.ws.hdr[1];
-    float tvp[NT], rm[NT];
+  // one 32-id tile: q from the logits and the draft normaliser, p from the target and its
+  // normaliser; sum |p - q| always, and on the first rejected row the residual mass of the
+  // 64-id block with its first-level Gumbel score
+  template <int HALF, bool MASK>
+  __device__ static void tile(const Params& p, State& s, const f32x16& acc, const uint4 (&x)[2],
+                              int b, int, bool owner) {
+    const int h = (threadIdx.x & 63) >> 5;
+    float t[16];  // target logits of the tile; acc holds U_j + bias
+    widen8(x[0], t);
+    widen8(x[1], t + 8);
+    float tv = 0.0f, rho = 0.0f;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      // normalisers of this lane's row in n-tile nt, kept by lane n + 32*nt
-      const int row = rowbase + 32 * nt + n;
-      const float lq = __shfl(s.lq, n + 32 * nt, kWave);
-      const float lp = __shfl(s.lp, n + 32 * nt, kWave);
-      float tv = 0.0f, rho = 0.0f;
-      if (row < nB) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int v0 = b * kVB + 32 * mt + 16 * h;
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const uint4 u = pre.u[nt][mt][c], t = pre.t[nt][mt][c];
-            const uint32_t uw[4] = {u.x, u.y, u.z, u.w}, tw[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int jj = 8 * c + e;
-              if (v0 + jj < p.V) {
-                const float uv = (e & 1) ? bf16hi(uw[e >> 1]) : bf16lo(uw[e >> 1]);
-                const float tt = (e & 1) ? bf16hi(tw[e >> 1]) : bf16lo(tw[e >> 1]);
-                const float qv = __expf(acc[nt][mt][jj] + uv - lq);
-                const float pv = __expf(tt - lp);
-                tv += fabsf(pv - qv);
-                rho += fmaxf(pv - qv, 0.0f);
-              }
-            }
-          }
-        }
-      }
-      tvp[nt] = tv + __shfl_xor(tv, 32, kWave);
-      rm[nt] = rho + __shfl_xor(rho, 32, kWave);
+    for (int j = 0; j < 16; ++j) {
+      const bool ok = !MASK || b * kVB + kTile * HALF + vocab_of_reg(h, j) < p.V;
+      const float qv = ok ? __expf(acc[j] - s.lq) : 0.0f;
+      const float pv = ok ? __expf(t[j] - s.lp) : 0.0f;
+      tv += fabsf(pv - qv);
+      rho += fmaxf(pv - qv, 0.0f);
     }
-    if (myrow < 0 || myrow >= nB) return;
-    const int mine = (NT == 2) ? h : 0;
-    s.tv += tvp[mine];
-    if (s.resid) {
-      const float mass = rm[mine];
-      s.mass += mass;
-      if (mass > 0.0f) {
-        const int grp = b >> 2;
-        if (grp != s.grp) {
-          s.grp = grp;
-          s.words = Rng(p.seed, p.cycle).block(kStreamResidBlk, (uint32_t)s.q, (uint32_t)s.j,
-                                               (uint32_t)grp);
-        }
-        const float G = __logf(mass) + gumbel_of(pick_word(s.words, (uint32_t)b & 3u));
-        if (G > s.G) {
-          s.G = G;
-          s.B = b;
-        }
-      }
+    tv = half_sum(tv);
+    rho = half_sum(rho);
+    s.tv += owner ? tv : 0.0f;
+    if (HALF == 0) {
+      s.hr = rho;
+      return;
     }
+    rho += s.hr;  // the whole 64-id block
+    const bool mine = owner && s.resid;
+    const float G = (rho > 0.0f) ? __logf(rho) + gumbel_of(pick_word(s.words, (uint32_t)b & 3u))
+                                 : -INFINITY;
+    const bool better = mine && G > s.G;
+    s.mass += mine ? rho : 0.0f;
+    s.G = better ? G : s.G;
+    s.B = better ? b : s.B;
   }
-  __device__ static void finish(const Params& p, const State& s, int myrow, int range) {
-    if (myrow < 0 || myrow >= p.ws.hdr[1]) return;
-    p.ws.partials[(size_t)myrow * p.nranges + range] = make_float4(s.tv, s.G, __int_as_float(s.B), s.mass);
+  __device__ static void finish(const Params& p, const State& s, int row, bool owner, int range) {
+    if (!owner) return;
+    p.ws.partials[(size_t)row * p.nranges + range] = make_float4(s.tv, s.G, __int_as_float(s.B), s.mass);
   }
 };
 
@@ -542,8 +507,9 @@ static int verify_run(int R, int gamma, int V, int r, const void* target_, const
   const int rows_max = R * gamma;
   int nranges;
   if (BF) {
-    const int nt = rows_max > 128 ? 2 : 1;
-    SweepGeom g = make_geom(rows_max, V, r, reinterpret_cast<const uint16_t*>(W2t), nt, device_cus());
+    // every vocabulary range for every possible row group; groups past the verified rows
+    // (known on the device only) exit at once
+    SweepGeom g = make_geom(rows_max, V, r, reinterpret_cast<const uint16_t*>(W2t), device_cus());
     nranges = g.nranges;
     VerifySweepParams p{};
     p.U = reinterpret_cast<const uint16_t*>(U);
@@ -558,12 +524,7 @@ static int verify_run(int R, int gamma, int V, int r, const void* target_, const
     p.seed = seed;
     p.cycle = cycle;
     p.nranges = nranges;
-    const size_t sh = sweep_lds_bytes(r);
-    const int ntask = g.nranges * g.ngroups;
-    if (nt == 2)
-      sweep_kernel<2, SPLIT, VerifyEpi<SPLIT>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
-    else
-      sweep_kernel<1, SPLIT, VerifyEpi<SPLIT>><<<ntask, kSweepThreads, sh, stream>>>(g, p);
+    launch_sweep<SPLIT, VerifyEpi<SPLIT>>(g, p, stream);
   } else {
     const int nblocks = (V + kVB - 1) / kVB;
     nranges = nblocks < 64 ? nblocks : 64;
@@ -602,6 +563,9 @@ int dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, const void* t
       !c_star || !ws)
     return DSPARK_EINVAL;
   if (!aligned16(target) || !aligned16(U) || !aligned16(W2t) || !aligned16(bias_rows))
+    return DSPARK_EINVAL;
+  // the bf16 sweep addresses U and target rows with 32-bit byte offsets
+  if (dt == DSPARK_BF16 && (uint64_t)R * (gamma + 1) * V * 2 >= ((uint64_t)1 << 32))
     return DSPARK_EINVAL;
   if (ws_bytes < carve_verify(nullptr, R, gamma, V).bytes) return DSPARK_EWORKSPACE;
   if (!aligned16(ws)) return DSPARK_EINVAL;

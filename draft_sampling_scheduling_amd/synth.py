@@ -30,11 +30,14 @@ import numpy as np
 # bf16 helpers (encoding only)
 # --------------------------------------------------------------------------------------
 def bf16_bits(x) -> np.ndarray:
-    """Round float32 values to bf16 (nearest, ties to even); returns uint16 bit patterns."""
+    """Round finite float32 values to bf16 (nearest, ties to even); returns uint16 bits."""
     f = np.ascontiguousarray(x, dtype=np.float32)
-    b = f.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return b.astype(np.uint16)
+    b = f.view(np.uint32)
+    r = (b >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += b  # finite inputs: no 32-bit overflow
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_to_f32(bits) -> np.ndarray:
@@ -130,10 +133,24 @@ def anchors(cfg: Config) -> np.ndarray:
     return _rng(cfg.seed, 0).integers(0, cfg.V, cfg.R).astype(np.int32)
 
 
+def _map(fn, items):
+    """fn over items on a thread pool (numpy releases the GIL); order kept."""
+    items = list(items)
+    if len(items) < 4:
+        return [fn(i) for i in items]
+    import concurrent.futures as cf
+    import os
+    workers = min(16, os.cpu_count() or 1, len(items))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
+
+
 def U_rows(cfg: Config, reqs) -> np.ndarray:
     """U[reqs] as [len(reqs)][gamma][V] (encoded)."""
-    out = [_u_rows(cfg, _rng(cfg.seed, 1, q), q, cfg.gamma) for q in reqs]
-    return _encode(cfg, np.stack(out) if out else np.zeros((0, cfg.gamma, cfg.V), np.float32))
+    out = _map(lambda q: _encode(cfg, _u_rows(cfg, _rng(cfg.seed, 1, q), q, cfg.gamma)), reqs)
+    if not out:
+        return _encode(cfg, np.zeros((0, cfg.gamma, cfg.V), np.float32))
+    return np.stack(out)
 
 
 def h_rows(cfg: Config, reqs) -> np.ndarray:
@@ -145,11 +162,17 @@ def h_rows(cfg: Config, reqs) -> np.ndarray:
 def weights(cfg: Config) -> dict:
     """W1 [V][r], W2 [r][V] (the pages' layout), w [d+r] fp32, W_gco [3r][2r+d] (rnn)."""
     s = np.float32(_wstd(cfg))
-    W1 = _rng(cfg.seed, 3).standard_normal((cfg.V, cfg.r), dtype=np.float32) * s
-    W2 = _rng(cfg.seed, 4).standard_normal((cfg.r, cfg.V), dtype=np.float32) * s
+
+    def draw(key_shape):
+        key, shape = key_shape
+        return _encode(cfg, _rng(cfg.seed, key).standard_normal(shape, dtype=np.float32) * s)
+
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(max_workers=2) as ex:
+        W1, W2 = ex.map(draw, [(3, (cfg.V, cfg.r)), (4, (cfg.r, cfg.V))])
     wstd = cfg.w_std if cfg.w_std is not None else math.sqrt(1.0 / (cfg.d + cfg.r))
     w = _rng(cfg.seed, 5).standard_normal(cfg.d + cfg.r, dtype=np.float32) * np.float32(wstd)
-    out = dict(W1=_encode(cfg, W1), W2=_encode(cfg, W2), w=w)
+    out = dict(W1=W1, W2=W2, w=w)
     if cfg.head == "rnn":
         K = 2 * cfg.r + cfg.d
         gs = np.float32(cfg.weight_std if cfg.weight_std is not None else 1.0 / math.sqrt(K))

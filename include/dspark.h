@@ -30,7 +30,7 @@
  *     with the largest l + Gumbel noise (exact in distribution).
  *   - Size limits (DSPARK_EINVAL otherwise): V % 8 == 0; r in {16,32,64,128,256};
  *     d % 8 == 0; 1 <= gamma <= 64; R >= 0 (R == 0 is a no-op); R*gamma <= 8192 for the
- *     scheduler.
+ *     scheduler; with bf16 operands U and the target logits below 4 GiB each.
  *   - Thread safety: no global mutable state; concurrent calls on different streams with
  *     disjoint outputs and workspaces are safe.
  */
@@ -108,6 +108,17 @@ int dspark_draft_markov(int R, int gamma, int V, int r, int d, dspark_dtype dt,
                         const float *w, const int32_t *x0, uint64_t seed, uint64_t cycle,
                         int32_t *x, float *c, float *lse, float *logit_x, void *bias_rows,
                         int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Benchmark hook: exactly dspark_draft_markov, and additionally records ev_begin[k-1] and
+ * ev_end[k-1] (events the caller created, gamma of each) on `stream` immediately before
+ * and after the vocabulary-sweep kernel of draft position k, so that kernel can be timed
+ * alone with hipEventElapsedTime.  DSPARK_EINVAL if either array is NULL. */
+int dspark_draft_markov_timed(int R, int gamma, int V, int r, int d, dspark_dtype dt,
+                              const void *U, const void *h, const void *W1, const void *W2t,
+                              const float *w, const int32_t *x0, uint64_t seed, uint64_t cycle,
+                              int32_t *x, float *c, float *lse, float *logit_x, void *bias_rows,
+                              int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t *ev_begin, hipEvent_t *ev_end);
 
 /* RNN head, eq. (6): W_gco [3r][2r + d] dt stacks the gate, candidate and output
  * projections (row blocks in that order; columns ordered [s ; W1 row ; h]; no biases);
