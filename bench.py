@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run a 512 MiB device copy (byte-counter calibration)")
     return ap.parse_args()
 
 
@@ -194,22 +196,30 @@ def main():
     log("target stand-in built")
 
     nsteps = args.warmup + args.steps
-    hip, evs = hip_events(2 * G * nsteps)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nsteps)]
+    # one sweep launch per step is bracketed by events (draft position k = step mod gamma,
+    # so every position is sampled); the other positions run unbracketed
+    hip, evs = hip_events(2 * nsteps)
+    null = C.c_void_p()
 
-    def step(i):
-        e = ev[i]
-        e[0].record()
-        evb = C.cast(C.addressof(evs) + (2 * G * i) * C.sizeof(C.c_void_p), C.POINTER(C.c_void_p))
-        eve = C.cast(C.addressof(evs) + (2 * G * i + G) * C.sizeof(C.c_void_p), C.POINTER(C.c_void_p))
+    def ev_arrays(i):
+        k = i % G
+        evb, eve = (C.c_void_p * G)(), (C.c_void_p * G)()
+        evb[k], eve[k] = evs[2 * i], evs[2 * i + 1]
+        return evb, eve
+
+    ev_args = [ev_arrays(i) for i in range(nsteps)]
+
+    def step(i=None, stage_ev=None):
+        e = stage_ev
+        if e: e[0].record()
         ds.draft_markov(U, h, W1, W2t, w, x0, SEED, CYCLE, out=dout, ws=dws, status=status,
-                        events=(evb, eve))
-        e[1].record()
+                        events=ev_args[i] if i is not None else None)
+        if e: e[1].record()
         ds.schedule(dout["c"], sps, cfg.sps_B0, ds.SYNC_BREAK, out=sout, status=status)
-        e[2].record()
+        if e: e[2].record()
         ds.verify(target, U, W2t, dout["bias_rows"], dout["x"], dout["lse"], dout["logit_x"],
                   sout["ell"], SEED, CYCLE, out=vout, ws=vws, status=status)
-        e[3].record()
+        if e: e[3].record()
 
     for i in range(args.warmup):
         step(i)
@@ -222,13 +232,26 @@ def main():
     log(f"{args.steps} timed cycles: {wall * 1e3 / args.steps:.3f} ms each")
     if int(status.item()) != 0:
         raise SystemExit(f"device fault bits set: {int(status.item())}")
-
     timed = range(args.warmup, nsteps)
-    t_draft = np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in timed])
-    t_sched = np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in timed])
-    t_ver = np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in timed])
-    sweep_ms = np.mean([elapsed_ms(hip, evs[2 * G * i + k], evs[2 * G * i + G + k])
-                        for i in timed for k in range(G)])
+    sweep_ms = np.mean([elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in timed])
+
+    # stage breakdown, outside the timed region (its events add gaps of their own)
+    nb = min(5, args.steps)
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
+    for i in range(nb):
+        step(None, sev[i])
+    torch.cuda.synchronize()
+    t_draft = np.mean([e[0].elapsed_time(e[1]) for e in sev])
+    t_sched = np.mean([e[1].elapsed_time(e[2]) for e in sev])
+    t_ver = np.mean([e[2].elapsed_time(e[3]) for e in sev])
+    if args.copy_probe:
+        # a plain device copy of known size, for scaling the HBM byte counters
+        a = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        for _ in range(3):
+            bcopy.copy_(a)
+        torch.cuda.synchronize()
+        log("copy probe: 3 device copies of 512 MiB")
     ms_per_step = wall * 1000.0 / args.steps
     n_acc = vout["n_acc"].cpu().numpy()
     ell = sout["ell"].cpu().numpy()
@@ -267,7 +290,7 @@ def main():
                    "R": R, "gamma": G, "V": V, "r": r, "d": d},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "draft sweep (sweep_kernel<2,false,DraftEpi<false>>)",
+                     "kernel": f"draft sweep (sweep_kernel<{r // 16}, false, *, DraftEpi<false>>)",
                      "bytes_per_launch": sweep_bytes, "launch_us": sweep_ms * 1e3},
         "emitted_tokens_per_s": emitted / (ms_per_step * 1e-3),
         "stage_ms": {"draft": t_draft, "schedule": t_sched, "verify": t_ver},

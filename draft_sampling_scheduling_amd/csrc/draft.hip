@@ -62,12 +62,17 @@ template <bool RNN>
 struct DraftEpi {
   static constexpr int kStreams = 1;  // U_k
   using Params = DraftSweepParams;
+  // Row state, kept alike in the row's two lanes except for the partial sums: one running
+  // reference ref (log2 units: the largest l * log2(e) seen so far), so each tile's
+  // exponentials are taken against it directly and only the sums rescale when it grows.
   struct State {
-    float M, S, G;  // running normaliser (max, sum exp) and best block score of the range
-    int B;          // best block
-    int grp;        // block group (4 blocks) whose random words are cached
+    float ref;    // running reference of the row (log2 units)
+    float S;      // this lane's sum of exp2(l log2e - ref) over finished blocks
+    float hs;     // this lane's sum over the first half of the current block
+    float G;      // best first-level score LSE_b + g_b of the range so far
+    int B;        // its block
+    int grp;      // block group (4 blocks) whose random words are cached
     uint4 words;
-    float hm, hs;   // (max, sum exp) of the first half of the current block
   };
   __device__ static bool group_live(const Params& p, int row0) { return row0 < p.R; }
   __device__ static int nrows(const Params& p) { return p.R; }
@@ -81,14 +86,13 @@ struct DraftEpi {
     return (uint32_t)((size_t)row * p.ustride);
   }
   __device__ static void init(const Params&, State& s, int) {
-    s.M = -INFINITY;
+    s.ref = -FLT_MAX;  // finite: ref - new_ref never forms inf - inf
     s.S = 0.0f;
+    s.hs = 0.0f;
     s.G = -INFINITY;
     s.B = 0x7fffffff;
     s.grp = -1;
     s.words = make_uint4(0, 0, 0, 0);
-    s.hm = -INFINITY;
-    s.hs = 0.0f;
   }
   // random words of block b's group of four (uniform value across the wave)
   __device__ static void refresh(const Params& p, State& s, int b, int row) {
@@ -97,13 +101,14 @@ struct DraftEpi {
       s.words = Rng(p.seed, p.cycle).block(kStreamDraftBlk, (uint32_t)row, p.k, (uint32_t)s.grp);
     }
   }
-  // one 32-id tile (half HALF of block b): the tile's (max, sum exp) joins the other half;
-  // after the second half the block's LSE_b feeds the row normaliser and LSE_b + g_b the
-  // running first-level Gumbel-max.  Branch-free unless MASK.
+  // one 32-id tile (half HALF of block b): its exponentials join the lane's sums; after the
+  // second half, the block's LSE_b + g_b enters the running first-level Gumbel-max.
+  // Branch-free unless MASK.  Rows past R compute on clamped data and are never written.
   template <int HALF, bool MASK>
   __device__ static void tile(const Params& p, State& s, const f32x16& acc, const uint4 (&)[2],
-                              int b, int row, bool owner) {
+                              int b, int, bool) {
     constexpr float kLog2e = 1.4426950408889634f;
+    constexpr float kLn2 = 0.69314718055994531f;
     const int h = (threadIdx.x & 63) >> 5;
     float l[16];  // U_k + bias (the accumulator was seeded with U_k)
 #pragma unroll
@@ -117,30 +122,31 @@ struct DraftEpi {
 #pragma unroll
     for (int j = 3; j < 15; j += 2) m = fmaxf(fmaxf(m, l[j]), l[j + 1]);
     m = fmaxf(m, l[15]);
-    const float ref = (m == -INFINITY) ? 0.0f : m * kLog2e;
+    const float ref = fmaxf(s.ref, half_max(m * kLog2e));
+    const float sc = __builtin_amdgcn_exp2f(s.ref - ref);
+    s.S *= sc;
+    if (HALF == 1) s.hs *= sc;
+    s.ref = ref;
     float sum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) sum += __builtin_amdgcn_exp2f(fmaf(l[j], kLog2e, -ref));
-    half_lse(m, sum);  // both lane halves: the row's 32 ids
     if (HALF == 0) {
-      s.hm = m;
       s.hs = sum;
       return;
     }
-    lse_merge(m, sum, s.hm, s.hs);  // the whole 64-id block
-    float M = s.M, S = s.S;
-    lse_merge(M, S, m, sum);
-    const float G = m + __logf(sum) + gumbel_of(pick_word(s.words, (uint32_t)b & 3u));
-    const bool better = owner && G > s.G;
-    s.M = owner ? M : s.M;
-    s.S = owner ? S : s.S;
+    const float own = s.hs + sum;  // this lane's share of block b
+    s.S += own;
+    const float lse_b = (ref + __builtin_amdgcn_logf(half_sum(own))) * kLn2;
+    const float G = lse_b + gumbel_of(pick_word(s.words, (uint32_t)b & 3u));
+    const bool better = G > s.G;
     s.G = better ? G : s.G;
     s.B = better ? b : s.B;
-    (void)row;
   }
   __device__ static void finish(const Params& p, const State& s, int row, bool owner, int range) {
+    const float S = half_sum(s.S);
     if (!owner) return;
-    p.partials[(size_t)row * p.nranges + range] = make_float4(s.M, s.S, s.G, __int_as_float(s.B));
+    p.partials[(size_t)row * p.nranges + range] =
+        make_float4(s.ref * 0.69314718055994531f, S, s.G, __int_as_float(s.B));
   }
 };
 
@@ -440,9 +446,7 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
   SweepGeom g{};
   int nranges;
   if (BF) {
-    const int ngroups = (R + kRowsPerGroup - 1) / kRowsPerGroup;
-    g = make_geom(R, V, r, reinterpret_cast<const uint16_t*>(W2t),
-                  device_cus() / (ngroups > 0 ? ngroups : 1));
+    g = make_geom(R, V, r, reinterpret_cast<const uint16_t*>(W2t), nranges_for(V, 1));
     nranges = g.nranges;
   } else {
     nranges = nranges_for(V, R);
@@ -457,7 +461,7 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
       rnn_step_kernel<T><<<R, 256, sh, stream>>>(R, gamma, V, r, d, W1, Wg, ws.Gh, prev, ps,
                                                  (uint32_t)k, ws.s, ws.orow, status);
     }
-    if (evb) (void)hipEventRecord(evb[k - 1], stream);
+    if (evb && evb[k - 1]) (void)hipEventRecord(evb[k - 1], stream);
     if (BF) {
       DraftSweepParams p{};
       p.U = reinterpret_cast<const uint16_t*>(U) + (size_t)(k - 1) * V;
@@ -488,7 +492,7 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
           reinterpret_cast<const float*>(W2t), (uint32_t)k, seed, cycle, ws.partials, nranges,
           nblocks, status);
     }
-    if (eve) (void)hipEventRecord(eve[k - 1], stream);
+    if (eve && eve[k - 1]) (void)hipEventRecord(eve[k - 1], stream);
     if (rnn)
       draft_combine_kernel<T, true><<<R, 64, 0, stream>>>(
           R, gamma, V, r, d, U, W1, W2t, w, ws.zh, prev, ps, ws.orow, ws.partials, nranges,

@@ -7,15 +7,18 @@
 // epilogue that folds it into per-row running state (normalisers, Gumbel maxima,
 // distances), so no V-wide row is ever written to memory.
 //
-// Work split: one workgroup of 8 waves per task; grid = vocabulary ranges x row groups.
-//   - Each wave owns 32 rows; their B rows (K = r) live in registers for the whole sweep.
+// Work split: one workgroup of 8 waves per vocabulary range (grid = ranges, about one per
+// CU); the workgroup walks the row groups of 256 in order, so a row count known only on the
+// device costs no idle workgroups.
+//   - Each wave owns 32 rows of the group; their B rows (K = r) live in registers for the
+//     group's whole sweep.
 //   - Per 32-id tile the workgroup stages in LDS the tile's W2t rows (32 x r bf16, shared by
 //     all waves) and every wave's 32 x 32 slice of each streamed operand (U, and the target
 //     logits in verification).  Staging is asynchronous: the loads go straight to LDS
-//     (global_load_lds_dwordx4), three stages deep when LDS allows, so each tile's HBM
-//     traffic is issued two tiles ahead of its use and the matrix-core and epilogue work
-//     of the current tile hides the memory latency.  The waits on those loads are explicit
-//     vmcnt waits.
+//     (global_load_lds_dwordx4), up to four stages deep as LDS allows, so each tile's HBM
+//     traffic is issued up to three tiles ahead of its use and the matrix-core and
+//     epilogue work of the current tile hides the memory latency.  The waits on those
+//     loads are explicit vmcnt waits.
 //   - MFMA 32x32x16 bf16 with A = W2t tile (vocabulary on M) and B = B^T (rows on N):
 //     accumulator lane (n, h) holds row n; its 16 registers are permuted (see
 //     tile_row_of_vocab) to two runs of 8 consecutive ids, which the epilogue matches with
@@ -74,16 +77,6 @@ __device__ __forceinline__ int tile_row_of_vocab(int vv) {
 }
 __device__ __forceinline__ int vocab_of_reg(int h, int j) { return 16 * (j >> 3) + 8 * h + (j & 7); }
 
-__device__ __forceinline__ void task_of(const SweepGeom& g, int& range, int& group) {
-  const int ntask = g.nranges * g.ngroups;
-  int t = blockIdx.x;
-  // consecutive tasks share a vocabulary range; keep them on one XCD (round-robin
-  // dispatch over 8 XCDs) so that the range's W2t rows are fetched into one L2
-  if ((ntask & 7) == 0) t = (t & 7) * (ntask >> 3) + (t >> 3);
-  range = t / g.ngroups;
-  group = t - range * g.ngroups;
-}
-
 __device__ __forceinline__ void range_blocks(const SweepGeom& g, int range, int& b0, int& b1) {
   b0 = range * g.blocks_lo + (range < g.blocks_extra ? range : g.blocks_extra);
   b1 = b0 + g.blocks_lo + (range < g.blocks_extra ? 1 : 0);
@@ -139,12 +132,26 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
       : "memory", "m0");
 }
 
+// Workgroup barrier for the staging pipeline.  __syncthreads() carries a release fence,
+// which the compiler implements by draining every outstanding vector-memory load first
+// (vmcnt(0)) -- that would retire the prefetched tiles too and collapse the pipeline to
+// depth one.  Here the copies are awaited explicitly (vm_wait), so the barrier only has to
+// retire this wave's LDS reads before another wave may overwrite the stage; the memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // x of the lane 32 apart (lane l <-> l ^ 32) combined with op, on both halves: the swap
 // returns (x[0..31], x[0..31]) and (x[32..63], x[32..63]), so op(first, second) is
 // op(x[l], x[l ^ 32]) on every lane when op is commutative
 __device__ __forceinline__ float half_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ void half_lse(float& m, float& s) {
   const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
@@ -187,207 +194,216 @@ __global__ void __launch_bounds__(kSweepThreads, 1)
   constexpr int D = NSTAGE - 1;              // prefetch distance in tiles
   extern __shared__ uint4 lds[];
 
-  int range, group;
-  task_of(g, range, group);
+  const int range = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int group_row0 = group * kRowsPerGroup;
-  if (!Epi::group_live(ep, group_row0)) return;
   const int nrows = Epi::nrows(ep);
-  const int row = group_row0 + wave * 32 + n;
-  const bool live = row < nrows;
-  const bool owner = live && h == 0;
+  for (int group = 0; Epi::group_live(ep, group * kRowsPerGroup); ++group) {
+    // values derived from the group are recomputed per group rather than hoisted out of
+    // the group loop and held (the scalar register file is the tight resource here)
+    int group_row0 = group * kRowsPerGroup;
+    asm volatile("" : "+s"(group_row0));
+    const int row = group_row0 + wave * 32 + n;
+    const bool live = row < nrows;
+    const bool owner = live && h == 0;
 
-  // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row
-  bf16x8 bh[NKS];
-  bf16x8 bl[SPLIT ? NKS : 1];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    uint4 hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
-    if (live) {
-      const int k0 = 16 * ks + 8 * h;
-      if (SPLIT) {
-        const float* p = reinterpret_cast<const float*>(Epi::brow(ep, row)) + k0;
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 c = *reinterpret_cast<const float4*>(p + 4);
-        const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-        split8(x, hi, lo);
-      } else {
-        hi = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(Epi::brow(ep, row)) + k0);
-      }
-    }
-    bh[ks] = as_bf16x8(hi);
-    if (SPLIT) bl[SPLIT ? ks : 0] = as_bf16x8(lo);
-  }
-  typename Epi::State st;
-  Epi::init(ep, st, live ? row : -1);
-
-  // per-lane byte offsets of the copies (constant over tiles)
-  //   W2t copy i (index I = wave + 8i): lane -> padded position P = 64I + lane -> tile row
-  //   m = P / RS, chunk c = P % RS; the pad chunk and positions past the tile read row 0
-  //   stream copy k: lane -> chunk lane & 3 (xor-permuted) of the wave's row 16k + lane/4;
-  //   rows past the end read the last live row
-  uint32_t w2off[W2_MAX];
-#pragma unroll
-  for (int i = 0; i < W2_MAX; ++i) {
-    const int P = 64 * (wave + kSweepWaves * i) + lane;
-    const int m = P / RS, c = P - m * RS;
-    w2off[i] = (m < 32 && c < CH) ? (uint32_t)(tile_row_of_vocab(m) * g.r + 8 * c) * 2u : 0u;
-  }
-  uint32_t soff[NS][2];
-  int sx[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int rl = 16 * k + (lane >> 2);
-    int rr = group_row0 + wave * 32 + rl;
-    if (rr >= nrows) rr = nrows - 1;
-    sx[k] = 8 * ((lane & 3) ^ ((rl >> 2) & 3));  // element offset inside the 32-id slice
-#pragma unroll
-    for (int s = 0; s < NS; ++s) soff[s][k] = (Epi::srow(ep, s, rr) + (uint32_t)sx[k]) * 2u;
-  }
-  const uint16_t* sb[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) sb[s] = Epi::sbase(ep, s);
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
-  // LDS chunk indices this lane reads (stage 0): A fragments at a_idx + 2*ks, stream chunks
-  const int a_idx = n * RS + h;
-  const int s_idx0 = w2_tile_chunks(CH) + wave * 128 + stream_pos(n, h);
-  const int s_idx1 = w2_tile_chunks(CH) + wave * 128 + stream_pos(n, 2 + h);
-
-  // copies of full tile t into stage stg (scalar bases; per-lane offsets fixed)
-  auto issue = [&](int t, int stg) {
-    const uint32_t base = lds0 + 16u * stg * SCH;
-    const uint16_t* w2b = g.W2t + (size_t)kTile * t * g.r;
-#pragma unroll
-    for (int i = 0; i < W2_MAX; ++i) {
-      const int I = wave + kSweepWaves * i;
-      if (I < NI) dma16s(w2b, w2off[i], base + 16u * 64u * I);
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        dma16s(sb[s] + kTile * t, soff[s][k],
-               base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
-  };
-  // the same for the short last tile: clamp each lane's source into the arrays
-  auto issue_ragged = [&](int t, int stg) {
-    const uint32_t base = lds0 + 16u * stg * SCH;
-#pragma unroll
-    for (int i = 0; i < W2_MAX; ++i) {
-      const int I = wave + kSweepWaves * i;
-      const int P = 64 * I + lane;
-      const int m = P / RS, c = P - m * RS;
-      int v = kTile * t + (m < 32 ? tile_row_of_vocab(m) : 0);
-      if (v >= g.V) v = g.V - 1;
-      const uint32_t off = (m < 32 && c < CH) ? (uint32_t)(v * g.r + 8 * c) * 2u : 0u;
-      if (I < NI) dma16s(g.W2t, off, base + 16u * 64u * I);
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        int v = kTile * t + sx[k];
-        if (v > g.V - 8) v = g.V - 8;
-        dma16s(sb[s], soff[s][k] + (uint32_t)(v - sx[k]) * 2u,
-               base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
-      }
-  };
-  // loads one tile puts in flight for this wave
-  const int ops = (wave < NI - kSweepWaves * (W2_MAX - 1) ? W2_MAX : W2_MAX - 1) + 2 * NS;
-  // wait until at most `left` tiles' copies are still in flight (loads complete in order)
-  auto wait_tiles = [&](int left) {
-    if (left == 0) {
-      vm_wait<0>();
-    } else if (ops == W2_MAX + 2 * NS) {
-      vm_wait<W2_MAX + 2 * NS>();
-    } else {
-      vm_wait<W2_MAX - 1 + 2 * NS>();
-    }
-  };
-
-  // matrix-core chain of the tile in stage stg, seeded with its U slice
-  auto mma = [&](int stg, f32x16& acc, uint4 (&x)[2]) {
-    const uint4* sl = lds + stg * SCH;
-    float u[16];
-    widen8(sl[s_idx0], u);
-    widen8(sl[s_idx1], u + 8);
-    if (NS == 2) {
-      x[0] = sl[s_idx0 + stream_tile_chunks()];
-      x[1] = sl[s_idx1 + stream_tile_chunks()];
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = u[j];
-    const uint4* ab = sl + a_idx;
+    // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row
+    bf16x8 bh[NKS];
+    bf16x8 bl[SPLIT ? NKS : 1];
+    const void* brow = live ? Epi::brow(ep, row) : nullptr;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 a = as_bf16x8(ab[2 * ks]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc, 0, 0, 0);
-      if (SPLIT) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[SPLIT ? ks : 0], acc, 0, 0, 0);
+      uint4 hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
+      if (live) {
+        const int k0 = 16 * ks + 8 * h;
+        if (SPLIT) {
+          const float* p = reinterpret_cast<const float*>(brow) + k0;
+          const float4 a = *reinterpret_cast<const float4*>(p);
+          const float4 c = *reinterpret_cast<const float4*>(p + 4);
+          const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+          split8(x, hi, lo);
+        } else {
+          hi = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(brow) + k0);
+        }
+      }
+      bh[ks] = as_bf16x8(hi);
+      if (SPLIT) bl[SPLIT ? ks : 0] = as_bf16x8(lo);
     }
-  };
+    typename Epi::State st;
+    Epi::init(ep, st, live ? row : -1);
 
-  int b0, b1;
-  range_blocks(g, range, b0, b1);
-  // the last block of the vocabulary is short when V % 64 != 0: it leaves the pipeline
-  const bool ragged = (b1 * kVB > g.V);
-  const int bp1 = ragged ? b1 - 1 : b1;  // pipelined blocks [b0, bp1)
-  const int t0 = 2 * b0, t1 = 2 * bp1;
-
-  // a wait the compiler sees: every load issued so far (B rows, epilogue state) has
-  // landed, so none of them is pending at the loop header
-  __builtin_amdgcn_s_waitcnt(0);
+    // per-lane byte offsets of the copies (constant over tiles)
+    //   W2t copy i (index I = wave + 8i): lane -> padded position P = 64I + lane -> tile row
+    //   m = P / RS, chunk c = P % RS; the pad chunk and positions past the tile read row 0
+    //   stream copy k: lane -> chunk lane & 3 (xor-permuted) of the wave's row 16k + lane/4;
+    //   rows past the end read the last live row
+    uint32_t w2off[W2_MAX];
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (t0 + d < t1) issue(t0 + d, d);
-  f32x16 accA, accB;
-  uint4 xA[2], xB[2];
-  xA[0] = xA[1] = xB[0] = xB[1] = make_uint4(0, 0, 0, 0);
-  int stg = 0;
-  // one pipeline step: tile t's copies are awaited, tile t+D's issued, tile t's matrix
-  // chain runs, and the epilogue of tile t-1 (HALF = 1 - half of t) overlaps it
-  for (int t = t0; t < t1; t += 2) {
-    const int b = t >> 1;
-    // -- tile t = 2b (half 0); epilogue of tile 2b-1 (half 1 of block b-1)
-    wait_tiles(D == 2 && t + 1 < t1 ? 1 : 0);
-    __syncthreads();
-    if (t + D < t1) issue(t + D, stg + D >= NSTAGE ? stg + D - NSTAGE : stg + D);
-    if (t > t0) Epi::refresh(ep, st, b - 1, row);
-    mma(stg, accA, xA);
-    if (t > t0) Epi::template tile<1, false>(ep, st, accB, xB, b - 1, row, owner);
-    stg = stg + 1 == NSTAGE ? 0 : stg + 1;
-    // -- tile t + 1 (half 1); epilogue of tile t (half 0 of block b)
-    wait_tiles(D == 2 && t + 2 < t1 ? 1 : 0);
-    __syncthreads();
-    if (t + 1 + D < t1) issue(t + 1 + D, stg + D >= NSTAGE ? stg + D - NSTAGE : stg + D);
-    mma(stg, accB, xB);
-    Epi::template tile<0, false>(ep, st, accA, xA, b, row, owner);
-    stg = stg + 1 == NSTAGE ? 0 : stg + 1;
-  }
-  if (t1 > t0) {
-    Epi::refresh(ep, st, bp1 - 1, row);
-    Epi::template tile<1, false>(ep, st, accB, xB, bp1 - 1, row, owner);
-  }
-  if (ragged) {  // the short last block, unpipelined
-    const int b = b1 - 1;
+    for (int i = 0; i < W2_MAX; ++i) {
+      const int P = 64 * (wave + kSweepWaves * i) + lane;
+      const int m = P / RS, c = P - m * RS;
+      w2off[i] = (m < 32 && c < CH) ? (uint32_t)(tile_row_of_vocab(m) * g.r + 8 * c) * 2u : 0u;
+    }
+    uint32_t soff[NS][2];
+    int sx[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int rl = 16 * k + (lane >> 2);
+      int rr = group_row0 + wave * 32 + rl;
+      if (rr >= nrows) rr = nrows - 1;
+      sx[k] = 8 * ((lane & 3) ^ ((rl >> 2) & 3));  // element offset inside the 32-id slice
+#pragma unroll
+      for (int s = 0; s < NS; ++s) soff[s][k] = (Epi::srow(ep, s, rr) + (uint32_t)sx[k]) * 2u;
+    }
+    const uint16_t* sb[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sb[s] = Epi::sbase(ep, s);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+    // LDS chunk indices this lane reads (stage 0): A fragments at a_idx + 2*ks, stream chunks
+    const int a_idx = n * RS + h;
+    const int s_idx0 = w2_tile_chunks(CH) + wave * 128 + stream_pos(n, h);
+    const int s_idx1 = w2_tile_chunks(CH) + wave * 128 + stream_pos(n, 2 + h);
+
+    // copies of full tile t into stage stg (scalar bases; per-lane offsets fixed)
+    auto issue = [&](int t, int stg) {
+      const uint32_t base = lds0 + 16u * stg * SCH;
+      const uint16_t* w2b = g.W2t + (size_t)kTile * t * g.r;
+#pragma unroll
+      for (int i = 0; i < W2_MAX; ++i) {
+        const int I = wave + kSweepWaves * i;
+        if (I < NI) dma16s(w2b, w2off[i], base + 16u * 64u * I);
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          dma16s(sb[s] + kTile * t, soff[s][k],
+                 base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
+    };
+    // the same for the short last tile: clamp each lane's source into the arrays
+    auto issue_ragged = [&](int t, int stg) {
+      const uint32_t base = lds0 + 16u * stg * SCH;
+#pragma unroll
+      for (int i = 0; i < W2_MAX; ++i) {
+        const int I = wave + kSweepWaves * i;
+        const int P = 64 * I + lane;
+        const int m = P / RS, c = P - m * RS;
+        int v = kTile * t + (m < 32 ? tile_row_of_vocab(m) : 0);
+        if (v >= g.V) v = g.V - 1;
+        const uint32_t off = (m < 32 && c < CH) ? (uint32_t)(v * g.r + 8 * c) * 2u : 0u;
+        if (I < NI) dma16s(g.W2t, off, base + 16u * 64u * I);
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          int v = kTile * t + sx[k];
+          if (v > g.V - 8) v = g.V - 8;
+          dma16s(sb[s], soff[s][k] + (uint32_t)(v - sx[k]) * 2u,
+                 base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
+        }
+    };
+    // loads one tile puts in flight for this wave
+    constexpr int OPS_BIG = W2_MAX + 2 * NS, OPS_SMALL = W2_MAX - 1 + 2 * NS;
+    const bool big = wave < NI - kSweepWaves * (W2_MAX - 1);
+    // wait until at most `left` (0 .. D-1) tiles' copies are still in flight (loads complete
+    // in order)
+    auto wait_tiles = [&](int left) {
+      if (left <= 0) {
+        vm_wait<0>();
+      } else if (left == 1 || D < 3) {
+        if (big) vm_wait<OPS_BIG>(); else vm_wait<OPS_SMALL>();
+      } else {
+        if (big) vm_wait<2 * OPS_BIG>(); else vm_wait<2 * OPS_SMALL>();
+      }
+    };
+
+    // matrix-core chain of the tile in stage stg, seeded with its U slice
+    auto mma = [&](int stg, f32x16& acc, uint4 (&x)[2]) {
+      const uint4* sl = lds + stg * SCH;
+      float u[16];
+      widen8(sl[s_idx0], u);
+      widen8(sl[s_idx1], u + 8);
+      if (NS == 2) {
+        x[0] = sl[s_idx0 + stream_tile_chunks()];
+        x[1] = sl[s_idx1 + stream_tile_chunks()];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] = u[j];
+      const uint4* ab = sl + a_idx;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 a = as_bf16x8(ab[2 * ks]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc, 0, 0, 0);
+        if (SPLIT) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[SPLIT ? ks : 0], acc, 0, 0, 0);
+      }
+    };
+
+    int b0, b1;
+    int rg = range + (group_row0 & 0);
+    asm volatile("" : "+s"(rg));
+    range_blocks(g, rg, b0, b1);
+    // the last block of the vocabulary is short when V % 64 != 0: it leaves the pipeline
+    const bool ragged = (b1 * kVB > g.V);
+    const int bp1 = ragged ? b1 - 1 : b1;  // pipelined blocks [b0, bp1)
+    const int t0 = 2 * b0, t1 = 2 * bp1;
+
+    // a wait the compiler sees: every load issued so far (B rows, epilogue state) has
+    // landed, so none of them is pending at the loop header
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (t0 + d < t1) issue(t0 + d, d);
+    f32x16 accA, accB;
+    uint4 xA[2], xB[2];
+    xA[0] = xA[1] = xB[0] = xB[1] = make_uint4(0, 0, 0, 0);
+    int stg = 0;
+    // one pipeline step: tile t's copies are awaited, tile t+D's issued, tile t's matrix
+    // chain runs, and the epilogue of tile t-1 (HALF = 1 - half of t) overlaps it
+    for (int t = t0; t < t1; t += 2) {
+      const int b = t >> 1;
+      // -- tile t = 2b (half 0); epilogue of tile 2b-1 (half 1 of block b-1)
+      wait_tiles(min(D - 1, t1 - 1 - t));
+      stage_barrier();
+      if (t + D < t1) issue(t + D, stg + D >= NSTAGE ? stg + D - NSTAGE : stg + D);
+      if (t > t0) Epi::refresh(ep, st, b - 1, row);
+      mma(stg, accA, xA);
+      if (t > t0) Epi::template tile<1, false>(ep, st, accB, xB, b - 1, row, owner);
+      stg = stg + 1 == NSTAGE ? 0 : stg + 1;
+      // -- tile t + 1 (half 1); epilogue of tile t (half 0 of block b)
+      wait_tiles(min(D - 1, t1 - 2 - t));
+      stage_barrier();
+      if (t + 1 + D < t1) issue(t + 1 + D, stg + D >= NSTAGE ? stg + D - NSTAGE : stg + D);
+      mma(stg, accB, xB);
+      Epi::template tile<0, false>(ep, st, accA, xA, b, row, owner);
+      stg = stg + 1 == NSTAGE ? 0 : stg + 1;
+    }
+    if (t1 > t0) {
+      Epi::refresh(ep, st, bp1 - 1, row);
+      Epi::template tile<1, false>(ep, st, accB, xB, bp1 - 1, row, owner);
+    }
+    if (ragged) {  // the short last block, unpipelined
+      const int b = b1 - 1;
+      vm_wait<0>();
+      __syncthreads();
+      issue_ragged(2 * b, 0);
+      issue_ragged(2 * b + 1, 1);
+      vm_wait<0>();
+      __syncthreads();
+      mma(0, accA, xA);
+      Epi::template tile<0, true>(ep, st, accA, xA, b, row, owner);
+      mma(1, accB, xB);
+      Epi::refresh(ep, st, b, row);
+      Epi::template tile<1, true>(ep, st, accB, xB, b, row, owner);
+    }
     vm_wait<0>();
-    __syncthreads();
-    issue_ragged(2 * b, 0);
-    issue_ragged(2 * b + 1, 1);
-    vm_wait<0>();
-    __syncthreads();
-    mma(0, accA, xA);
-    Epi::template tile<0, true>(ep, st, accA, xA, b, row, owner);
-    mma(1, accB, xB);
-    Epi::refresh(ep, st, b, row);
-    Epi::template tile<1, true>(ep, st, accB, xB, b, row, owner);
+    Epi::finish(ep, st, row, owner, range);
+    __syncthreads();  // the next group reuses the stages
   }
-  vm_wait<0>();
-  Epi::finish(ep, st, row, owner, range);
 }
 
-// host-side geometry: row groups of 256, target_ranges vocabulary ranges per group
+// host-side geometry: target_ranges vocabulary ranges (the grid), row groups of 256
 inline SweepGeom make_geom(int nrows, int V, int r, const uint16_t* W2t, int target_ranges) {
   SweepGeom g{};
   g.nrows = nrows;
@@ -433,29 +449,30 @@ inline void launch_sweep_nks(const SweepGeom& g, const typename Epi::Params& p, 
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
     attr = true;
   }
-  kern<<<g.nranges * g.ngroups, kSweepThreads, sh, s>>>(g, p);
+  kern<<<g.nranges, kSweepThreads, sh, s>>>(g, p);
 }
 
-// launch with NKS = r / 16 fixed at compile time (r in {16, 32, 64, 128, 256}) and three
-// pipeline stages when the device's LDS allows them, else two
+// launch with NKS = r / 16 fixed at compile time (r in {16, 32, 64, 128, 256}) and as many
+// pipeline stages (2 to 4) as the device's LDS allows
+template <int NKS, bool SPLIT, class Epi>
+inline void launch_sweep_stages(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s) {
+  const size_t lds = device_max_lds();
+  if (sweep_lds_bytes(g.r, Epi::kStreams, 4) <= lds)
+    launch_sweep_nks<NKS, SPLIT, 4, Epi>(g, p, s);
+  else if (sweep_lds_bytes(g.r, Epi::kStreams, 3) <= lds)
+    launch_sweep_nks<NKS, SPLIT, 3, Epi>(g, p, s);
+  else
+    launch_sweep_nks<NKS, SPLIT, 2, Epi>(g, p, s);
+}
+
 template <bool SPLIT, class Epi>
 inline void launch_sweep(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s) {
-  const bool three = sweep_lds_bytes(g.r, Epi::kStreams, 3) <= device_max_lds();
   switch (g.nks) {
-    case 1:
-      three ? launch_sweep_nks<1, SPLIT, 3, Epi>(g, p, s) : launch_sweep_nks<1, SPLIT, 2, Epi>(g, p, s);
-      break;
-    case 2:
-      three ? launch_sweep_nks<2, SPLIT, 3, Epi>(g, p, s) : launch_sweep_nks<2, SPLIT, 2, Epi>(g, p, s);
-      break;
-    case 4:
-      three ? launch_sweep_nks<4, SPLIT, 3, Epi>(g, p, s) : launch_sweep_nks<4, SPLIT, 2, Epi>(g, p, s);
-      break;
-    case 8:
-      three ? launch_sweep_nks<8, SPLIT, 3, Epi>(g, p, s) : launch_sweep_nks<8, SPLIT, 2, Epi>(g, p, s);
-      break;
-    default:
-      three ? launch_sweep_nks<16, SPLIT, 3, Epi>(g, p, s) : launch_sweep_nks<16, SPLIT, 2, Epi>(g, p, s);
+    case 1: launch_sweep_stages<1, SPLIT, Epi>(g, p, s); break;
+    case 2: launch_sweep_stages<2, SPLIT, Epi>(g, p, s); break;
+    case 4: launch_sweep_stages<4, SPLIT, Epi>(g, p, s); break;
+    case 8: launch_sweep_stages<8, SPLIT, Epi>(g, p, s); break;
+    default: launch_sweep_stages<16, SPLIT, Epi>(g, p, s);
   }
 }
 

@@ -8,9 +8,11 @@
 //   prep    one workgroup: exclusive scans of ell; list A = (q, j) for j = 1..ell_q + 1
 //           (every row whose target normaliser is needed, the bonus row included), list B
 //           = (q, j) for j = 1..ell_q (every verified position);
-//   lse     one workgroup per list-A row: log-sum-exp of the target row; on the bonus row
-//           also the first level of the bonus sample (streams 5);
-//   decide  one thread per request: the acceptance tests u < p_j(x_j)/q_j(x_j) in order
+//   lse     each list-A row in kLsePieces block-aligned pieces (a persistent grid walks
+//           the pieces): (max, sum exp) of the target logits; on the bonus row also the
+//           first level of the bonus sample (stream 5) per piece;
+//   decide  one thread per request: merges the pieces into the target normalisers and
+//           the bonus block, then the acceptance tests u < p_j(x_j)/q_j(x_j) in order
 //           (stream 2), the first rejection j*, the accepted tokens;
 //   sweep   matrix cores over list B (sweep.h): q_j recomputed from U_j + bias_j W2 and
 //           normalised by the drafted lse; sum |p - q| per row, and on the row j* the
@@ -24,6 +26,10 @@
 
 namespace dspark {
 
+constexpr int kLsePieces = 4;   // pieces per target row in the lse pass
+constexpr int kLseThreads = 256;
+constexpr int kLseUnroll = 4;   // 16-byte loads in flight per thread
+
 struct VerifyWs {
   int* hdr;        // [0] = |A|, [1] = |B|
   int* offA;       // [R]
@@ -31,6 +37,7 @@ struct VerifyWs {
   int2* rowA;      // [R*(gamma+1)] (q, j)
   int2* rowB;      // [R*gamma]
   float* lset;     // [R*(gamma+1)] target log-sum-exp of list-A rows
+  float4* lpart;   // [R*(gamma+1)][kLsePieces] (max, sum exp, best G, block) per piece
   float2* bonus;   // [R] (best G, block) of the bonus row
   int* jstar;      // [R] first rejected position, 0 = none
   float4* partials;  // [R*gamma][nranges]: (sum |p-q|, best G, block, residual mass)
@@ -46,6 +53,7 @@ static VerifyWs carve_verify(void* ws, int R, int gamma, int V) {
   w.rowA = cv.take<int2>((size_t)R * (gamma + 1));
   w.rowB = cv.take<int2>((size_t)R * gamma);
   w.lset = cv.take<float>((size_t)R * (gamma + 1));
+  w.lpart = cv.take<float4>((size_t)R * (gamma + 1) * kLsePieces);
   w.bonus = cv.take<float2>((size_t)R);
   w.jstar = cv.take<int>((size_t)R);
   const int nblocks = (V + kVB - 1) / kVB;
@@ -104,83 +112,94 @@ __global__ void __launch_bounds__(1024) verify_prep_kernel(int R, int gamma, con
 __device__ __forceinline__ int clamp_len(int L, int gamma) { return L < 0 ? 0 : (L > gamma ? gamma : L); }
 
 // ---------------------------------------------------------------------------------------
-// lse: target normaliser per list-A row (+ first level of the bonus sample)
+// lse: (max, sum exp) of one piece of a list-A row (+ first level of the bonus sample)
 // ---------------------------------------------------------------------------------------
 template <class T>
-__global__ void __launch_bounds__(256) verify_lse_kernel(int R, int gamma, int V,
-                                                         const T* __restrict__ target,
-                                                         const int32_t* ell, VerifyWs ws,
-                                                         uint64_t seed, uint64_t cycle) {
-  __shared__ float sm[4], ss[4], sg[4];
-  __shared__ int sb[4];
-  const int i = blockIdx.x;
-  if (i >= ws.hdr[0]) return;
-  const int2 qj = ws.rowA[i];
-  const int q = qj.x, j = qj.y;
-  const int L = clamp_len(ell[q], gamma);
-  const bool bonus = (j == L + 1);
-  const T* row = target + ((size_t)q * (gamma + 1) + (j - 1)) * V;
-  const Rng rng(seed, cycle);
+__global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamma, int V,
+                                                                 const T* __restrict__ target,
+                                                                 const int32_t* ell, VerifyWs ws,
+                                                                 uint64_t seed, uint64_t cycle) {
+  __shared__ float4 red[kLseThreads / kWave];
+  const int nitems = ws.hdr[0] * kLsePieces;
+  const int nblocks = (V + kVB - 1) / kVB;
+  const int nch = V / 8;  // V % 8 == 0: whole chunks
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float M = -INFINITY, S = 0.0f, G = -INFINITY;
-  int Bk = 0x7fffffff;
-  const int nch = (V + 7) / 8;  // V % 8 == 0: whole chunks
-  for (int base = 0; base < nch; base += 256) {
-    const int ci = base + threadIdx.x;
-    float x[8];
-    float m = -INFINITY;
-    if (ci < nch) {
-      ld8<T>(row + (size_t)ci * 8, x);
+  const Rng rng(seed, cycle);
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int i = item / kLsePieces, piece = item - i * kLsePieces;
+    const int2 qj = ws.rowA[i];
+    const int q = qj.x, j = qj.y;
+    const int L = clamp_len(ell[q], gamma);
+    const bool bonus = (j == L + 1);
+    const T* row = target + ((size_t)q * (gamma + 1) + (j - 1)) * V;
+    // whole 64-id blocks per piece: chunks [c0, c1)
+    const int c0 = (int)(((long long)piece * nblocks) / kLsePieces) * 8;
+    const int c1 = min(nch, (int)(((long long)(piece + 1) * nblocks) / kLsePieces) * 8);
+    float M = -INFINITY, S = 0.0f, G = -INFINITY;
+    int Bk = 0x7fffffff;
+    for (int base = c0; base < c1; base += kLseThreads * kLseUnroll) {
+      float x[kLseUnroll][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, x[e]);
-    }
-    float s = 0.0f;
-    if (m != -INFINITY) {
+      for (int u = 0; u < kLseUnroll; ++u) {
+        const int ci = base + u * kLseThreads + threadIdx.x;
+        if (ci < c1) {
+          ld8<T>(row + (size_t)ci * 8, x[u]);
+        } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += __expf(x[e] - m);
-    }
-    if (bonus) {
-      // one 64-id block = 8 consecutive threads (chunks ci & ~7 .. ci | 7)
-      float bm = m, bs = s;
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        const float m2 = __shfl_xor(bm, o, kWave), s2 = __shfl_xor(bs, o, kWave);
-        lse_merge(bm, bs, m2, s2);
-      }
-      const int b = ci >> 3;
-      if ((threadIdx.x & 7) == 0 && ci < nch) {
-        const float g = gumbel_of(rng.word(kStreamBonusBlk, (uint32_t)q, (uint32_t)j, (uint32_t)b));
-        const float Gb = bm + __logf(bs) + g;
-        if (Gb > G) {
-          G = Gb;
-          Bk = b;
+          for (int e = 0; e < 8; ++e) x[u][e] = -INFINITY;
         }
       }
-    }
-    lse_merge(M, S, m, s);
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
-    lse_merge(M, S, m2, s2);
-  }
-  wave_argmax(G, Bk);
-  if (lane == 0) {
-    sm[wave] = M;
-    ss[wave] = S;
-    sg[wave] = G;
-    sb[wave] = Bk;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w) {
-      lse_merge(M, S, sm[w], ss[w]);
-      if (sg[w] > G || (sg[w] == G && sb[w] < Bk)) {
-        G = sg[w];
-        Bk = sb[w];
+#pragma unroll
+      for (int u = 0; u < kLseUnroll; ++u) {
+        float m = x[u][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) m = fmaxf(m, x[u][e]);
+        const float ref = m == -INFINITY ? 0.0f : m;
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += __expf(x[u][e] - ref);
+        if (bonus) {
+          // one 64-id block = 8 consecutive threads
+          float bm = m, bs = s;
+#pragma unroll
+          for (int o = 1; o < 8; o <<= 1) {
+            const float m2 = __shfl_xor(bm, o, kWave), s2 = __shfl_xor(bs, o, kWave);
+            lse_merge(bm, bs, m2, s2);
+          }
+          const int ci = base + u * kLseThreads + threadIdx.x;
+          const int b = ci >> 3;
+          if ((threadIdx.x & 7) == 0 && ci < c1) {
+            const float g = gumbel_of(rng.word(kStreamBonusBlk, (uint32_t)q, (uint32_t)j, (uint32_t)b));
+            const float Gb = bm + __logf(bs) + g;
+            if (Gb > G) {  // blocks visited in increasing order per thread
+              G = Gb;
+              Bk = b;
+            }
+          }
+        }
+        lse_merge(M, S, m, s);
       }
     }
-    ws.lset[i] = M + __logf(S);
-    if (bonus) ws.bonus[q] = make_float2(G, __int_as_float(Bk));
+    for (int o = 32; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
+      lse_merge(M, S, m2, s2);
+    }
+    wave_argmax(G, Bk);
+    if (lane == 0) red[wave] = make_float4(M, S, G, __int_as_float(Bk));
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 1; w < kLseThreads / kWave; ++w) {
+        const float4 o = red[w];
+        lse_merge(M, S, o.x, o.y);
+        const int ob = __float_as_int(o.w);
+        if (o.z > G || (o.z == G && ob < Bk)) {
+          G = o.z;
+          Bk = ob;
+        }
+      }
+      ws.lpart[item] = make_float4(M, S, G, __int_as_float(Bk));
+    }
+    __syncthreads();  // red is reused by the next item
   }
 }
 
@@ -195,6 +214,25 @@ __global__ void __launch_bounds__(256) verify_decide_kernel(
   const int q = blockIdx.x * 256 + threadIdx.x;
   if (q >= R) return;
   const int L = clamp_len(ell[q], gamma);
+  // target normalisers of rows 1..L+1 and the bonus block, from the lse pieces (in piece
+  // order, so ties keep the lowest block)
+  for (int j = 1; j <= L + 1; ++j) {
+    const int i = ws.offA[q] + j - 1;
+    float M = -INFINITY, S = 0.0f, G = -INFINITY;
+    int Bk = 0x7fffffff;
+#pragma unroll
+    for (int pc = 0; pc < kLsePieces; ++pc) {
+      const float4 o = ws.lpart[(size_t)i * kLsePieces + pc];
+      lse_merge(M, S, o.x, o.y);
+      const int ob = __float_as_int(o.w);
+      if (o.z > G || (o.z == G && ob < Bk)) {
+        G = o.z;
+        Bk = ob;
+      }
+    }
+    ws.lset[i] = M + __logf(S);
+    if (j == L + 1) ws.bonus[q] = make_float2(G, __int_as_float(Bk));
+  }
   const Rng rng(seed, cycle);
   int js = 0;
   for (int j = 1; j <= L; ++j) {
@@ -500,16 +538,22 @@ static int verify_run(int R, int gamma, int V, int r, const void* target_, const
   constexpr bool SPLIT = BF && sizeof(BT) == 4;
 
   verify_prep_kernel<<<1, 1024, 0, stream>>>(R, gamma, ell, ws, status);
-  verify_lse_kernel<T><<<R * (gamma + 1), 256, 0, stream>>>(R, gamma, V, target, ell, ws, seed, cycle);
+  {
+    // persistent grid over the pieces of list A (its length is known on the device only)
+    const int items = R * (gamma + 1) * kLsePieces, cap = 8 * device_cus();
+    verify_lse_kernel<T><<<items < cap ? items : cap, kLseThreads, 0, stream>>>(
+        R, gamma, V, target, ell, ws, seed, cycle);
+  }
   verify_decide_kernel<T><<<(R + 255) / 256, 256, 0, stream>>>(
       R, gamma, V, target, x, lse, logit_x, ell, ws, seed, cycle, n_acc, y, status);
 
   const int rows_max = R * gamma;
   int nranges;
   if (BF) {
-    // every vocabulary range for every possible row group; groups past the verified rows
-    // (known on the device only) exit at once
-    SweepGeom g = make_geom(rows_max, V, r, reinterpret_cast<const uint16_t*>(W2t), device_cus());
+    // one workgroup per vocabulary range; each walks the row groups of list B, whose
+    // length is known on the device only
+    SweepGeom g = make_geom(rows_max, V, r, reinterpret_cast<const uint16_t*>(W2t),
+                            device_cus() < kMaxRanges ? device_cus() : kMaxRanges);
     nranges = g.nranges;
     VerifySweepParams p{};
     p.U = reinterpret_cast<const uint16_t*>(U);
