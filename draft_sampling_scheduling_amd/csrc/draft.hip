@@ -5,9 +5,9 @@
 //   sweep   (matrix cores, see sweep.h): per request and per vocabulary range, the running
 //           normaliser (max, sum exp) of l = U_k + bias_k and the best block score
 //           LSE_b + g_b of the sampler's first level;
-//   combine (one wave per request): merge the ranges, take the winning block, recompute its
-//           64 logits, draw x_k inside it (second level), and write lse, l(x_k), c_k and
-//           the bias row.
+//   combine (one workgroup of four waves per request): merge the ranges, take the winning
+//           block, recompute its 64 logits (the r-long dot products split over the waves),
+//           draw x_k inside it (second level), and write lse, l(x_k), c_k and the bias row.
 // The position-independent half of the confidence, w_h . h_k, is computed for all k by one
 // launch up front; the RNN head adds one state-update launch per position and one
 // h-projection launch up front.
@@ -42,6 +42,8 @@ __global__ void __launch_bounds__(256) conf_h_kernel(int rows, int d, const T* _
 // ---------------------------------------------------------------------------------------
 // sweep epilogue of a draft step
 // ---------------------------------------------------------------------------------------
+constexpr int kCombineThreads = 256;  // per request in the combine step
+
 struct DraftSweepParams {
   const uint16_t* U;     // U + (k-1)*V; row q at U + q*ustride  (bf16)
   size_t ustride;        // gamma * V
@@ -194,19 +196,29 @@ __global__ void __launch_bounds__(64) draft_sweep_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// combine: one wave per request
+// combine: one workgroup per request
 // ---------------------------------------------------------------------------------------
 template <class T, bool RNN>
-__global__ void __launch_bounds__(64) draft_combine_kernel(
+__global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
     int R, int gamma, int V, int r, int d, const T* __restrict__ U, const T* __restrict__ W1,
     const T* __restrict__ W2t, const float* __restrict__ w, const float* __restrict__ zh,
     const int32_t* prev, int prev_stride, const float* __restrict__ orow,
     const float4* __restrict__ partials, int nranges, uint32_t k, uint64_t seed, uint64_t cycle,
     int32_t* x, float* c, float* lse, float* logit_x, void* bias_rows, int32_t* status) {
-  const int q = blockIdx.x, lane = threadIdx.x;
+  constexpr int kWaves = kCombineThreads / kWave;
+  __shared__ float4 red[kWaves];
+  __shared__ float dotp[kWaves][kWave];
+  __shared__ float zred[kWaves];
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t rk = (size_t)q * gamma + (k - 1);
+  // the previous token's embedding row (independent of the partials)
+  const int32_t tprev = checked_token(prev[(size_t)q * prev_stride], V, status);
+  const T* e = W1 + (size_t)tprev * r;
+
+  // first level: normaliser and winning block over the ranges' partials
   float M = -INFINITY, S = 0.0f, G = -INFINITY;
   int Bk = 0x7fffffff;
-  for (int i = lane; i < nranges; i += 64) {
+  for (int i = tid; i < nranges; i += kCombineThreads) {
     const float4 pr = partials[(size_t)q * nranges + i];
     const int pb = __float_as_int(pr.w);
     if (pb == 0x7fffffff) continue;
@@ -222,59 +234,80 @@ __global__ void __launch_bounds__(64) draft_combine_kernel(
     lse_merge(M, S, m2, s2);
   }
   wave_argmax(G, Bk);
+  if (lane == 0) red[wave] = make_float4(M, S, G, __int_as_float(Bk));
+  __syncthreads();
+  {
+    const float4 r0 = red[0];
+    M = r0.x; S = r0.y; G = r0.z; Bk = __float_as_int(r0.w);
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) {
+      const float4 ri = red[i];
+      lse_merge(M, S, ri.x, ri.y);
+      const int bi = __float_as_int(ri.w);
+      if (ri.z > G || (ri.z == G && bi < Bk)) {
+        G = ri.z;
+        Bk = bi;
+      }
+    }
+  }
   const int nblocks = (V + kVB - 1) / kVB;
   if (Bk < 0 || Bk >= nblocks) Bk = 0;  // only if every partial was empty (cannot happen)
-  const float row_lse = M + __logf(S);
 
-  const int32_t tprev = checked_token(prev[(size_t)q * prev_stride], V, status);
-  const T* e = W1 + (size_t)tprev * r;
-  const size_t rk = (size_t)q * gamma + (k - 1);
-
-  // second level: recompute the winning block's logits and draw inside it
+  // second level: the winning block's 64 logits, the k sum split over the waves in
+  // 8-element chunks
   const int v = Bk * kVB + lane;
-  float l = -INFINITY;
+  const float u = (wave == 0 && v < V) ? ld<T>(U, (size_t)q * gamma * V + (size_t)(k - 1) * V + v) : 0.0f;
+  float part = 0.0f;
   if (v < V) {
-    float acc = 0.0f;
     const T* wr = W2t + (size_t)v * r;
-    for (int i = 0; i < r; i += 8) {
+    for (int ch = wave; ch < r / 8; ch += kWaves) {
       float a[8], bv[8];
-      ld8<T>(wr + i, a);
+      ld8<T>(wr + ch * 8, a);
       if (RNN) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bv[j] = orow[(size_t)q * r + i + j];
+        for (int j = 0; j < 8; ++j) bv[j] = orow[(size_t)q * r + ch * 8 + j];
       } else {
-        ld8<T>(e + i, bv);
+        ld8<T>(e + ch * 8, bv);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = fmaf(bv[j], a[j], acc);
+      for (int j = 0; j < 8; ++j) part = fmaf(bv[j], a[j], part);
     }
-    l = ld<T>(U, (size_t)q * gamma * V + (size_t)(k - 1) * V + v) + acc;
   }
-  const Rng rng(seed, cycle);
-  float score = (v < V) ? l + gumbel_of(rng.word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v))
-                        : -INFINITY;
-  int idx = v;
-  wave_argmax(score, idx);
-  const float lx = __shfl(l, idx - Bk * kVB, kWave);
-
-  // confidence head: sigmoid(w_h . h_k + w_e . W1[x_{k-1}])
+  dotp[wave][lane] = part;
+  // confidence head, embedding part: w_e . W1[x_{k-1}]
   float ze = 0.0f;
-  for (int i = lane; i < r; i += 64) ze = fmaf(w[d + i], ld<T>(e, i), ze);
+  for (int i = tid; i < r; i += kCombineThreads) ze = fmaf(w[d + i], ld<T>(e, i), ze);
   ze = wave_sum(ze);
-  const float z = zh[rk] + ze;
-
-  if (lane == 0) {
-    x[rk] = idx;
-    c[rk] = 1.0f / (1.0f + __expf(-z));
-    lse[rk] = row_lse;
-    logit_x[rk] = lx;
-  }
+  if (lane == 0) zred[wave] = ze;
+  // the bias row this step used, for verification
   if (RNN) {
     float* br = static_cast<float*>(bias_rows) + rk * r;
-    for (int i = lane; i < r; i += 64) br[i] = orow[(size_t)q * r + i];
+    for (int i = tid; i < r; i += kCombineThreads) br[i] = orow[(size_t)q * r + i];
   } else {
     T* br = static_cast<T*>(bias_rows) + rk * r;
-    for (int i = lane; i < r; i += 64) br[i] = e[i];
+    for (int i = tid; i < r; i += kCombineThreads) br[i] = e[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) acc += dotp[i][lane];
+    const float l = (v < V) ? u + acc : -INFINITY;
+    const Rng rng(seed, cycle);
+    float score = (v < V) ? l + gumbel_of(rng.word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v))
+                          : -INFINITY;
+    int idx = v;
+    wave_argmax(score, idx);
+    const float lx = __shfl(l, idx - Bk * kVB, kWave);
+    float z = zh[rk];
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) z += zred[i];
+    if (lane == 0) {
+      x[rk] = idx;
+      c[rk] = 1.0f / (1.0f + __expf(-z));
+      lse[rk] = M + __logf(S);
+      logit_x[rk] = lx;
+    }
   }
 }
 
@@ -494,11 +527,11 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
     }
     if (eve && eve[k - 1]) (void)hipEventRecord(eve[k - 1], stream);
     if (rnn)
-      draft_combine_kernel<T, true><<<R, 64, 0, stream>>>(
+      draft_combine_kernel<T, true><<<R, kCombineThreads, 0, stream>>>(
           R, gamma, V, r, d, U, W1, W2t, w, ws.zh, prev, ps, ws.orow, ws.partials, nranges,
           (uint32_t)k, seed, cycle, x, c, lse, logit_x, bias_rows, status);
     else
-      draft_combine_kernel<T, false><<<R, 64, 0, stream>>>(
+      draft_combine_kernel<T, false><<<R, kCombineThreads, 0, stream>>>(
           R, gamma, V, r, d, U, W1, W2t, w, ws.zh, prev, ps, nullptr, ws.partials, nranges,
           (uint32_t)k, seed, cycle, x, c, lse, logit_x, bias_rows, status);
   }

@@ -208,30 +208,9 @@ __global__ void __launch_bounds__(kSweepThreads, 1)
     const bool live = row < nrows;
     const bool owner = live && h == 0;
 
-    // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row
-    bf16x8 bh[NKS];
+    bf16x8 bh[NKS];  // B operand (filled once the first tiles are in flight)
     bf16x8 bl[SPLIT ? NKS : 1];
-    const void* brow = live ? Epi::brow(ep, row) : nullptr;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      uint4 hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
-      if (live) {
-        const int k0 = 16 * ks + 8 * h;
-        if (SPLIT) {
-          const float* p = reinterpret_cast<const float*>(brow) + k0;
-          const float4 a = *reinterpret_cast<const float4*>(p);
-          const float4 c = *reinterpret_cast<const float4*>(p + 4);
-          const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-          split8(x, hi, lo);
-        } else {
-          hi = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(brow) + k0);
-        }
-      }
-      bh[ks] = as_bf16x8(hi);
-      if (SPLIT) bl[SPLIT ? ks : 0] = as_bf16x8(lo);
-    }
     typename Epi::State st;
-    Epi::init(ep, st, live ? row : -1);
 
     // per-lane byte offsets of the copies (constant over tiles)
     //   W2t copy i (index I = wave + 8i): lane -> padded position P = 64I + lane -> tile row
@@ -349,12 +328,37 @@ __global__ void __launch_bounds__(kSweepThreads, 1)
     const int bp1 = ragged ? b1 - 1 : b1;  // pipelined blocks [b0, bp1)
     const int t0 = 2 * b0, t1 = 2 * bp1;
 
-    // a wait the compiler sees: every load issued so far (B rows, epilogue state) has
-    // landed, so none of them is pending at the loop header
-    __builtin_amdgcn_s_waitcnt(0);
+    // the first tiles go out before anything else: they depend on nothing the B rows or
+    // the epilogue state need
 #pragma unroll
     for (int d = 0; d < D; ++d)
       if (t0 + d < t1) issue(t0 + d, d);
+
+    // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row
+    const void* brow = live ? Epi::brow(ep, row) : nullptr;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
+      if (live) {
+        const int k0 = 16 * ks + 8 * h;
+        if (SPLIT) {
+          const float* p = reinterpret_cast<const float*>(brow) + k0;
+          const float4 a = *reinterpret_cast<const float4*>(p);
+          const float4 c = *reinterpret_cast<const float4*>(p + 4);
+          const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+          split8(x, hi, lo);
+        } else {
+          hi = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(brow) + k0);
+        }
+      }
+      bh[ks] = as_bf16x8(hi);
+      if (SPLIT) bl[SPLIT ? ks : 0] = as_bf16x8(lo);
+    }
+    Epi::init(ep, st, live ? row : -1);
+
+    // a wait the compiler sees: every load issued so far (first tiles, B rows, epilogue
+    // state) has landed, so none of them is pending at the loop header
+    __builtin_amdgcn_s_waitcnt(0);
     f32x16 accA, accB;
     uint4 xA[2], xB[2];
     xA[0] = xA[1] = xB[0] = xB[1] = make_uint4(0, 0, 0, 0);

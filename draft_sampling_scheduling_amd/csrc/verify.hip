@@ -8,36 +8,36 @@
 //   prep    one workgroup: exclusive scans of ell; list A = (q, j) for j = 1..ell_q + 1
 //           (every row whose target normaliser is needed, the bonus row included), list B
 //           = (q, j) for j = 1..ell_q (every verified position);
-//   lse     each list-A row in kLsePieces block-aligned pieces (a persistent grid walks
-//           the pieces): (max, sum exp) of the target logits; on the bonus row also the
-//           first level of the bonus sample (stream 5) per piece;
-//   decide  one thread per request: merges the pieces into the target normalisers and
-//           the bonus block, then the acceptance tests u < p_j(x_j)/q_j(x_j) in order
-//           (stream 2), the first rejection j*, the accepted tokens;
+//   lse     each list-A row in items of 256 blocks of 64 ids (a persistent grid walks the
+//           items; loads coalesced, 8 lanes per block): (max, sum exp) of the target
+//           logits; on the bonus row also the first level of the bonus sample (stream 5);
+//   decide  one wave per request, one lane per position: merges the lse items into the
+//           target normalisers (and the bonus block), then the acceptance tests
+//           u < p_j(x_j)/q_j(x_j) (stream 2), the first rejection j*, the accepted tokens;
 //   sweep   matrix cores over list B (sweep.h): q_j recomputed from U_j + bias_j W2 and
 //           normalised by the drafted lse; sum |p - q| per row, and on the row j* the
 //           residual max(0, p - q) per 64-id block with its first-level Gumbel score
 //           (stream 3);
-//   final   one wave per request: c* for every verified row, then the second level of
-//           the correction (stream 4) or of the bonus (stream 6).
+//   final   one workgroup of four waves per request: c* for every verified row, then the
+//           second level of the correction (stream 4) or of the bonus (stream 6).
 #include "dev.h"
 #include "host.h"
 #include "sweep.h"
 
 namespace dspark {
 
-constexpr int kLsePieces = 4;   // pieces per target row in the lse pass
-constexpr int kLseThreads = 256;
-constexpr int kLseUnroll = 4;   // 16-byte loads in flight per thread
+constexpr int kLseThreads = 256;  // lse pass: one thread per 64-id block, 256 blocks per item
+
+__host__ __device__ inline int lse_tiles(int V) { return ((V + kVB - 1) / kVB + kLseThreads - 1) / kLseThreads; }
 
 struct VerifyWs {
   int* hdr;        // [0] = |A|, [1] = |B|
   int* offA;       // [R]
   int* offB;       // [R]
-  int2* rowA;      // [R*(gamma+1)] (q, j)
+  int4* rowA;      // [R*(gamma+1)] (q, j, 1 if j is the bonus row, 0)
   int2* rowB;      // [R*gamma]
   float* lset;     // [R*(gamma+1)] target log-sum-exp of list-A rows
-  float4* lpart;   // [R*(gamma+1)][kLsePieces] (max, sum exp, best G, block) per piece
+  float4* lpart;   // [R*(gamma+1)][lse_tiles(V)] (max, sum exp, best G, block) per item
   float2* bonus;   // [R] (best G, block) of the bonus row
   int* jstar;      // [R] first rejected position, 0 = none
   float4* partials;  // [R*gamma][nranges]: (sum |p-q|, best G, block, residual mass)
@@ -50,10 +50,10 @@ static VerifyWs carve_verify(void* ws, int R, int gamma, int V) {
   w.hdr = cv.take<int>(4);
   w.offA = cv.take<int>((size_t)R);
   w.offB = cv.take<int>((size_t)R);
-  w.rowA = cv.take<int2>((size_t)R * (gamma + 1));
+  w.rowA = cv.take<int4>((size_t)R * (gamma + 1));
   w.rowB = cv.take<int2>((size_t)R * gamma);
   w.lset = cv.take<float>((size_t)R * (gamma + 1));
-  w.lpart = cv.take<float4>((size_t)R * (gamma + 1) * kLsePieces);
+  w.lpart = cv.take<float4>((size_t)R * (gamma + 1) * lse_tiles(V));
   w.bonus = cv.take<float2>((size_t)R);
   w.jstar = cv.take<int>((size_t)R);
   const int nblocks = (V + kVB - 1) / kVB;
@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(1024) verify_prep_kernel(int R, int gamma, con
     L = L < 0 ? 0 : (L > gamma ? gamma : L);
     ws.offA[q] = oa;
     ws.offB[q] = ob;
-    for (int j = 1; j <= L + 1; ++j) ws.rowA[oa + j - 1] = make_int2(q, j);
+    for (int j = 1; j <= L + 1; ++j) ws.rowA[oa + j - 1] = make_int4(q, j, j == L + 1, 0);
     for (int j = 1; j <= L; ++j) ws.rowB[ob + j - 1] = make_int2(q, j);
     oa += L + 1;
     ob += L;
@@ -112,78 +112,99 @@ __global__ void __launch_bounds__(1024) verify_prep_kernel(int R, int gamma, con
 __device__ __forceinline__ int clamp_len(int L, int gamma) { return L < 0 ? 0 : (L > gamma ? gamma : L); }
 
 // ---------------------------------------------------------------------------------------
-// lse: (max, sum exp) of one piece of a list-A row (+ first level of the bonus sample)
+// lse: (max, sum exp) of 256 blocks of a list-A row (+ first level of the bonus sample)
 // ---------------------------------------------------------------------------------------
+// reductions over the 8 lanes 8k .. 8k+7 on the DPP network (xor 1, xor 2, then the
+// half-row mirror, which pairs the two quads)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  return fmaxf(x, dpp_f<0x141>(x));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  return x + dpp_f<0x141>(x);
+}
+
 template <class T>
 __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamma, int V,
                                                                  const T* __restrict__ target,
                                                                  const int32_t* ell, VerifyWs ws,
                                                                  uint64_t seed, uint64_t cycle) {
   __shared__ float4 red[kLseThreads / kWave];
-  const int nitems = ws.hdr[0] * kLsePieces;
+  const int tiles = lse_tiles(V);
+  const int nitems = ws.hdr[0] * tiles;
   const int nblocks = (V + kVB - 1) / kVB;
-  const int nch = V / 8;  // V % 8 == 0: whole chunks
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const Rng rng(seed, cycle);
+  // the row descriptor of the next item is fetched while the current one streams
+  int4 info = blockIdx.x < nitems ? ws.rowA[blockIdx.x / tiles] : make_int4(0, 1, 0, 0);
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int i = item / kLsePieces, piece = item - i * kLsePieces;
-    const int2 qj = ws.rowA[i];
-    const int q = qj.x, j = qj.y;
-    const int L = clamp_len(ell[q], gamma);
-    const bool bonus = (j == L + 1);
+    const int nxt = item + gridDim.x;
+    const int4 info_next = nxt < nitems ? ws.rowA[nxt / tiles] : info;
+    const int tile = item % tiles;
+    const int q = info.x, j = info.y;
+    const bool bonus = info.z != 0;
     const T* row = target + ((size_t)q * (gamma + 1) + (j - 1)) * V;
-    // whole 64-id blocks per piece: chunks [c0, c1)
-    const int c0 = (int)(((long long)piece * nblocks) / kLsePieces) * 8;
-    const int c1 = min(nch, (int)(((long long)(piece + 1) * nblocks) / kLsePieces) * 8);
-    float M = -INFINITY, S = 0.0f, G = -INFINITY;
+    // wave w covers blocks tile*256 + 64w .. + 64 in 8 coalesced rounds: in round c lane l
+    // holds chunk l & 7 of block 8c + l/8.  One reference serves the whole window (its
+    // largest logit), so the row needs no per-block max; on the bonus row the block sums
+    // are 8-lane reductions on the DPP network.
+    constexpr float kLog2e = 1.4426950408889634f;
+    constexpr float kLn2 = 0.69314718055994531f;
+    const int bw = tile * kLseThreads + wave * kWave;  // first block of this wave
+    float xa[8][8];  // all eight rounds' loads go out together
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int v = (bw + 8 * c + (lane >> 3)) * kVB + 8 * (lane & 7);
+      if (v < V) {  // V % 8 == 0: whole chunks
+        ld8<T>(row + v, xa[c]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xa[c][e] = -INFINITY;
+      }
+    }
+    float mx = xa[0][0];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int e = (c == 0 ? 1 : 0); e < 8; ++e) mx = fmaxf(mx, xa[c][e]);
+    mx = wave_max(mx);
+    const float ref = mx == -INFINITY ? 0.0f : mx * kLog2e;
+    // random words of the window's 16 block groups: lane l < 16 holds group bw/4 + l
+    uint4 wds = make_uint4(0, 0, 0, 0);
+    if (bonus)
+      wds = rng.block(kStreamBonusBlk, (uint32_t)q, (uint32_t)j, (uint32_t)((bw >> 2) + (lane & 15)));
+    float S = 0.0f, G = -INFINITY;
     int Bk = 0x7fffffff;
-    for (int base = c0; base < c1; base += kLseThreads * kLseUnroll) {
-      float x[kLseUnroll][8];
 #pragma unroll
-      for (int u = 0; u < kLseUnroll; ++u) {
-        const int ci = base + u * kLseThreads + threadIdx.x;
-        if (ci < c1) {
-          ld8<T>(row + (size_t)ci * 8, x[u]);
-        } else {
+    for (int c = 0; c < 8; ++c) {
+      float sb = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[u][e] = -INFINITY;
+      for (int e = 0; e < 8; ++e) sb += __builtin_amdgcn_exp2f(fmaf(xa[c][e], kLog2e, -ref));
+      S += sb;
+      if (bonus) {
+        const float bs = sum8(sb);
+        const int m = lane >> 3, b = bw + 8 * c + m;
+        const int src = 2 * c + (m >> 2);  // lane holding group b / 4
+        const uint4 gw = make_uint4(__shfl(wds.x, src, kWave), __shfl(wds.y, src, kWave),
+                                    __shfl(wds.z, src, kWave), __shfl(wds.w, src, kWave));
+        const bool lead = (lane & 7) == 0 && b < nblocks && bs > 0.0f;
+        const float Gb = lead ? (ref + __builtin_amdgcn_logf(bs)) * kLn2 + gumbel_of(pick_word(gw, (uint32_t)b & 3u))
+                              : -INFINITY;
+        if (Gb > G) {  // blocks visited in increasing order per lane
+          G = Gb;
+          Bk = b;
         }
       }
-#pragma unroll
-      for (int u = 0; u < kLseUnroll; ++u) {
-        float m = x[u][0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) m = fmaxf(m, x[u][e]);
-        const float ref = m == -INFINITY ? 0.0f : m;
-        float s = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s += __expf(x[u][e] - ref);
-        if (bonus) {
-          // one 64-id block = 8 consecutive threads
-          float bm = m, bs = s;
-#pragma unroll
-          for (int o = 1; o < 8; o <<= 1) {
-            const float m2 = __shfl_xor(bm, o, kWave), s2 = __shfl_xor(bs, o, kWave);
-            lse_merge(bm, bs, m2, s2);
-          }
-          const int ci = base + u * kLseThreads + threadIdx.x;
-          const int b = ci >> 3;
-          if ((threadIdx.x & 7) == 0 && ci < c1) {
-            const float g = gumbel_of(rng.word(kStreamBonusBlk, (uint32_t)q, (uint32_t)j, (uint32_t)b));
-            const float Gb = bm + __logf(bs) + g;
-            if (Gb > G) {  // blocks visited in increasing order per thread
-              G = Gb;
-              Bk = b;
-            }
-          }
-        }
-        lse_merge(M, S, m, s);
-      }
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
-      lse_merge(M, S, m2, s2);
-    }
+    S = wave_sum(S);
+    float M = mx == -INFINITY ? -INFINITY : ref * kLn2;
     wave_argmax(G, Bk);
     if (lane == 0) red[wave] = make_float4(M, S, G, __int_as_float(Bk));
     __syncthreads();
@@ -200,6 +221,7 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
       ws.lpart[item] = make_float4(M, S, G, __int_as_float(Bk));
     }
     __syncthreads();  // red is reused by the next item
+    info = info_next;
   }
 }
 
@@ -207,22 +229,24 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
 // decide: acceptance tests in order
 // ---------------------------------------------------------------------------------------
 template <class T>
-__global__ void __launch_bounds__(256) verify_decide_kernel(
+__global__ void __launch_bounds__(64) verify_decide_kernel(
     int R, int gamma, int V, const T* __restrict__ target, const int32_t* __restrict__ x,
     const float* __restrict__ lse, const float* __restrict__ logit_x, const int32_t* ell,
     VerifyWs ws, uint64_t seed, uint64_t cycle, int32_t* n_acc, int32_t* y, int32_t* status) {
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  if (q >= R) return;
+  // one wave per request; lane j - 1 tests position j (gamma <= 64)
+  const int q = blockIdx.x, lane = threadIdx.x, j = lane + 1;
   const int L = clamp_len(ell[q], gamma);
-  // target normalisers of rows 1..L+1 and the bonus block, from the lse pieces (in piece
-  // order, so ties keep the lowest block)
-  for (int j = 1; j <= L + 1; ++j) {
-    const int i = ws.offA[q] + j - 1;
+  // target normaliser of rows 1..L+1 from their lse items (in item order, so ties keep the
+  // lowest block); the bonus row's winning block
+  const int tiles = lse_tiles(V);
+  float lset_j = 0.0f;
+  for (int jj = j; jj <= L + 1; jj += kWave) {
+    const int i = ws.offA[q] + jj - 1;
     float M = -INFINITY, S = 0.0f, G = -INFINITY;
     int Bk = 0x7fffffff;
-#pragma unroll
-    for (int pc = 0; pc < kLsePieces; ++pc) {
-      const float4 o = ws.lpart[(size_t)i * kLsePieces + pc];
+#pragma unroll 4
+    for (int pc = 0; pc < tiles; ++pc) {
+      const float4 o = ws.lpart[(size_t)i * tiles + pc];
       lse_merge(M, S, o.x, o.y);
       const int ob = __float_as_int(o.w);
       if (o.z > G || (o.z == G && ob < Bk)) {
@@ -230,30 +254,38 @@ __global__ void __launch_bounds__(256) verify_decide_kernel(
         Bk = ob;
       }
     }
-    ws.lset[i] = M + __logf(S);
-    if (j == L + 1) ws.bonus[q] = make_float2(G, __int_as_float(Bk));
+    const float ls = M + __logf(S);
+    ws.lset[i] = ls;
+    if (jj == j) lset_j = ls;
+    if (jj == L + 1) ws.bonus[q] = make_float2(G, __int_as_float(Bk));
   }
   const Rng rng(seed, cycle);
-  int js = 0;
-  for (int j = 1; j <= L; ++j) {
+  bool reject = false, bad = false;
+  int xj = 0;
+  if (j <= L) {
     const size_t rj = (size_t)q * gamma + (j - 1);
-    const int xj = checked_token(x[rj], V, status);
-    const float t = ld<T>(target, ((size_t)q * (gamma + 1) + (j - 1)) * V + xj);
-    const float lp = t - ws.lset[ws.offA[q] + j - 1];  // log p_j(x_j)
-    const float lq = logit_x[rj] - lse[rj];             // log q_j(x_j)
+    const int32_t t = x[rj];
+    bad = t < 0 || t >= V;
+    xj = bad ? 0 : t;
+    const float tv = ld<T>(target, ((size_t)q * (gamma + 1) + (j - 1)) * V + xj);
+    const float lp = tv - lset_j;                          // log p_j(x_j)
+    const float lq = logit_x[rj] - lse[rj];              // log q_j(x_j)
     const float ratio = __expf(lp - lq);
     const float u = uniform_of(rng.word(kStreamAccept, (uint32_t)q, (uint32_t)j, 0u));
-    if (!(u < ratio)) {
-      js = j;
-      break;
-    }
+    reject = !(u < ratio);
   }
-  ws.jstar[q] = js;
+  // the tests run in order: the first rejection ends them
+  const unsigned long long rm = __ballot(reject);
+  const int js = rm ? __ffsll(rm) : 0;
   const int na = js ? js - 1 : L;
-  n_acc[q] = na;
+  if (bad && j <= (js ? js : L)) raise_fault(status, DSPARK_FAULT_TOKEN);
+  if (lane == 0) {
+    ws.jstar[q] = js;
+    n_acc[q] = na;
+  }
   int32_t* yq = y + (size_t)q * (gamma + 1);
-  for (int j = 0; j < na; ++j) yq[j] = checked_token(x[(size_t)q * gamma + j], V, status);
-  for (int j = na; j <= gamma; ++j) yq[j] = -1;
+  if (lane <= gamma) yq[lane] = lane < na ? xj : -1;  // lane j - 1 holds x_j
+  if (gamma == kWave && lane == 0) yq[kWave] = -1;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -444,54 +476,126 @@ __device__ int sample_row_wave(const T* row, int V, const Rng& rng, uint32_t sbl
 // ---------------------------------------------------------------------------------------
 // final: c* of every verified row, then the correction or the bonus token
 // ---------------------------------------------------------------------------------------
+constexpr int kFinalThreads = 256;  // per request in the final step
+
 template <class T, class BT>
-__global__ void __launch_bounds__(64) verify_final_kernel(
+__global__ void __launch_bounds__(kFinalThreads) verify_final_kernel(
     int R, int gamma, int V, int r, const T* __restrict__ target, const T* __restrict__ U,
     const T* __restrict__ W2t, const BT* __restrict__ brows, const float* __restrict__ lse,
     const int32_t* ell, VerifyWs ws, int nranges, uint64_t seed, uint64_t cycle,
     const int32_t* n_acc, int32_t* y, float* c_star) {
-  const int q = blockIdx.x, lane = threadIdx.x;
+  constexpr int kWaves = kFinalThreads / kWave;
+  constexpr int kJ = 8;  // verified rows whose range sums are in flight together
+  __shared__ float tvs[kWaves][kJ];
+  __shared__ float4 red[kWaves];
+  __shared__ float dotp[kWaves][kWave];
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = clamp_len(ell[q], gamma);
-  for (int j = 1; j <= gamma; ++j) {
-    float cs = __int_as_float(0x7fc00000);  // NaN past the scheduled length
-    if (j <= L) {
-      const size_t row = (size_t)ws.offB[q] + j - 1;
-      float s = 0.0f;
-      for (int i = lane; i < nranges; i += 64) s += ws.partials[row * nranges + i].x;
-      s = wave_sum(s);
-      cs = 1.0f - 0.5f * s;
-    }
-    if (lane == 0) c_star[(size_t)q * gamma + (j - 1)] = cs;
-  }
-  const Rng rng(seed, cycle);
+  const int nblocks = (V + kVB - 1) / kVB;
   const int js = ws.jstar[q];
-  int token;
+  const size_t offB = (size_t)ws.offB[q];
+
+  // c* = 1 - 1/2 sum |p - q| for every verified row (eq. (8)); NaN past the scheduled length
+  for (int j0 = 1; j0 <= gamma; j0 += kJ) {
+    float sum[kJ];
+#pragma unroll
+    for (int u = 0; u < kJ; ++u) {
+      sum[u] = 0.0f;
+      if (j0 + u <= L)
+        for (int i = tid; i < nranges; i += kFinalThreads)
+          sum[u] += ws.partials[(offB + j0 + u - 1) * nranges + i].x;
+    }
+#pragma unroll
+    for (int u = 0; u < kJ; ++u) {
+      const float t = wave_sum(sum[u]);
+      if (lane == 0) tvs[wave][u] = t;
+    }
+    __syncthreads();
+    if (tid < kJ && j0 + tid <= gamma) {
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) t += tvs[w][tid];
+      c_star[(size_t)q * gamma + (j0 + tid - 1)] =
+          (j0 + tid <= L) ? 1.0f - 0.5f * t : __int_as_float(0x7fc00000);
+    }
+    __syncthreads();
+  }
+
+  const Rng rng(seed, cycle);
+  // the block the token is drawn from: the residual's winning block at the first rejected
+  // row, or the bonus row's
+  int Bk;
+  float mass = 1.0f;
   if (js > 0) {
-    const size_t row = (size_t)ws.offB[q] + js - 1;
-    float G = -INFINITY, mass = 0.0f;
-    int Bk = 0x7fffffff;
-    for (int i = lane; i < nranges; i += 64) {
+    const size_t row = offB + js - 1;
+    float G = -INFINITY, m = 0.0f;
+    int B = 0x7fffffff;
+    for (int i = tid; i < nranges; i += kFinalThreads) {
       const float4 pr = ws.partials[row * nranges + i];
       const int pb = __float_as_int(pr.z);
-      mass += pr.w;
-      if (pr.y > G || (pr.y == G && pb < Bk)) {
+      m += pr.w;
+      if (pr.y > G || (pr.y == G && pb < B)) {
         G = pr.y;
-        Bk = pb;
+        B = pb;
       }
     }
-    mass = wave_sum(mass);
-    wave_argmax(G, Bk);
+    m = wave_sum(m);
+    wave_argmax(G, B);
+    if (lane == 0) red[wave] = make_float4(G, m, __int_as_float(B), 0.0f);
+    __syncthreads();
+    G = red[0].x;
+    m = red[0].y;
+    B = __float_as_int(red[0].z);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const float4 o = red[w];
+      m += o.y;
+      const int ob = __float_as_int(o.z);
+      if (o.x > G || (o.x == G && ob < B)) {
+        G = o.x;
+        B = ob;
+      }
+    }
+    mass = m;
+    Bk = B;
+  } else {
+    Bk = __float_as_int(ws.bonus[q].y);
+  }
+  const bool resid_ok = js > 0 && mass > 0.0f && Bk >= 0 && Bk < nblocks;
+  if (Bk < 0 || Bk >= nblocks) Bk = 0;
+  const int jrow = js > 0 ? js : L + 1;  // target row of the draw
+  const T* trow = target + ((size_t)q * (gamma + 1) + (jrow - 1)) * V;
+  const int v = Bk * kVB + lane;
+
+  // residual: q over the winning block, the k sum split over the waves in 8-element chunks
+  if (resid_ok) {
     const size_t rj = (size_t)q * gamma + (js - 1);
-    const T* trow = target + ((size_t)q * (gamma + 1) + (js - 1)) * V;
-    const int nblocks = (V + kVB - 1) / kVB;
-    if (mass > 0.0f && Bk >= 0 && Bk < nblocks) {
+    float part = 0.0f;
+    if (v < V) {
+      const BT* e = brows + rj * r;
+      const T* wr = W2t + (size_t)v * r;
+      for (int ch = wave; ch < r / 8; ch += kWaves) {
+        float a[8], bv[8];
+        ld8<T>(wr + ch * 8, a);
+        ld8<BT>(e + ch * 8, bv);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) part = fmaf(bv[jj], a[jj], part);
+      }
+    }
+    dotp[wave][lane] = part;
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  int token;
+  if (js > 0) {
+    if (resid_ok) {
+      const size_t rj = (size_t)q * gamma + (js - 1);
       const float lq = lse[rj], lp = ws.lset[ws.offA[q] + js - 1];
-      const int v = Bk * kVB + lane;
       float score = -INFINITY;
       if (v < V) {
         float acc = 0.0f;
-        const BT* e = brows + rj * r;
-        for (int i = 0; i < r; ++i) acc = fmaf(ld<BT>(e, i), ld<T>(W2t, (size_t)v * r + i), acc);
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) acc += dotp[w][lane];
         const float qv = __expf(ld<T>(U, rj * V + v) + acc - lq);
         const float pv = __expf(ld<T>(trow, v) - lp);
         const float rho = pv - qv;
@@ -502,17 +606,13 @@ __global__ void __launch_bounds__(64) verify_final_kernel(
       wave_argmax(score, idx);
       token = idx;
     } else {
+      // the residual mass is zero in floating point: draw from the target row instead
       token = sample_row_wave<T>(trow, V, rng, kStreamResidBlk, kStreamResidIn, (uint32_t)q,
                                  (uint32_t)js);
     }
   } else {
-    const int j = L + 1;
-    const T* trow = target + ((size_t)q * (gamma + 1) + L) * V;
-    const int nblocks = (V + kVB - 1) / kVB;
-    int Bk = __float_as_int(ws.bonus[q].y);
-    if (Bk < 0 || Bk >= nblocks) Bk = 0;
-    const int v = Bk * kVB + lane;
-    float score = v < V ? ld<T>(trow, v) + gumbel_of(rng.word(kStreamBonusIn, (uint32_t)q, (uint32_t)j, (uint32_t)v))
+    float score = v < V ? ld<T>(trow, v) + gumbel_of(rng.word(kStreamBonusIn, (uint32_t)q,
+                                                               (uint32_t)jrow, (uint32_t)v))
                         : -INFINITY;
     int idx = v;
     wave_argmax(score, idx);
@@ -539,12 +639,12 @@ static int verify_run(int R, int gamma, int V, int r, const void* target_, const
 
   verify_prep_kernel<<<1, 1024, 0, stream>>>(R, gamma, ell, ws, status);
   {
-    // persistent grid over the pieces of list A (its length is known on the device only)
-    const int items = R * (gamma + 1) * kLsePieces, cap = 8 * device_cus();
+    // persistent grid over the items of list A (its length is known on the device only)
+    const int items = R * (gamma + 1) * lse_tiles(V), cap = 6 * device_cus();
     verify_lse_kernel<T><<<items < cap ? items : cap, kLseThreads, 0, stream>>>(
         R, gamma, V, target, ell, ws, seed, cycle);
   }
-  verify_decide_kernel<T><<<(R + 255) / 256, 256, 0, stream>>>(
+  verify_decide_kernel<T><<<R, 64, 0, stream>>>(
       R, gamma, V, target, x, lse, logit_x, ell, ws, seed, cycle, n_acc, y, status);
 
   const int rows_max = R * gamma;
@@ -578,7 +678,7 @@ static int verify_run(int R, int gamma, int V, int r, const void* target_, const
         reinterpret_cast<const float*>(W2t), reinterpret_cast<const float*>(brows), lse, ws,
         seed, cycle, nranges, nblocks);
   }
-  verify_final_kernel<T, BT><<<R, 64, 0, stream>>>(R, gamma, V, r, target, U, W2t, brows, lse,
+  verify_final_kernel<T, BT><<<R, kFinalThreads, 0, stream>>>(R, gamma, V, r, target, U, W2t, brows, lse,
                                                     ell, ws, nranges, seed, cycle, n_acc, y, c_star);
   return launch_status();
 }
