@@ -1,22 +1,23 @@
 // sweep.h -- the vocabulary sweep shared by the draft step and verification.
 //
-// For a group of up to 256 rows (requests at one draft position, or verified positions)
+// For a group of up to 128 rows (requests at one draft position, or verified positions)
 // and a contiguous range of 64-id vocabulary blocks, it forms
 //     l(row, v) = sum_i B[row][i] * W2t[v][i] + stream_0[row][v]   (eq. (4) with eq. (5))
-// on the matrix cores, 32 ids at a time, and hands each 32 x 256 tile of fp32 logits to an
+// on the matrix cores, 32 ids at a time, and hands each 32 x 128 tile of fp32 logits to an
 // epilogue that folds it into per-row running state (normalisers, Gumbel maxima,
 // distances), so no V-wide row is ever written to memory.
 //
-// Work split: one workgroup of 8 waves per vocabulary range (grid = ranges, about one per
-// CU); the workgroup walks the row groups of 256 in order, so a row count known only on the
-// device costs no idle workgroups.
+// Work split: workgroups of 4 waves, two per vocabulary range (grid = 2 x ranges, about two
+// per CU, each with its own barrier domain so one's waits overlap the other's work); the
+// workgroups of a range walk the row groups of 128 alternately, so a row count known only
+// on the device costs no idle workgroups.
 //   - Each wave owns 32 rows of the group; their B rows (K = r) live in registers for the
 //     group's whole sweep.
 //   - Per 32-id tile the workgroup stages in LDS the tile's W2t rows (32 x r bf16, shared by
 //     all waves) and every wave's 32 x 32 slice of each streamed operand (U, and the target
 //     logits in verification).  Staging is asynchronous: the loads go straight to LDS
-//     (global_load_lds_dwordx4), up to four stages deep as LDS allows, so each tile's HBM
-//     traffic is issued up to three tiles ahead of its use and the matrix-core and
+//     (global_load_lds_dwordx4), three stages deep when two workgroups still fit a CU, so
+//     each tile's HBM traffic is issued two tiles ahead of its use and the matrix-core and
 //     epilogue work of the current tile hides the memory latency.  The waits on those
 //     loads are explicit vmcnt waits.
 //   - MFMA 32x32x16 bf16 with A = W2t tile (vocabulary on M) and B = B^T (rows on N):
@@ -29,7 +30,7 @@
 
 namespace dspark {
 
-constexpr int kSweepThreads = 512;  // 8 waves; each wave owns 32 rows of the group
+constexpr int kSweepThreads = 256;  // 4 waves; each wave owns 32 rows of the group
 constexpr int kSweepWaves = kSweepThreads / kWave;
 constexpr int kRowsPerGroup = kSweepWaves * 32;
 constexpr int kTile = 32;           // vocabulary ids per pipeline step (one m-tile)
@@ -42,6 +43,7 @@ struct SweepGeom {
   int nblocks;    // ceil(V / 64)
   int nranges;    // vocabulary ranges (one per task column)
   int ngroups;    // row groups
+  int gsplit;     // workgroups per vocabulary range; each takes every gsplit-th row group
   int blocks_lo;  // range i spans blocks_lo + (i < blocks_extra) blocks
   int blocks_extra;
   const uint16_t* W2t;  // [V][r] bf16
@@ -52,7 +54,7 @@ struct SweepGeom {
 //   [W2t tile: 32 rows, row stride CH + 1 (the odd stride puts the 16 rows one
 //    ds_read_b128 phase reads on distinct banks, so every fragment address is a per-lane
 //    base plus an immediate); rounded up to whole 64-chunk copies]
-//   [stream s: 8 waves x 32 rows x 4 chunks] for each streamed operand
+//   [stream s: 4 waves x 32 rows x 4 chunks] for each streamed operand
 // ---------------------------------------------------------------------------------------
 __host__ __device__ constexpr int w2_copies(int CH) { return (32 * (CH + 1) + 63) / 64; }
 __host__ __device__ constexpr int w2_tile_chunks(int CH) { return 64 * w2_copies(CH); }
@@ -161,7 +163,7 @@ __device__ __forceinline__ void half_lse(float& m, float& s) {
   lse_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
 }
 
-// The sweep kernel.  Lane (n, h) of wave w works on row = group*256 + 32w + n; the lanes
+// The sweep kernel.  Lane (n, h) of wave w works on row = group*128 + 32w + n; the lanes
 // with h == 0 own the row's running state.  Epi provides:
 //   static constexpr int kStreams;       streamed operands: 1 (U) or 2 (U, target)
 //   struct Params; struct State;
@@ -183,7 +185,7 @@ __device__ __forceinline__ void half_lse(float& m, float& s) {
 // SPLIT: B rows are float and enter as hi + lo bf16 terms (two MFMAs each).
 // Host guarantees: every stream array is smaller than 4 GiB (32-bit byte offsets).
 template <int NKS, bool SPLIT, int NSTAGE, class Epi>
-__global__ void __launch_bounds__(kSweepThreads, 1)
+__global__ void __launch_bounds__(kSweepThreads, 2)
     sweep_kernel(SweepGeom g, typename Epi::Params ep) {
   constexpr int CH = 2 * NKS;
   constexpr int RS = CH + 1;                 // W2t tile row stride (chunks)
@@ -194,12 +196,26 @@ __global__ void __launch_bounds__(kSweepThreads, 1)
   constexpr int D = NSTAGE - 1;              // prefetch distance in tiles
   extern __shared__ uint4 lds[];
 
-  const int range = blockIdx.x;
+  // task -> (vocabulary range, first row group); the gsplit workgroups of one range are
+  // dispatched to the same XCD (round-robin dispatch over 8 XCDs) so its W2t tiles come
+  // from HBM once and from that XCD's L2 after
+  int range, g0;
+  {
+    const int bid = blockIdx.x, G = g.gsplit;
+    if ((g.nranges & 7) == 0) {
+      const int slot = bid >> 3;
+      range = (slot / G) * 8 + (bid & 7);
+      g0 = slot - (slot / G) * G;
+    } else {
+      range = bid / G;
+      g0 = bid - range * G;
+    }
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h = lane >> 5;
   const int nrows = Epi::nrows(ep);
-  for (int group = 0; Epi::group_live(ep, group * kRowsPerGroup); ++group) {
+  for (int group = g0; Epi::group_live(ep, group * kRowsPerGroup); group += g.gsplit) {
     // values derived from the group are recomputed per group rather than hoisted out of
     // the group loop and held (the scalar register file is the tight resource here)
     int group_row0 = group * kRowsPerGroup;
@@ -328,11 +344,10 @@ __global__ void __launch_bounds__(kSweepThreads, 1)
     const int bp1 = ragged ? b1 - 1 : b1;  // pipelined blocks [b0, bp1)
     const int t0 = 2 * b0, t1 = 2 * bp1;
 
-    // the first tiles go out before anything else: they depend on nothing the B rows or
-    // the epilogue state need
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-      if (t0 + d < t1) issue(t0 + d, d);
+    // the first tile goes out before anything else (it depends on nothing the B rows or
+    // the epilogue state need); the rest of the pipeline fills once they are in, so the
+    // first step waits for one tile rather than D
+    if (t0 < t1) issue(t0, 0);
 
     // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row
     const void* brow = live ? Epi::brow(ep, row) : nullptr;
@@ -356,32 +371,51 @@ __global__ void __launch_bounds__(kSweepThreads, 1)
     }
     Epi::init(ep, st, live ? row : -1);
 
-    // a wait the compiler sees: every load issued so far (first tiles, B rows, epilogue
+    // a wait the compiler sees: every load issued so far (first tile, B rows, epilogue
     // state) has landed, so none of them is pending at the loop header
     __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int d = 1; d < D; ++d)
+      if (t0 + d < t1) issue(t0 + d, d);
     f32x16 accA, accB;
     uint4 xA[2], xB[2];
     xA[0] = xA[1] = xB[0] = xB[1] = make_uint4(0, 0, 0, 0);
     int stg = 0;
     // one pipeline step: tile t's copies are awaited, tile t+D's issued, tile t's matrix
-    // chain runs, and the epilogue of tile t-1 (HALF = 1 - half of t) overlaps it
-    for (int t = t0; t < t1; t += 2) {
+    // chain runs, and the epilogue of tile t-1 (HALF = 1 - half of t) is interleaved with it
+    // (the first pair has no previous tile and is peeled off)
+    auto next_stage = [&](int sg) { return sg + 1 == NSTAGE ? 0 : sg + 1; };
+    auto ahead = [&](int sg) { return sg + D >= NSTAGE ? sg + D - NSTAGE : sg + D; };
+    if (t1 > t0) {
+      wait_tiles(min(D - 1, t1 - 1 - t0));
+      stage_barrier();
+      if (t0 + D < t1) issue(t0 + D, ahead(stg));
+      mma(stg, accA, xA);
+      stg = next_stage(stg);
+      wait_tiles(min(D - 1, t1 - 2 - t0));
+      stage_barrier();
+      if (t0 + 1 + D < t1) issue(t0 + 1 + D, ahead(stg));
+      mma(stg, accB, xB);
+      Epi::template tile<0, false>(ep, st, accA, xA, t0 >> 1, row, owner);
+      stg = next_stage(stg);
+    }
+    for (int t = t0 + 2; t < t1; t += 2) {
       const int b = t >> 1;
+      Epi::refresh(ep, st, b - 1, row);
       // -- tile t = 2b (half 0); epilogue of tile 2b-1 (half 1 of block b-1)
       wait_tiles(min(D - 1, t1 - 1 - t));
       stage_barrier();
-      if (t + D < t1) issue(t + D, stg + D >= NSTAGE ? stg + D - NSTAGE : stg + D);
-      if (t > t0) Epi::refresh(ep, st, b - 1, row);
+      if (t + D < t1) issue(t + D, ahead(stg));
       mma(stg, accA, xA);
-      if (t > t0) Epi::template tile<1, false>(ep, st, accB, xB, b - 1, row, owner);
-      stg = stg + 1 == NSTAGE ? 0 : stg + 1;
+      Epi::template tile<1, false>(ep, st, accB, xB, b - 1, row, owner);
+      stg = next_stage(stg);
       // -- tile t + 1 (half 1); epilogue of tile t (half 0 of block b)
       wait_tiles(min(D - 1, t1 - 2 - t));
       stage_barrier();
-      if (t + 1 + D < t1) issue(t + 1 + D, stg + D >= NSTAGE ? stg + D - NSTAGE : stg + D);
+      if (t + 1 + D < t1) issue(t + 1 + D, ahead(stg));
       mma(stg, accB, xB);
       Epi::template tile<0, false>(ep, st, accA, xA, b, row, owner);
-      stg = stg + 1 == NSTAGE ? 0 : stg + 1;
+      stg = next_stage(stg);
     }
     if (t1 > t0) {
       Epi::refresh(ep, st, bp1 - 1, row);
@@ -407,7 +441,7 @@ __global__ void __launch_bounds__(kSweepThreads, 1)
   }
 }
 
-// host-side geometry: target_ranges vocabulary ranges (the grid), row groups of 256
+// host-side geometry: target_ranges vocabulary ranges, row groups of 128
 inline SweepGeom make_geom(int nrows, int V, int r, const uint16_t* W2t, int target_ranges) {
   SweepGeom g{};
   g.nrows = nrows;
@@ -422,6 +456,7 @@ inline SweepGeom make_geom(int nrows, int V, int r, const uint16_t* W2t, int tar
   if (nr < 1) nr = 1;
   if (nr > g.nblocks) nr = g.nblocks;
   g.nranges = nr;
+  g.gsplit = g.ngroups >= 2 ? 2 : 1;
   g.blocks_lo = g.nblocks / nr;
   g.blocks_extra = g.nblocks - g.blocks_lo * nr;
   g.W2t = W2t;
@@ -453,17 +488,14 @@ inline void launch_sweep_nks(const SweepGeom& g, const typename Epi::Params& p, 
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
     attr = true;
   }
-  kern<<<g.nranges, kSweepThreads, sh, s>>>(g, p);
+  kern<<<g.nranges * g.gsplit, kSweepThreads, sh, s>>>(g, p);
 }
 
-// launch with NKS = r / 16 fixed at compile time (r in {16, 32, 64, 128, 256}) and as many
-// pipeline stages (2 to 4) as the device's LDS allows
+// launch with NKS = r / 16 fixed at compile time (r in {16, 32, 64, 128, 256}) and three
+// pipeline stages when two workgroups still fit one CU's LDS, else two
 template <int NKS, bool SPLIT, class Epi>
 inline void launch_sweep_stages(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s) {
-  const size_t lds = device_max_lds();
-  if (sweep_lds_bytes(g.r, Epi::kStreams, 4) <= lds)
-    launch_sweep_nks<NKS, SPLIT, 4, Epi>(g, p, s);
-  else if (sweep_lds_bytes(g.r, Epi::kStreams, 3) <= lds)
+  if (2 * sweep_lds_bytes(g.r, Epi::kStreams, 3) <= device_max_lds())
     launch_sweep_nks<NKS, SPLIT, 3, Epi>(g, p, s);
   else
     launch_sweep_nks<NKS, SPLIT, 2, Epi>(g, p, s);
