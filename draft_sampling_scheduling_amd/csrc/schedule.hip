@@ -34,11 +34,29 @@ __device__ __forceinline__ unsigned long long incr_of_key(unsigned long long key
   return (unsigned long long)((double)a * 4294967296.0);
 }
 
-// steps 1-3 for one batch of confidences; returns the candidate count |E|
+// smallest power of two >= x (x >= 1)
+__device__ __forceinline__ int pow2_ceil(int x) { return x <= 1 ? 1 : 1 << (32 - __clz(x - 1)); }
+
+// steps 1-3 for one batch of confidences; returns the candidate count |E|.  *npad_io is the
+// sorted length on entry (bitonic layout) and on return (the layout actually used).
+//
+// Each request's keys already ascend (a falls along j, ties keep j order), so when the
+// padded layout fits, the order is R runs merged pairwise: round r merges runs of length
+// P * 2^r, every key finding its place by one binary search in the partner run (keys are
+// unique; the even run counts partner keys below it, the odd run those not above it, which
+// also keeps the padding keys of the two runs apart).  Otherwise a bitonic sort.
 __device__ int sched_sort_scan(int R, int gamma, const float* __restrict__ c, float* a_out,
-                               int npad, SchedShared sh, unsigned long long* red_u64,
+                               int* npad_io, SchedShared sh, unsigned long long* red_u64,
                                int* red_i, int32_t* status) {
-  const int N = R * gamma;
+  (void)(R * gamma);
+  const int P = pow2_ceil(gamma), Rp = pow2_ceil(R);
+  const bool merge = (long)Rp * P <= *npad_io;  // both buffers hold *npad_io keys
+  const int npad = merge ? Rp * P : *npad_io;
+  *npad_io = npad;
+  // merge layout: request q's run at [q * P, q * P + P) of the source buffer (sh.pre)
+  unsigned long long* src = merge ? sh.pre : sh.key;
+  for (int i = threadIdx.x; i < npad; i += kSchedThreads) src[i] = ~0ull;
+  __syncthreads();
   for (int q = threadIdx.x; q < R; q += kSchedThreads) {
     float run = 1.0f;
     for (int j = 0; j < gamma; ++j) {
@@ -50,16 +68,50 @@ __device__ int sched_sort_scan(int R, int gamma, const float* __restrict__ c, fl
       run = (j == 0) ? cj : __fmul_rn(run, cj);
       const int idx = q * gamma + j;
       if (a_out) a_out[idx] = run;
-      sh.key[idx] = (run > 0.0f)
-                        ? (((unsigned long long)(~__float_as_uint(run)) << 32) | (unsigned)idx)
-                        : ~0ull;
+      src[merge ? q * P + j : idx] =
+          (run > 0.0f) ? (((unsigned long long)(~__float_as_uint(run)) << 32) | (unsigned)idx)
+                       : ~0ull;
     }
   }
-  for (int i = N + threadIdx.x; i < npad; i += kSchedThreads) sh.key[i] = ~0ull;
   __syncthreads();
 
-  // bitonic sort, ascending
-  for (int k = 2; k <= npad; k <<= 1) {
+  if (merge) {
+    unsigned long long* in = sh.pre;
+    unsigned long long* out = sh.key;
+    for (int L = P; L < npad; L <<= 1) {
+      for (int i = threadIdx.x; i < npad; i += kSchedThreads) {
+        const unsigned long long k = in[i];
+        const int run0 = i & ~(2 * L - 1);  // first run of the pair
+        const bool odd = (i & L) != 0;
+        const int pos = i & (L - 1);
+        const unsigned long long* other = in + run0 + (odd ? 0 : L);
+        // number of partner keys below k (even run) or not above k (odd run)
+        int lo = 0, len = L;
+        while (len > 0) {
+          const int half = len >> 1;
+          const unsigned long long o = other[lo + half];
+          if (odd ? (o <= k) : (o < k)) {
+            lo += half + 1;
+            len -= half + 1;
+          } else {
+            len = half;
+          }
+        }
+        out[run0 + pos + lo] = k;
+      }
+      __syncthreads();
+      unsigned long long* t = in;
+      in = out;
+      out = t;
+    }
+    if (in != sh.key) {  // the sorted keys belong in sh.key
+      for (int i = threadIdx.x; i < npad; i += kSchedThreads) sh.key[i] = in[i];
+      __syncthreads();
+    }
+  }
+
+  // bitonic sort, ascending (when the merge layout does not fit)
+  for (int k = 2; !merge && k <= npad; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = threadIdx.x; i < npad; i += kSchedThreads) {
         const int ixj = i ^ j;
@@ -177,14 +229,16 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(
 
   int K = -1;  // admitted-count cap from the lagged batch
   if (mode == DSPARK_SCHED_ASYNC_LAG2) {
-    const int nEl = sched_sort_scan(R_lag, gamma, c_lag, nullptr, npad_lag, sh, red_u64,
+    int np_lag = npad_lag;
+    const int nEl = sched_sort_scan(R_lag, gamma, c_lag, nullptr, &np_lag, sh, red_u64,
                                     &red_one, status);
     const int nl = sched_argmax(R_lag, nEl, sps, sps_B0, sh, red_d, red_i);
     const int cap = R_lag + nl;
     K = cap - R > 0 ? cap - R : 0;
     __syncthreads();
   }
-  const int nE = sched_sort_scan(R, gamma, c, a_out, npad, sh, red_u64, &red_one, status);
+  int np_cur = npad;
+  const int nE = sched_sort_scan(R, gamma, c, a_out, &np_cur, sh, red_u64, &red_one, status);
   int n;
   if (mode == DSPARK_SCHED_SYNC_BREAK)
     n = sched_first_drop(R, nE, sps, sps_B0, sh, &red_one);
