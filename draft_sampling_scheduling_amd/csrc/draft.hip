@@ -260,18 +260,24 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
   float part = 0.0f;
   if (v < V) {
     const T* wr = W2t + (size_t)v * r;
-    for (int ch = wave; ch < r / 8; ch += kWaves) {
-      float a[8], bv[8];
-      ld8<T>(wr + ch * 8, a);
+    // r <= 256: at most 8 chunks per wave, all loads in flight together
+    float a[8][8], bv[8][8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int ch = wave + kWaves * it < r / 8 ? wave + kWaves * it : 0;
+      ld8<T>(wr + ch * 8, a[it]);
       if (RNN) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bv[j] = orow[(size_t)q * r + ch * 8 + j];
+        for (int j = 0; j < 8; ++j) bv[it][j] = orow[(size_t)q * r + ch * 8 + j];
       } else {
-        ld8<T>(e + ch * 8, bv);
+        ld8<T>(e + ch * 8, bv[it]);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) part = fmaf(bv[j], a[j], part);
     }
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+      if (wave + kWaves * it < r / 8)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) part = fmaf(bv[it][j], a[it][j], part);
   }
   dotp[wave][lane] = part;
   // confidence head, embedding part: w_e . W1[x_{k-1}]

@@ -131,49 +131,96 @@ __device__ __forceinline__ float sum8(float x) {
   return x + dpp_f<0x141>(x);
 }
 
+// one wave's eight chunks of a 64-block window, held raw until they are used
+template <class T>
+struct LseRaw;
+template <>
+struct LseRaw<uint16_t> {
+  uint4 c[8];
+  __device__ __forceinline__ void load(const uint16_t* row, const int (&v)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = *reinterpret_cast<const uint4*>(row + v[k]);
+  }
+  __device__ __forceinline__ void widen_one(int k, float (&x)[8]) const { widen8(c[k], x); }
+};
+template <>
+struct LseRaw<float> {
+  float4 c[16];
+  __device__ __forceinline__ void load(const float* row, const int (&v)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      c[2 * k] = *reinterpret_cast<const float4*>(row + v[k]);
+      c[2 * k + 1] = *reinterpret_cast<const float4*>(row + v[k] + 4);
+    }
+  }
+  __device__ __forceinline__ void widen_one(int k, float (&x)[8]) const {
+    const float4 a = c[2 * k], b = c[2 * k + 1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+
 template <class T>
 __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamma, int V,
                                                                  const T* __restrict__ target,
                                                                  const int32_t* ell, VerifyWs ws,
                                                                  uint64_t seed, uint64_t cycle) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kLn2 = 0.69314718055994531f;
   __shared__ float4 red[kLseThreads / kWave];
   const int tiles = lse_tiles(V);
   const int nitems = ws.hdr[0] * tiles;
   const int nblocks = (V + kVB - 1) / kVB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G0 = gridDim.x;
   const Rng rng(seed, cycle);
+  // Wave w of an item covers blocks tile*256 + 64w .. + 64 in 8 coalesced rounds: in round
+  // c lane l holds chunk l & 7 of block 8c + l/8.  One reference serves the whole window
+  // (its largest logit), so the row needs no per-block max; on the bonus row the block sums
+  // are 8-lane reductions on the DPP network.
+  auto offsets = [&](int item, int4 inf, const T*& row, int (&v)[8]) {
+    const int tile = item % tiles;
+    row = target + ((size_t)inf.x * (gamma + 1) + (inf.y - 1)) * V;
+    const int bw = tile * kLseThreads + wave * kWave;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      v[c] = (bw + 8 * c + (lane >> 3)) * kVB + 8 * (lane & 7);
+      v[c] = v[c] < V ? v[c] : V - 8;  // clamped, unconditional loads (V % 8 == 0)
+    }
+  };
+  const int4 dflt = make_int4(0, 1, 0, 0);
   // the row descriptor of the next item is fetched while the current one streams
-  int4 info = blockIdx.x < nitems ? ws.rowA[blockIdx.x / tiles] : make_int4(0, 1, 0, 0);
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int nxt = item + gridDim.x;
-    const int4 info_next = nxt < nitems ? ws.rowA[nxt / tiles] : info;
+  int4 info = blockIdx.x < nitems ? ws.rowA[blockIdx.x / tiles] : dflt;
+  for (int item = blockIdx.x; item < nitems; item += G0) {
+    const int4 info1 = item + G0 < nitems ? ws.rowA[(item + G0) / tiles] : dflt;
+    LseRaw<T> cur;
+    {
+      const T* row;
+      int v[8];
+      offsets(item, info, row, v);
+      cur.load(row, v);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all eight loads go out before their first use
     const int tile = item % tiles;
     const int q = info.x, j = info.y;
     const bool bonus = info.z != 0;
-    const T* row = target + ((size_t)q * (gamma + 1) + (j - 1)) * V;
-    // wave w covers blocks tile*256 + 64w .. + 64 in 8 coalesced rounds: in round c lane l
-    // holds chunk l & 7 of block 8c + l/8.  One reference serves the whole window (its
-    // largest logit), so the row needs no per-block max; on the bonus row the block sums
-    // are 8-lane reductions on the DPP network.
-    constexpr float kLog2e = 1.4426950408889634f;
-    constexpr float kLn2 = 0.69314718055994531f;
     const int bw = tile * kLseThreads + wave * kWave;  // first block of this wave
-    float xa[8][8];  // all eight rounds' loads go out together
+    // chunk c widened on demand (twice: for the max, then for the sums), which keeps the
+    // register footprint at two raw items
+    auto chunk = [&](int c, float (&x)[8]) {
+      cur.widen_one(c, x);
+      const int v = (bw + 8 * c + (lane >> 3)) * kVB + 8 * (lane & 7);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = v < V ? x[e] : -INFINITY;
+    };
+    float mx = -INFINITY;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int v = (bw + 8 * c + (lane >> 3)) * kVB + 8 * (lane & 7);
-      if (v < V) {  // V % 8 == 0: whole chunks
-        ld8<T>(row + v, xa[c]);
-      } else {
+      float x[8];
+      chunk(c, x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xa[c][e] = -INFINITY;
-      }
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[e]);
     }
-    float mx = xa[0][0];
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int e = (c == 0 ? 1 : 0); e < 8; ++e) mx = fmaxf(mx, xa[c][e]);
     mx = wave_max(mx);
     const float ref = mx == -INFINITY ? 0.0f : mx * kLog2e;
     // random words of the window's 16 block groups: lane l < 16 holds group bw/4 + l
@@ -184,9 +231,11 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
     int Bk = 0x7fffffff;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
+      float x[8];
+      chunk(c, x);
       float sb = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sb += __builtin_amdgcn_exp2f(fmaf(xa[c][e], kLog2e, -ref));
+      for (int e = 0; e < 8; ++e) sb += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -ref));
       S += sb;
       if (bonus) {
         const float bs = sum8(sb);
@@ -221,7 +270,7 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
       ws.lpart[item] = make_float4(M, S, G, __int_as_float(Bk));
     }
     __syncthreads();  // red is reused by the next item
-    info = info_next;
+    info = info1;
   }
 }
 
@@ -244,14 +293,20 @@ __global__ void __launch_bounds__(64) verify_decide_kernel(
     const int i = ws.offA[q] + jj - 1;
     float M = -INFINITY, S = 0.0f, G = -INFINITY;
     int Bk = 0x7fffffff;
-#pragma unroll 4
-    for (int pc = 0; pc < tiles; ++pc) {
-      const float4 o = ws.lpart[(size_t)i * tiles + pc];
-      lse_merge(M, S, o.x, o.y);
-      const int ob = __float_as_int(o.w);
-      if (o.z > G || (o.z == G && ob < Bk)) {
-        G = o.z;
-        Bk = ob;
+    for (int pc0 = 0; pc0 < tiles; pc0 += 8) {
+      float4 o[8];  // eight items in flight together (clamped, unconditional loads)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        o[u] = ws.lpart[(size_t)i * tiles + (pc0 + u < tiles ? pc0 + u : tiles - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (pc0 + u >= tiles) break;
+        lse_merge(M, S, o[u].x, o[u].y);
+        const int ob = __float_as_int(o[u].w);
+        if (o[u].z > G || (o[u].z == G && ob < Bk)) {
+          G = o[u].z;
+          Bk = ob;
+        }
       }
     }
     const float ls = M + __logf(S);
@@ -498,12 +553,20 @@ __global__ void __launch_bounds__(kFinalThreads) verify_final_kernel(
   // c* = 1 - 1/2 sum |p - q| for every verified row (eq. (8)); NaN past the scheduled length
   for (int j0 = 1; j0 <= gamma; j0 += kJ) {
     float sum[kJ];
+    // every range of the kJ rows at once (unconditional loads of clamped addresses, so
+    // they are all in flight together)
 #pragma unroll
-    for (int u = 0; u < kJ; ++u) {
-      sum[u] = 0.0f;
-      if (j0 + u <= L)
-        for (int i = tid; i < nranges; i += kFinalThreads)
-          sum[u] += ws.partials[(offB + j0 + u - 1) * nranges + i].x;
+    for (int u = 0; u < kJ; ++u) sum[u] = 0.0f;
+    for (int i0 = 0; i0 < nranges; i0 += kFinalThreads) {
+      const int i = i0 + tid;
+      float v[kJ];
+#pragma unroll
+      for (int u = 0; u < kJ; ++u) {
+        const int jj = j0 + u <= L ? j0 + u : 1;
+        v[u] = ws.partials[(offB + jj - 1) * nranges + (i < nranges ? i : 0)].x;
+      }
+#pragma unroll
+      for (int u = 0; u < kJ; ++u) sum[u] += (j0 + u <= L && i < nranges) ? v[u] : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < kJ; ++u) {
@@ -574,13 +637,19 @@ __global__ void __launch_bounds__(kFinalThreads) verify_final_kernel(
     if (v < V) {
       const BT* e = brows + rj * r;
       const T* wr = W2t + (size_t)v * r;
-      for (int ch = wave; ch < r / 8; ch += kWaves) {
-        float a[8], bv[8];
-        ld8<T>(wr + ch * 8, a);
-        ld8<BT>(e + ch * 8, bv);
+      // r <= 256: at most 8 chunks per wave, all loads in flight together
+      float a[8][8], bv[8][8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) part = fmaf(bv[jj], a[jj], part);
+      for (int it = 0; it < 8; ++it) {
+        const int ch = wave + kWaves * it < r / 8 ? wave + kWaves * it : 0;
+        ld8<T>(wr + ch * 8, a[it]);
+        ld8<BT>(e + ch * 8, bv[it]);
       }
+#pragma unroll
+      for (int it = 0; it < 8; ++it)
+        if (wave + kWaves * it < r / 8)
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) part = fmaf(bv[it][jj], a[it][jj], part);
     }
     dotp[wave][lane] = part;
     __syncthreads();
@@ -640,7 +709,7 @@ static int verify_run(int R, int gamma, int V, int r, const void* target_, const
   verify_prep_kernel<<<1, 1024, 0, stream>>>(R, gamma, ell, ws, status);
   {
     // persistent grid over the items of list A (its length is known on the device only)
-    const int items = R * (gamma + 1) * lse_tiles(V), cap = 6 * device_cus();
+    const int items = R * (gamma + 1) * lse_tiles(V), cap = 4 * device_cus();
     verify_lse_kernel<T><<<items < cap ? items : cap, kLseThreads, 0, stream>>>(
         R, gamma, V, target, ell, ws, seed, cycle);
   }
