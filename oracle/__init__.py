@@ -52,9 +52,11 @@ def lib():
         L.ora_sample_trials.argtypes = [C.c_int, f64p, C.c_uint64, C.c_uint64, C.c_int,
                                         C.c_int, C.c_long, i64p]
         common = [C.c_int] * 6 + [vp, vp, vp, vp]
-        outs = [i32p, f64p, f64p, f64p, f64p, f64p, f64p]
-        L.ora_draft_markov.argtypes = common + [f32p, i32p, i32p, C.c_uint64, C.c_uint64] + outs
-        L.ora_draft_rnn.argtypes = common + [vp, f32p, i32p, i32p, C.c_uint64, C.c_uint64] + outs
+        outs = [i32p, f64p, f64p, f64p, f64p, f64p, f64p, f64p]
+        L.ora_draft_markov.argtypes = common + [f32p, f32p, i32p, i32p, C.c_uint64,
+                                                C.c_uint64] + outs
+        L.ora_draft_rnn.argtypes = common + [vp, f32p, f32p, i32p, i32p, C.c_uint64,
+                                             C.c_uint64] + outs
         L.ora_draft_markov.restype = L.ora_draft_rnn.restype = C.c_int
         L.ora_schedule.argtypes = [C.c_int, C.c_int, f32p, f32p, C.c_int, f32p, C.c_int,
                                    C.c_int, C.c_int, i32p, f32p, f64p, f64p]
@@ -62,6 +64,9 @@ def lib():
         L.ora_verify.argtypes = ([C.c_int] * 5 + [vp, vp, vp, f64p, i32p, i32p, i32p, C.c_uint64,
                                  C.c_uint64, i32p, i32p, f64p, f64p, f64p, f64p, f64p])
         L.ora_verify.restype = C.c_int
+        L.ora_sts_fit.argtypes = [C.c_int, C.c_int, f32p, i32p, f32p, C.c_int, C.c_int, f32p,
+                                  f64p]
+        L.ora_sts_fit.restype = C.c_int
         L.ora_num_threads.restype = C.c_int
         _lib = L
     return _lib
@@ -127,7 +132,7 @@ def sample_trials(l, seed, cycle, stream_blk, stream_in, ntrials) -> np.ndarray:
     return counts
 
 
-def _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=None, req_ids=None):
+def _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=None, req_ids=None, temps=None):
     U, h, W1, W2 = (np.ascontiguousarray(a) for a in (U, h, W1, W2))
     dt = _dt_of(U)
     for a in (h, W1, W2) + ((W_gco,) if W_gco is not None else ()):
@@ -142,13 +147,15 @@ def _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=None, req_ids=None):
     x0 = _c(x0, np.int32)
     rid = None if req_ids is None else _c(req_ids, np.int32)
     assert rid is None or rid.shape == (R,)
+    tp = None if temps is None else _c(temps, np.float32)
+    assert tp is None or tp.shape == (gamma,)
     x = np.zeros((R, gamma), np.int32)
-    c, lse, logit_x, gb, gi = (np.zeros((R, gamma)) for _ in range(5))
+    c, zc, lse, logit_x, gb, gi = (np.zeros((R, gamma)) for _ in range(6))
     bias_rows = np.zeros((R, gamma, rank))
     args = [R, gamma, V, rank, d, dt, _vp(U), _vp(h), _vp(W1), _vp(W2)]
-    tail = [_p(w, C.c_float), _p(x0, C.c_int32), _p(rid, C.c_int32), seed, cycle,
-            _p(x, C.c_int32),
-            _p(c, C.c_double), _p(lse, C.c_double), _p(logit_x, C.c_double),
+    tail = [_p(w, C.c_float), _p(tp, C.c_float), _p(x0, C.c_int32), _p(rid, C.c_int32), seed,
+            cycle, _p(x, C.c_int32), _p(c, C.c_double), _p(zc, C.c_double),
+            _p(lse, C.c_double), _p(logit_x, C.c_double),
             _p(bias_rows, C.c_double), _p(gb, C.c_double), _p(gi, C.c_double)]
     if W_gco is None:
         rc = lib().ora_draft_markov(*args, *tail)
@@ -158,18 +165,37 @@ def _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=None, req_ids=None):
         rc = lib().ora_draft_rnn(*args, _vp(W_gco), *tail)
     if rc != 0:
         raise ValueError(f"oracle draft rejected its arguments (rc={rc})")
-    return dict(x=x, c=c, lse=lse, logit_x=logit_x, bias_rows=bias_rows, gap_blk=gb,
+    return dict(x=x, c=c, z=zc, lse=lse, logit_x=logit_x, bias_rows=bias_rows, gap_blk=gb,
                 gap_in=gi)
 
 
-def draft_markov(U, h, W1, W2, w, x0, seed=0, cycle=0, req_ids=None):
-    """Markov-head draft (eqs. 4, 5, 7).  W2 is [rank][V] as on the pages."""
-    return _draft(U, h, W1, W2, w, x0, seed, cycle, req_ids=req_ids)
+def draft_markov(U, h, W1, W2, w, x0, seed=0, cycle=0, req_ids=None, temps=None):
+    """Markov-head draft (eqs. 4, 5, 7).  W2 is [rank][V] as on the pages.  temps: the
+    STS temperatures per position (Module D), None = 1."""
+    return _draft(U, h, W1, W2, w, x0, seed, cycle, req_ids=req_ids, temps=temps)
 
 
-def draft_rnn(U, h, W1, W2, W_gco, w, x0, seed=0, cycle=0, req_ids=None):
+def draft_rnn(U, h, W1, W2, W_gco, w, x0, seed=0, cycle=0, req_ids=None, temps=None):
     """RNN-head draft (eq. 6, confidence eq. 7)."""
-    return _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=W_gco, req_ids=req_ids)
+    return _draft(U, h, W1, W2, w, x0, seed, cycle, W_gco=W_gco, req_ids=req_ids, temps=temps)
+
+
+def sts_fit(z, n_acc, grid, nbins=15):
+    """STS calibration (Module D): per-position temperatures from held-out confidence
+    logits z [N][gamma] and accepted lengths n_acc [N].  Returns (T [gamma], ece [gamma])."""
+    z = _c(z, np.float32)
+    N, gamma = z.shape
+    n_acc = _c(n_acc, np.int32)
+    grid = _c(grid, np.float32)
+    assert n_acc.shape == (N,)
+    T = np.zeros(gamma, np.float32)
+    ece = np.zeros(gamma)
+    rc = lib().ora_sts_fit(N, gamma, _p(z, C.c_float), _p(n_acc, C.c_int32),
+                           _p(grid, C.c_float), grid.size, nbins, _p(T, C.c_float),
+                           _p(ece, C.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle sts_fit rejected its arguments (rc={rc})")
+    return T, ece
 
 
 def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, trace=False):

@@ -182,13 +182,15 @@ static void logits_row(int V, int rank, int dt, const void *U, size_t u_off, con
   }
 }
 
-/* c_k = sigma(w^T [h_k ; W1[x_{k-1}]]), eq. (7): no bias term */
-static double confidence(int d, int rank, int dt, const void *h, size_t h_off,
-                         const float *w, const double *e) {
+/* the confidence logit z_k = w^T [h_k ; W1[x_{k-1}]] of eq. (7): no bias term; c_k =
+ * sigma(z_k / T_k) with the position's temperature from the STS calibration (Module D),
+ * T_k = 1 when uncalibrated */
+static double confidence_logit(int d, int rank, int dt, const void *h, size_t h_off,
+                               const float *w, const double *e) {
   double z = 0.0;
   for (int i = 0; i < d; ++i) z += (double)w[i] * elem(h, dt, h_off + (size_t)i);
   for (int i = 0; i < rank; ++i) z += (double)w[d + i] * e[i];
-  return sigmoid(z);
+  return z;
 }
 
 static int check_dims(int R, int gamma, int V, int rank, int d, int dt) {
@@ -208,10 +210,14 @@ static int check_dims(int R, int gamma, int V, int rank, int d, int dt) {
  * ------------------------------------------------------------------------------------ */
 static int draft_common(int R, int gamma, int V, int rank, int d, int dt, const void *U,
                         const void *h, const void *W1, const void *W2, const void *W_gco,
-                        const float *w, const int32_t *x0, const int32_t *req_ids,
-                        uint64_t seed, uint64_t cycle, int32_t *x, double *c, double *lse,
-                        double *logit_x, double *bias_rows, double *gap_blk, double *gap_in) {
+                        const float *w, const float *temps, const int32_t *x0,
+                        const int32_t *req_ids, uint64_t seed, uint64_t cycle, int32_t *x,
+                        double *c, double *zc, double *lse, double *logit_x,
+                        double *bias_rows, double *gap_blk, double *gap_in) {
   if (check_dims(R, gamma, V, rank, d, dt)) return -1;
+  if (temps)
+    for (int k = 0; k < gamma; ++k)
+      if (!(temps[k] > 0.0f)) return -1;
   int bad = 0;
   for (int r = 0; r < R; ++r)
     if (x0[r] < 0 || x0[r] >= V) bad = 1;
@@ -256,7 +262,9 @@ static int draft_common(int R, int gamma, int V, int rank, int d, int dt, const 
       int xk = ora_sample_two_level(V, l, seed, cycle, ORA_S_DRAFT_BLK, ORA_S_DRAFT_IN, rid,
                                     (uint32_t)k, &gb, &gi);
       x[rk] = xk;
-      c[rk] = confidence(d, rank, dt, h, rk * (size_t)d, w, e);
+      const double zk = confidence_logit(d, rank, dt, h, rk * (size_t)d, w, e);
+      c[rk] = sigmoid(zk / (temps ? (double)temps[k - 1] : 1.0));
+      if (zc) zc[rk] = zk;
       lse[rk] = L;
       logit_x[rk] = l[xk];
       for (int i = 0; i < rank; ++i) bias_rows[rk * (size_t)rank + i] = vec[i];
@@ -271,21 +279,72 @@ static int draft_common(int R, int gamma, int V, int rank, int d, int dt, const 
 
 int ora_draft_markov(int R, int gamma, int V, int rank, int d, int dt, const void *U,
                      const void *h, const void *W1, const void *W2, const float *w,
-                     const int32_t *x0, const int32_t *req_ids, uint64_t seed, uint64_t cycle,
-                     int32_t *x, double *c, double *lse, double *logit_x, double *bias_rows,
-                     double *gap_blk, double *gap_in) {
-  return draft_common(R, gamma, V, rank, d, dt, U, h, W1, W2, NULL, w, x0, req_ids, seed,
-                      cycle, x, c, lse, logit_x, bias_rows, gap_blk, gap_in);
+                     const float *temps, const int32_t *x0, const int32_t *req_ids,
+                     uint64_t seed, uint64_t cycle, int32_t *x, double *c, double *zc,
+                     double *lse, double *logit_x, double *bias_rows, double *gap_blk,
+                     double *gap_in) {
+  return draft_common(R, gamma, V, rank, d, dt, U, h, W1, W2, NULL, w, temps, x0, req_ids,
+                      seed, cycle, x, c, zc, lse, logit_x, bias_rows, gap_blk, gap_in);
 }
 
 int ora_draft_rnn(int R, int gamma, int V, int rank, int d, int dt, const void *U,
                   const void *h, const void *W1, const void *W2, const void *W_gco,
-                  const float *w, const int32_t *x0, const int32_t *req_ids, uint64_t seed,
-                  uint64_t cycle, int32_t *x, double *c, double *lse, double *logit_x,
-                  double *bias_rows, double *gap_blk, double *gap_in) {
+                  const float *w, const float *temps, const int32_t *x0,
+                  const int32_t *req_ids, uint64_t seed, uint64_t cycle, int32_t *x, double *c,
+                  double *zc, double *lse, double *logit_x, double *bias_rows, double *gap_blk,
+                  double *gap_in) {
   if (!W_gco) return -1;
-  return draft_common(R, gamma, V, rank, d, dt, U, h, W1, W2, W_gco, w, x0, req_ids, seed,
-                      cycle, x, c, lse, logit_x, bias_rows, gap_blk, gap_in);
+  return draft_common(R, gamma, V, rank, d, dt, U, h, W1, W2, W_gco, w, temps, x0, req_ids,
+                      seed, cycle, x, c, zc, lse, logit_x, bias_rows, gap_blk, gap_in);
+}
+
+/* ------------------------------------------------------------------------------------
+ * STS calibration (Module D).  Each c_k is a conditional probability, so the probability
+ * that the prefix through position k is accepted is the running product of c_1..c_k.
+ * Left to right, position k gets the temperature (from the candidate grid) whose scaled
+ * confidence sigma(z_k / T) makes that running product best calibrated -- smallest
+ * expected calibration error over the held-out samples -- with the earlier positions'
+ * temperatures fixed.  ECE over nbins equal-width bins of [0, 1]:
+ *   ECE = sum_bins | sum_{n in bin} (o_n - P_n) | / N,
+ * with P_n the sample's predicted prefix probability and o_n = 1 if its accepted length
+ * reaches k (0 otherwise).  Ties go to the earlier grid entry.
+ * ------------------------------------------------------------------------------------ */
+int ora_sts_fit(int N, int gamma, const float *z, const int32_t *n_acc, const float *grid,
+                int G, int nbins, float *T, double *ece) {
+  if (N < 1 || gamma < 1 || G < 1 || nbins < 1 || !z || !n_acc || !grid || !T) return -1;
+  for (int g = 0; g < G; ++g)
+    if (!(grid[g] > 0.0f)) return -1;
+  double *pref = (double *)malloc(sizeof(double) * (size_t)N);
+  double *sums = (double *)malloc(sizeof(double) * (size_t)nbins);
+  for (int n = 0; n < N; ++n) pref[n] = 1.0;
+  for (int k = 0; k < gamma; ++k) {
+    double best = INFINITY;
+    int gbest = 0;
+    for (int g = 0; g < G; ++g) {
+      for (int b = 0; b < nbins; ++b) sums[b] = 0.0;
+      for (int n = 0; n < N; ++n) {
+        const double P = pref[n] * sigmoid((double)z[(size_t)n * gamma + k] / (double)grid[g]);
+        const double o = n_acc[n] > k ? 1.0 : 0.0;
+        int b = (int)(P * nbins);
+        if (b > nbins - 1) b = nbins - 1;
+        sums[b] += o - P;
+      }
+      double e = 0.0;
+      for (int b = 0; b < nbins; ++b) e += fabs(sums[b]);
+      e /= (double)N;
+      if (e < best) {
+        best = e;
+        gbest = g;
+      }
+    }
+    T[k] = grid[gbest];
+    if (ece) ece[k] = best;
+    for (int n = 0; n < N; ++n)
+      pref[n] *= sigmoid((double)z[(size_t)n * gamma + k] / (double)T[k]);
+  }
+  free(pref);
+  free(sums);
+  return 0;
 }
 
 /* ------------------------------------------------------------------------------------

@@ -9,6 +9,7 @@
  * decoding"):
  *   [digest]    the technical digest page (slinene.github.io, ai-papers-daily):
  *               core idea eq. (1); Module B eqs. (4)-(6); Module C eqs. (7)-(8);
+ *               Module D (sequential temperature scaling);
  *               Module E (prefix survival, B, tau, Theta, Algorithm 1, Appendix-A
  *               counterexample); production section (no-break search, two-step lag).
  *   [explainer] the interactive explainer (share.concentrate1.com): section 06,
@@ -83,17 +84,21 @@ void ora_sample_trials(int n, const double *l, uint64_t seed, uint64_t cycle, in
 /* Markov-head draft, eqs. (4), (5), (7).  Layouts (row-major):
  *   U [R][gamma][V], h [R][gamma][d], W1 [V][rank], W2 [rank][V]   (dt)
  *   w [d + rank] fp32, order [h-part ; W1-row part]; x0 [R]
+ *   temps [gamma] (nullable): STS temperatures (Module D), c_k = sigma(z_k / temps[k-1]);
+ *     NULL means 1 at every position; each must be > 0
  *   req_ids [R] (nullable): the request index each row uses in the random counters
  *     (default: its position 0..R-1), so a subset of a batch can be checked alone
- * Outputs: x [R][gamma], c, lse, logit_x [R][gamma] (double),
+ * Outputs: x [R][gamma], c, lse, logit_x [R][gamma] (double), zc [R][gamma] (double,
+ *   nullable): the confidence logit z_k = w . [h_k ; W1[x_{k-1}]] before the temperature,
  *   bias_rows [R][gamma][rank] (double): the vector that multiplies W2 at step k,
  *   gap_blk, gap_in [R][gamma] (nullable).
  * Returns 0, or -1 on a bad argument / token out of range. */
 int ora_draft_markov(int R, int gamma, int V, int rank, int d, int dt, const void *U,
                      const void *h, const void *W1, const void *W2, const float *w,
-                     const int32_t *x0, const int32_t *req_ids, uint64_t seed, uint64_t cycle,
-                     int32_t *x, double *c, double *lse, double *logit_x, double *bias_rows,
-                     double *gap_blk, double *gap_in);
+                     const float *temps, const int32_t *x0, const int32_t *req_ids,
+                     uint64_t seed, uint64_t cycle, int32_t *x, double *c, double *zc,
+                     double *lse, double *logit_x, double *bias_rows, double *gap_blk,
+                     double *gap_in);
 
 /* RNN-head draft, eq. (6) with eq. (7) for c.  W_gco [3*rank][2*rank + d] (dt): rows
  * [0,rank) gate, [rank,2rank) candidate, [2rank,3rank) output; columns ordered
@@ -101,9 +106,21 @@ int ora_draft_markov(int R, int gamma, int V, int rank, int d, int dt, const voi
  * ora_draft_markov. */
 int ora_draft_rnn(int R, int gamma, int V, int rank, int d, int dt, const void *U,
                   const void *h, const void *W1, const void *W2, const void *W_gco,
-                  const float *w, const int32_t *x0, const int32_t *req_ids, uint64_t seed,
-                  uint64_t cycle, int32_t *x, double *c, double *lse, double *logit_x,
-                  double *bias_rows, double *gap_blk, double *gap_in);
+                  const float *w, const float *temps, const int32_t *x0,
+                  const int32_t *req_ids, uint64_t seed, uint64_t cycle, int32_t *x, double *c,
+                  double *zc, double *lse, double *logit_x, double *bias_rows, double *gap_blk,
+                  double *gap_in);
+
+/* STS calibration (Module D): per-position temperatures fitted left to right on held-out
+ * samples, each minimising the expected calibration error of the running product of the
+ * scaled confidences, earlier positions fixed.
+ *   z [N][gamma] fp32: confidence logits (before any temperature)
+ *   n_acc [N]: accepted length of each sample's drafted block (0..gamma)
+ *   grid [G] fp32 candidate temperatures (> 0); nbins equal-width bins of [0, 1]
+ * Outputs: T [gamma]; ece [gamma] (nullable): the ECE reached at each position.
+ * Returns 0, or -1 on a bad argument. */
+int ora_sts_fit(int N, int gamma, const float *z, const int32_t *n_acc, const float *grid,
+                int G, int nbins, float *T, double *ece);
 
 /* Prefix scheduler (Module E, Algorithm 1 and the production variants).
  *   c [R][gamma] fp32; c_lag [R_lag][gamma] (ASYNC_LAG2 only, else NULL)
