@@ -23,7 +23,8 @@ FAULT_TOKEN, FAULT_CONF, FAULT_LEN = 1, 2, 4
 EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov", "dspark_draft_markov_timed",
            "dspark_draft_rnn_workspace_bytes", "dspark_draft_rnn",
            "dspark_schedule_workspace_bytes", "dspark_schedule",
-           "dspark_verify_workspace_bytes", "dspark_verify", "dspark_version")
+           "dspark_verify_workspace_bytes", "dspark_verify",
+           "dspark_sts_workspace_bytes", "dspark_sts_fit", "dspark_version")
 
 _lib = None
 
@@ -53,12 +54,12 @@ def lib():
         L.dspark_draft_workspace_bytes.restype = sz
         L.dspark_draft_rnn_workspace_bytes.argtypes = [i] * 5
         L.dspark_draft_rnn_workspace_bytes.restype = sz
-        L.dspark_draft_markov.argtypes = ([i] * 6 + [vp] * 6 + [u64, u64] + [vp] * 6 +
+        L.dspark_draft_markov.argtypes = ([i] * 6 + [vp] * 7 + [u64, u64] + [vp] * 7 +
                                           [vp, sz, vp])
         L.dspark_draft_markov.restype = i
         L.dspark_draft_markov_timed.argtypes = L.dspark_draft_markov.argtypes + [vp, vp]
         L.dspark_draft_markov_timed.restype = i
-        L.dspark_draft_rnn.argtypes = ([i] * 6 + [vp] * 7 + [u64, u64] + [vp] * 6 +
+        L.dspark_draft_rnn.argtypes = ([i] * 6 + [vp] * 8 + [u64, u64] + [vp] * 7 +
                                        [vp, sz, vp])
         L.dspark_draft_rnn.restype = i
         L.dspark_schedule_workspace_bytes.argtypes = [i, i]
@@ -70,6 +71,10 @@ def lib():
         L.dspark_verify.argtypes = ([i] * 5 + [vp] * 4 + [i] + [vp] * 4 + [u64, u64] +
                                     [vp] * 4 + [vp, sz, vp])
         L.dspark_verify.restype = i
+        L.dspark_sts_workspace_bytes.argtypes = [i] * 3
+        L.dspark_sts_workspace_bytes.restype = sz
+        L.dspark_sts_fit.argtypes = [i, i, vp, vp, vp, i, i, vp, vp, vp, sz, vp]
+        L.dspark_sts_fit.restype = i
         L.dspark_version.restype = C.c_char_p
         _lib = L
     return _lib
@@ -144,8 +149,8 @@ def draft_rnn_workspace_bytes(R, gamma, V, r, d) -> int:
     return int(lib().dspark_draft_rnn_workspace_bytes(R, gamma, V, r, d))
 
 
-def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, out=None, ws=None, status=None,
-           events=None):
+def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, temps=None, out=None, ws=None,
+           status=None, events=None):
     torch = _torch()
     _chk(U, "U")
     R, gamma, V = U.shape
@@ -157,6 +162,8 @@ def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, out=None, ws=None
     _chk(W2t, "W2t", (V, r), U.dtype)
     _chk(w, "w", (d + r,), torch.float32)
     _chk(x0, "x0", (R,), torch.int32)
+    if temps is not None:
+        _chk(temps, "temps", (gamma,), torch.float32)
     if rnn:
         _chk(W_gco, "W_gco", (3 * r, 2 * r + d), U.dtype)
     dev = U.device
@@ -164,6 +171,7 @@ def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, out=None, ws=None
         out = dict(
             x=torch.empty((R, gamma), dtype=torch.int32, device=dev),
             c=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+            z=torch.empty((R, gamma), dtype=torch.float32, device=dev),
             lse=torch.empty((R, gamma), dtype=torch.float32, device=dev),
             logit_x=torch.empty((R, gamma), dtype=torch.float32, device=dev),
             bias_rows=torch.empty((R, gamma, r), dtype=torch.float32 if rnn else U.dtype,
@@ -175,8 +183,8 @@ def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, out=None, ws=None
     args = [R, gamma, V, r, d, dt, _p(U), _p(h), _p(W1), _p(W2t)]
     if rnn:
         args.append(_p(W_gco))
-    args += [_p(w), _p(x0), seed, cycle, _p(out["x"]), _p(out["c"]), _p(out["lse"]),
-             _p(out["logit_x"]), _p(out["bias_rows"]), _p(status), _p(ws),
+    args += [_p(w), _p(temps), _p(x0), seed, cycle, _p(out["x"]), _p(out["c"]),
+             _p(out.get("z")), _p(out["lse"]), _p(out["logit_x"]), _p(out["bias_rows"]), _p(status), _p(ws),
              ws.numel() * ws.element_size(), _stream()]
     fn = "dspark_draft_rnn" if rnn else "dspark_draft_markov"
     if events is not None:  # (begin, end): ctypes arrays of gamma hipEvent_t each
@@ -186,18 +194,21 @@ def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, out=None, ws=None
     return out
 
 
-def draft_markov(U, h, W1, W2t, w, x0, seed=0, cycle=0, *, out=None, ws=None, status=None,
-                 events=None):
-    """Markov-head draft; returns dict(x, c, lse, logit_x, bias_rows) (device tensors).
-    events=(begin, end) arrays of gamma hipEvent_t selects the timed variant."""
-    return _draft(False, U, h, W1, W2t, w, x0, seed, cycle, out=out, ws=ws, status=status,
-                  events=events)
+def draft_markov(U, h, W1, W2t, w, x0, seed=0, cycle=0, *, temps=None, out=None, ws=None,
+                 status=None, events=None):
+    """Markov-head draft; returns dict(x, c, z, lse, logit_x, bias_rows) (device tensors).
+    temps: [gamma] float32 STS temperatures (None: 1).  A caller-supplied `out` without a
+    "z" entry skips that output.  events=(begin, end) arrays of gamma hipEvent_t selects
+    the timed variant."""
+    return _draft(False, U, h, W1, W2t, w, x0, seed, cycle, temps=temps, out=out, ws=ws,
+                  status=status, events=events)
 
 
-def draft_rnn(U, h, W1, W2t, W_gco, w, x0, seed=0, cycle=0, *, out=None, ws=None, status=None):
+def draft_rnn(U, h, W1, W2t, W_gco, w, x0, seed=0, cycle=0, *, temps=None, out=None, ws=None,
+              status=None):
     """RNN-head draft; bias_rows is float32."""
-    return _draft(True, U, h, W1, W2t, w, x0, seed, cycle, W_gco=W_gco, out=out, ws=ws,
-                  status=status)
+    return _draft(True, U, h, W1, W2t, w, x0, seed, cycle, W_gco=W_gco, temps=temps, out=out,
+                  ws=ws, status=status)
 
 
 def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, *, out=None, status=None):
@@ -256,4 +267,36 @@ def verify(target, U, W2t, bias_rows, x, lse, logit_x, ell, seed=0, cycle=0, *, 
                              _p(out["n_acc"]), _p(out["y"]), _p(out["c_star"]), _p(status),
                              _p(ws), ws.numel() * ws.element_size(), _stream())
     _raise("dspark_verify", rc)
+    return out
+
+
+def sts_workspace_bytes(N, G, nbins) -> int:
+    return int(lib().dspark_sts_workspace_bytes(N, G, nbins))
+
+
+def sts_fit(z, n_acc, grid, nbins=15, *, out=None, ws=None):
+    """STS temperatures, fitted left to right on held-out (z, accepted length) samples.
+    z [N][gamma] float32 and n_acc [N] int32 are device tensors; grid is a host sequence of
+    candidate temperatures.  Returns dict(T [gamma] float32, ece [gamma] float64)."""
+    import numpy as np
+    torch = _torch()
+    _chk(z, "z", dtype=torch.float32)
+    if z.dim() != 2:
+        raise ValueError("z must be [N][gamma]")
+    N, gamma = z.shape
+    _chk(n_acc, "n_acc", (N,), torch.int32)
+    g = np.ascontiguousarray(np.asarray(grid, dtype=np.float32).ravel())
+    dev = z.device
+    if out is None:
+        out = dict(T=torch.empty(gamma, dtype=torch.float32, device=dev),
+                   ece=torch.empty(gamma, dtype=torch.float64, device=dev))
+    nbytes = sts_workspace_bytes(N, len(g), nbins)
+    if nbytes == 0:
+        raise DsparkError("dspark_sts_workspace_bytes", EINVAL)
+    ws = _ws(nbytes, dev, ws)
+    rc = lib().dspark_sts_fit(N, gamma, _p(z), _p(n_acc),
+                              g.ctypes.data_as(C.c_void_p), len(g), nbins, _p(out["T"]),
+                              _p(out.get("ece")), _p(ws), ws.numel() * ws.element_size(),
+                              _stream())
+    _raise("dspark_sts_fit", rc)
     return out

@@ -201,10 +201,11 @@ __global__ void __launch_bounds__(64) draft_sweep_f32_kernel(
 template <class T, bool RNN>
 __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
     int R, int gamma, int V, int r, int d, const T* __restrict__ U, const T* __restrict__ W1,
-    const T* __restrict__ W2t, const float* __restrict__ w, const float* __restrict__ zh,
-    const int32_t* prev, int prev_stride, const float* __restrict__ orow,
-    const float4* __restrict__ partials, int nranges, uint32_t k, uint64_t seed, uint64_t cycle,
-    int32_t* x, float* c, float* lse, float* logit_x, void* bias_rows, int32_t* status) {
+    const T* __restrict__ W2t, const float* __restrict__ w, const float* __restrict__ temps,
+    const float* __restrict__ zh, const int32_t* prev, int prev_stride,
+    const float* __restrict__ orow, const float4* __restrict__ partials, int nranges,
+    uint32_t k, uint64_t seed, uint64_t cycle, int32_t* x, float* c, float* zout, float* lse,
+    float* logit_x, void* bias_rows, int32_t* status) {
   constexpr int kWaves = kCombineThreads / kWave;
   __shared__ float4 red[kWaves];
   __shared__ float dotp[kWaves][kWave];
@@ -309,8 +310,15 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) z += zred[i];
     if (lane == 0) {
+      // the position's STS temperature (Module D); a non-positive one is a data fault
+      float Tk = temps ? temps[k - 1] : 1.0f;
+      if (!(Tk > 0.0f)) {
+        raise_fault(status, DSPARK_FAULT_CONF);
+        Tk = 1.0f;
+      }
       x[rk] = idx;
-      c[rk] = 1.0f / (1.0f + __expf(-z));
+      c[rk] = 1.0f / (1.0f + __expf(-z / Tk));
+      if (zout) zout[rk] = z;
       lse[rk] = M + __logf(S);
       logit_x[rk] = lx;
     }
@@ -447,9 +455,10 @@ static DraftWs carve_draft(void* ws, int R, int gamma, int V, int r, int d, bool
 template <class T>
 static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void* U_,
                      const void* h_, const void* W1_, const void* W2t_, const void* Wg_,
-                     const float* w, const int32_t* x0, uint64_t seed, uint64_t cycle, int32_t* x,
-                     float* c, float* lse, float* logit_x, void* bias_rows, int32_t* status,
-                     const DraftWs& ws, hipStream_t stream, hipEvent_t* evb, hipEvent_t* eve) {
+                     const float* w, const float* temps, const int32_t* x0, uint64_t seed,
+                     uint64_t cycle, int32_t* x, float* c, float* z, float* lse, float* logit_x,
+                     void* bias_rows, int32_t* status, const DraftWs& ws, hipStream_t stream,
+                     hipEvent_t* evb, hipEvent_t* eve) {
   const T* U = static_cast<const T*>(U_);
   const T* h = static_cast<const T*>(h_);
   const T* W1 = static_cast<const T*>(W1_);
@@ -534,22 +543,22 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
     if (eve && eve[k - 1]) (void)hipEventRecord(eve[k - 1], stream);
     if (rnn)
       draft_combine_kernel<T, true><<<R, kCombineThreads, 0, stream>>>(
-          R, gamma, V, r, d, U, W1, W2t, w, ws.zh, prev, ps, ws.orow, ws.partials, nranges,
-          (uint32_t)k, seed, cycle, x, c, lse, logit_x, bias_rows, status);
+          R, gamma, V, r, d, U, W1, W2t, w, temps, ws.zh, prev, ps, ws.orow, ws.partials,
+          nranges, (uint32_t)k, seed, cycle, x, c, z, lse, logit_x, bias_rows, status);
     else
       draft_combine_kernel<T, false><<<R, kCombineThreads, 0, stream>>>(
-          R, gamma, V, r, d, U, W1, W2t, w, ws.zh, prev, ps, nullptr, ws.partials, nranges,
-          (uint32_t)k, seed, cycle, x, c, lse, logit_x, bias_rows, status);
+          R, gamma, V, r, d, U, W1, W2t, w, temps, ws.zh, prev, ps, nullptr, ws.partials,
+          nranges, (uint32_t)k, seed, cycle, x, c, z, lse, logit_x, bias_rows, status);
   }
   return launch_status();
 }
 
 static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_dtype dt,
                        const void* U, const void* h, const void* W1, const void* W2t,
-                       const void* Wg, const float* w, const int32_t* x0, uint64_t seed,
-                       uint64_t cycle, int32_t* x, float* c, float* lse, float* logit_x,
-                       void* bias_rows, int32_t* status, void* ws, size_t ws_bytes,
-                       hipStream_t stream, hipEvent_t* evb = nullptr,
+                       const void* Wg, const float* w, const float* temps, const int32_t* x0,
+                       uint64_t seed, uint64_t cycle, int32_t* x, float* c, float* z,
+                       float* lse, float* logit_x, void* bias_rows, int32_t* status, void* ws,
+                       size_t ws_bytes, hipStream_t stream, hipEvent_t* evb = nullptr,
                        hipEvent_t* eve = nullptr) {
   if (!dims_ok(R, gamma, V, r, d) || (dt != DSPARK_F32 && dt != DSPARK_BF16)) return DSPARK_EINVAL;
   if (cycle >= ((uint64_t)1 << 28)) return DSPARK_EINVAL;
@@ -568,10 +577,11 @@ static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_d
   if (!aligned16(ws)) return DSPARK_EINVAL;
   const DraftWs lay = carve_draft(ws, R, gamma, V, r, d, rnn);
   if (dt == DSPARK_BF16)
-    return draft_run<uint16_t>(rnn, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, x0, seed, cycle, x,
-                               c, lse, logit_x, bias_rows, status, lay, stream, evb, eve);
-  return draft_run<float>(rnn, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, x0, seed, cycle, x, c,
-                          lse, logit_x, bias_rows, status, lay, stream, evb, eve);
+    return draft_run<uint16_t>(rnn, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, temps, x0, seed,
+                               cycle, x, c, z, lse, logit_x, bias_rows, status, lay, stream,
+                               evb, eve);
+  return draft_run<float>(rnn, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, temps, x0, seed, cycle,
+                          x, c, z, lse, logit_x, bias_rows, status, lay, stream, evb, eve);
 }
 
 }  // namespace dspark
@@ -590,34 +600,37 @@ size_t dspark_draft_rnn_workspace_bytes(int R, int gamma, int V, int r, int d) {
 
 int dspark_draft_markov(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void* U,
                         const void* h, const void* W1, const void* W2t, const float* w,
-                        const int32_t* x0, uint64_t seed, uint64_t cycle, int32_t* x, float* c,
-                        float* lse, float* logit_x, void* bias_rows, int32_t* dev_status,
-                        void* ws, size_t ws_bytes, hipStream_t stream) {
-  return dspark::draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, x0, seed,
-                             cycle, x, c, lse, logit_x, bias_rows, dev_status, ws, ws_bytes,
-                             stream);
+                        const float* temps, const int32_t* x0, uint64_t seed, uint64_t cycle,
+                        int32_t* x, float* c, float* z, float* lse, float* logit_x,
+                        void* bias_rows, int32_t* dev_status, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  return dspark::draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, temps, x0,
+                             seed, cycle, x, c, z, lse, logit_x, bias_rows, dev_status, ws,
+                             ws_bytes, stream);
 }
 
 int dspark_draft_markov_timed(int R, int gamma, int V, int r, int d, dspark_dtype dt,
                               const void* U, const void* h, const void* W1, const void* W2t,
-                              const float* w, const int32_t* x0, uint64_t seed, uint64_t cycle,
-                              int32_t* x, float* c, float* lse, float* logit_x, void* bias_rows,
-                              int32_t* dev_status, void* ws, size_t ws_bytes, hipStream_t stream,
+                              const float* w, const float* temps, const int32_t* x0,
+                              uint64_t seed, uint64_t cycle, int32_t* x, float* c, float* z,
+                              float* lse, float* logit_x, void* bias_rows, int32_t* dev_status,
+                              void* ws, size_t ws_bytes, hipStream_t stream,
                               hipEvent_t* ev_begin, hipEvent_t* ev_end) {
   if (!ev_begin || !ev_end) return DSPARK_EINVAL;
-  return dspark::draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, x0, seed,
-                             cycle, x, c, lse, logit_x, bias_rows, dev_status, ws, ws_bytes,
-                             stream, ev_begin, ev_end);
+  return dspark::draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, temps, x0,
+                             seed, cycle, x, c, z, lse, logit_x, bias_rows, dev_status, ws,
+                             ws_bytes, stream, ev_begin, ev_end);
 }
 
 int dspark_draft_rnn(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void* U,
                      const void* h, const void* W1, const void* W2t, const void* W_gco,
-                     const float* w, const int32_t* x0, uint64_t seed, uint64_t cycle,
-                     int32_t* x, float* c, float* lse, float* logit_x, float* bias_rows,
-                     int32_t* dev_status, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return dspark::draft_entry(true, R, gamma, V, r, d, dt, U, h, W1, W2t, W_gco, w, x0, seed,
-                             cycle, x, c, lse, logit_x, bias_rows, dev_status, ws, ws_bytes,
-                             stream);
+                     const float* w, const float* temps, const int32_t* x0, uint64_t seed,
+                     uint64_t cycle, int32_t* x, float* c, float* z, float* lse, float* logit_x,
+                     float* bias_rows, int32_t* dev_status, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  return dspark::draft_entry(true, R, gamma, V, r, d, dt, U, h, W1, W2t, W_gco, w, temps, x0,
+                             seed, cycle, x, c, z, lse, logit_x, bias_rows, dev_status, ws,
+                             ws_bytes, stream);
 }
 
 }  // extern "C"

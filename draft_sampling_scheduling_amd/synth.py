@@ -231,3 +231,18 @@ def encode(cfg: Config, x) -> np.ndarray:
 def decode(cfg: Config, a) -> np.ndarray:
     """Operand values as float32 (bf16 widened exactly)."""
     return bf16_to_f32(a) if cfg.is_bf16 else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def sts_heldout(N: int, temps, seed: int, loc: float = 1.5, scale: float = 2.0):
+    """Held-out calibration samples for the STS fit: confidence logits z [N][gamma] float32,
+    z ~ N(loc, scale^2), and accepted lengths n_acc [N] int32 drawn from a chain in which
+    position k is accepted, given its prefix was, with probability sigmoid(z_k / temps[k]).
+    The running product of those probabilities is then the calibrated prefix predictor,
+    so a correct fit recovers `temps` (up to the grid step and sampling noise)."""
+    rng = np.random.default_rng([0x575, seed])
+    gamma = len(temps)
+    z = rng.normal(loc, scale, (N, gamma)).astype(np.float32)
+    p = 1.0 / (1.0 + np.exp(-z.astype(np.float64) / np.asarray(temps, np.float64)))
+    ok = rng.uniform(size=(N, gamma)) < p
+    n_acc = np.where(ok.all(axis=1), gamma, np.argmin(ok, axis=1)).astype(np.int32)
+    return z, n_acc

@@ -85,7 +85,9 @@ enum { DSPARK_FAULT_TOKEN = 1, DSPARK_FAULT_CONF = 2, DSPARK_FAULT_LEN = 4 };
  *   lse[q][k]    = log sum_v exp l(v);   q_k = softmax(l)
  *   x[q][k]      = two-level Gumbel-max sample of q_k (streams 0, 1)
  *   logit_x      = l(x_k);  so q_k(x_k) = exp(logit_x - lse)
- *   c[q][k]      = sigmoid( sum_i w[i] h_k[i] + sum_i w[d+i] e[i] )   (no bias term)
+ *   z[q][k]      = sum_i w[i] h_k[i] + sum_i w[d+i] e[i]           (no bias term)
+ *   c[q][k]      = sigmoid(z / T_k), T_k = temps[k-1] (the STS temperatures of Module D;
+ *                  1 when temps is NULL)
  *
  * Inputs
  *   U   [R][gamma][V] dt   base logits U_1..U_gamma of the parallel backbone
@@ -94,9 +96,13 @@ enum { DSPARK_FAULT_TOKEN = 1, DSPARK_FAULT_CONF = 2, DSPARK_FAULT_LEN = 4 };
  *   W2t [V][r] dt          W_2 transposed: row v holds column v of W_2 in R^{r x V}
  *                          (the usual storage of an output projection)
  *   w   [d + r] float      confidence weights, ordered [h part ; W1-row part]
+ *   temps [gamma] float    per-position temperatures (> 0), or NULL; a value that is not
+ *                          > 0 sets DSPARK_FAULT_CONF and that position uses 1
  *   x0  [R] int32          anchors
  * Outputs
  *   x, c, lse, logit_x [R][gamma] (int32, float, float, float)
+ *   z [R][gamma] float (NULL: not written): the confidence logits before the temperature,
+ *     the held-out data dspark_sts_fit calibrates on
  *   bias_rows [R][gamma][r]: the vector that multiplied W2 at each step, for verify;
  *     Markov: type dt (exact copy of W1 rows);  RNN: float.
  * Workspace: ws_bytes >= dspark_draft_workspace_bytes(...), any 256-byte aligned buffer.
@@ -105,9 +111,10 @@ size_t dspark_draft_workspace_bytes(int R, int gamma, int V, int r, int d);
 
 int dspark_draft_markov(int R, int gamma, int V, int r, int d, dspark_dtype dt,
                         const void *U, const void *h, const void *W1, const void *W2t,
-                        const float *w, const int32_t *x0, uint64_t seed, uint64_t cycle,
-                        int32_t *x, float *c, float *lse, float *logit_x, void *bias_rows,
-                        int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream);
+                        const float *w, const float *temps, const int32_t *x0, uint64_t seed,
+                        uint64_t cycle, int32_t *x, float *c, float *z, float *lse,
+                        float *logit_x, void *bias_rows, int32_t *dev_status, void *ws,
+                        size_t ws_bytes, hipStream_t stream);
 
 /* Benchmark hook: exactly dspark_draft_markov, and additionally records ev_begin[k-1] and
  * ev_end[k-1] (events the caller created, gamma of each) on `stream` immediately before
@@ -116,9 +123,10 @@ int dspark_draft_markov(int R, int gamma, int V, int r, int d, dspark_dtype dt,
  * DSPARK_EINVAL if either array is NULL. */
 int dspark_draft_markov_timed(int R, int gamma, int V, int r, int d, dspark_dtype dt,
                               const void *U, const void *h, const void *W1, const void *W2t,
-                              const float *w, const int32_t *x0, uint64_t seed, uint64_t cycle,
-                              int32_t *x, float *c, float *lse, float *logit_x, void *bias_rows,
-                              int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream,
+                              const float *w, const float *temps, const int32_t *x0,
+                              uint64_t seed, uint64_t cycle, int32_t *x, float *c, float *z,
+                              float *lse, float *logit_x, void *bias_rows, int32_t *dev_status,
+                              void *ws, size_t ws_bytes, hipStream_t stream,
                               hipEvent_t *ev_begin, hipEvent_t *ev_end);
 
 /* RNN head, eq. (6): W_gco [3r][2r + d] dt stacks the gate, candidate and output
@@ -129,9 +137,10 @@ size_t dspark_draft_rnn_workspace_bytes(int R, int gamma, int V, int r, int d);
 
 int dspark_draft_rnn(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void *U,
                      const void *h, const void *W1, const void *W2t, const void *W_gco,
-                     const float *w, const int32_t *x0, uint64_t seed, uint64_t cycle,
-                     int32_t *x, float *c, float *lse, float *logit_x, float *bias_rows,
-                     int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream);
+                     const float *w, const float *temps, const int32_t *x0, uint64_t seed,
+                     uint64_t cycle, int32_t *x, float *c, float *z, float *lse,
+                     float *logit_x, float *bias_rows, int32_t *dev_status, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Schedule (digest, Module E and Algorithm 1; production deployment for the variants).
@@ -185,6 +194,32 @@ int dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, const void *t
                   const float *logit_x, const int32_t *ell, uint64_t seed, uint64_t cycle,
                   int32_t *n_acc, int32_t *y, float *c_star, int32_t *dev_status, void *ws,
                   size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * STS calibration (digest, Module D): per-position temperatures for the confidence head,
+ * fitted left to right on held-out cycles.  For k = 1..gamma in order, with T_1..T_{k-1}
+ * fixed, T_k is the grid entry minimising
+ *   ECE_k(T) = sum_{b < nbins} | sum_{n : bin(P_n) = b} (o_n - P_n) | / N,
+ *   P_n = prod_{j<k} sigmoid(z[n][j] / T_j) * sigmoid(z[n][k] / T),
+ *   o_n = (n_acc[n] >= k),   bin(P) = min(floor(P * nbins), nbins - 1),
+ * in double; ties go to the earlier grid entry.  Each (o - P) is added in fixed point with
+ * 2^-38 resolution, so the bin sums (and the choice) do not depend on the launch shape.
+ * Inputs (device unless noted)
+ *   z     [N][gamma] float  confidence logits of drafted positions (dspark_draft_* `z`),
+ *                           finite
+ *   n_acc [N] int32         accepted length of each sample's verified block
+ *   grid  [G] float, HOST   candidate temperatures, each finite and > 0
+ *   1 <= N <= 2^24, 1 <= G <= 128, 1 <= nbins <= 256, G * nbins <= 4096
+ * Outputs: T [gamma] float (device; usable as dspark_draft_* temps); ece [gamma] double
+ *   (device, nullable): ECE_k at the chosen T_k.
+ * Workspace: ws_bytes >= dspark_sts_workspace_bytes(N, G, nbins) (0: sizes out of range).
+ * DSPARK_EINVAL for sizes or grid values out of range or a NULL required pointer.
+ * ------------------------------------------------------------------------------------ */
+size_t dspark_sts_workspace_bytes(int N, int G, int nbins);
+
+int dspark_sts_fit(int N, int gamma, const float *z, const int32_t *n_acc, const float *grid,
+                   int G, int nbins, float *T, double *ece, void *ws, size_t ws_bytes,
+                   hipStream_t stream);
 
 /* Library version string (static storage). */
 const char *dspark_version(void);

@@ -43,6 +43,9 @@ def compare_draft(o, g, label=""):
             # outputs of step k depend on x_{k-1}, which matched
             assert abs(g["c"][q, k] - o["c"][q, k]) <= TOL_P, (label, q, k, g["c"][q, k], o["c"][q, k])
             assert abs(g["lse"][q, k] - o["lse"][q, k]) <= TOL_P, (label, q, k, g["lse"][q, k], o["lse"][q, k])
+            if "z" in g and "z" in o:  # confidence logit before the temperature
+                assert abs(g["z"][q, k] - o["z"][q, k]) <= TOL_P * (1 + abs(o["z"][q, k])), (
+                    label, q, k, g["z"][q, k], o["z"][q, k])
             if xg[q, k] != xo[q, k]:
                 near = min(o["gap_blk"][q, k], o["gap_in"][q, k]) < TIE_GAP
                 assert near, (label, "token mismatch off a near-tie", q, k, xg[q, k], xo[q, k],

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(ds):
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(ds.lib(), n), n
     assert set(names) == set(ds.EXPORTS)
@@ -52,9 +52,9 @@ def test_draft_rejects_bad_arguments(ds):
     ws = ds.draft_workspace_bytes(4, 4, 1024, 16, 64)
 
     def call(R=4, gamma=4, V=1024, r=16, d=64, dt=ds.F32, U=FAKE, ws_bytes=ws, cycle=0):
-        return L.dspark_draft_markov(R, gamma, V, r, d, dt, U, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
-                                     cycle, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_bytes,
-                                     None)
+        return L.dspark_draft_markov(R, gamma, V, r, d, dt, U, FAKE, FAKE, FAKE, FAKE, None,
+                                     FAKE, 0, cycle, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                     FAKE, ws_bytes, None)
 
     assert call(V=1001) == ds.EINVAL
     assert call(r=24) == ds.EINVAL
@@ -92,3 +92,27 @@ def test_verify_rejects_bad_arguments(ds):
     assert call(dt=ds.F32, bdt=ds.BF16) == ds.EINVAL  # bias rows must be float or dt
     assert call(ws_bytes=ws - 1) == ds.EWORKSPACE
     assert call(V=1020) == ds.EINVAL
+
+
+def test_sts_rejects_bad_arguments(ds):
+    import numpy as np
+    L = ds.lib()
+    assert ds.sts_workspace_bytes(0, 10, 15) == 0
+    assert ds.sts_workspace_bytes(1000, 129, 1) == 0       # G > 128
+    assert ds.sts_workspace_bytes(1000, 64, 65) == 0       # G * nbins > 4096
+    assert ds.sts_workspace_bytes((1 << 24) + 1, 4, 4) == 0
+    ws = ds.sts_workspace_bytes(1000, 3, 10)
+    assert ws >= 1000 * 8
+
+    def call(grid=(0.5, 1.0, 2.0), N=1000, gamma=4, nbins=10, ws_bytes=ws):
+        g = np.asarray(grid, np.float32)
+        return L.dspark_sts_fit(N, gamma, FAKE, FAKE, g.ctypes.data_as(C.c_void_p), len(g),
+                                nbins, FAKE, None, FAKE, ws_bytes, None)
+
+    assert call(grid=(0.5, 0.0, 2.0)) == ds.EINVAL
+    assert call(grid=(0.5, -1.0)) == ds.EINVAL
+    assert call(grid=(0.5, float("nan"))) == ds.EINVAL
+    assert call(grid=(0.5, float("inf"))) == ds.EINVAL
+    assert call(gamma=0) == ds.EINVAL
+    assert call(gamma=65) == ds.EINVAL
+    assert call(ws_bytes=ws - 1) == ds.EWORKSPACE

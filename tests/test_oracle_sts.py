@@ -15,16 +15,8 @@ from draft_sampling_scheduling_amd import synth
 GRID = np.round(np.arange(0.2, 4.01, 0.1), 2).astype(np.float32)
 
 
-def _chain(N, T_true, seed, loc=1.5, scale=2.0):
-    """z ~ N(loc, scale^2) per position; position k is accepted with probability
-    sigma(z_k / T_k) given the prefix was; n_acc = number of leading acceptances."""
-    rng = np.random.default_rng(seed)
-    gamma = len(T_true)
-    z = rng.normal(loc, scale, (N, gamma)).astype(np.float32)
-    p = 1.0 / (1.0 + np.exp(-z.astype(np.float64) / np.asarray(T_true, np.float64)))
-    ok = rng.uniform(size=(N, gamma)) < p
-    n_acc = np.where(ok.all(axis=1), gamma, np.argmin(ok, axis=1)).astype(np.int32)
-    return z, n_acc
+def _chain(N, T_true, seed):
+    return synth.sts_heldout(N, T_true, seed)
 
 
 def test_recovers_true_temperatures(ora):
