@@ -246,3 +246,18 @@ def sts_heldout(N: int, temps, seed: int, loc: float = 1.5, scale: float = 2.0):
     ok = rng.uniform(size=(N, gamma)) < p
     n_acc = np.where(ok.all(axis=1), gamma, np.argmin(ok, axis=1)).astype(np.int32)
     return z, n_acc
+
+
+def train_batch(cfg: Config) -> dict:
+    """Teacher-forced training blocks for the loss forward: target logits [R][gamma][V]
+    (a fresh U-law row of the request plus the config's target noise, encoded) and the
+    reference tokens x*_1..x*_gamma [R][gamma] int32, the argmax of each target row (a
+    greedy target continuation).  x*_0 is the request's anchor."""
+    T = np.empty((cfg.R, cfg.gamma, cfg.V), np.float32)
+    for q in range(cfg.R):
+        g = _rng(cfg.seed, 12, q)
+        T[q] = _u_rows(cfg, g, q, cfg.gamma)
+        T[q] += g.standard_normal((cfg.gamma, cfg.V), dtype=np.float32) * np.float32(
+            max(target_noise_std(cfg, q), 0.1))
+    xstar = np.argmax(T, axis=2).astype(np.int32)
+    return dict(target=_encode(cfg, T), xstar=xstar)

@@ -67,6 +67,9 @@ def lib():
         L.ora_sts_fit.argtypes = [C.c_int, C.c_int, f32p, i32p, f32p, C.c_int, C.c_int, f32p,
                                   f64p]
         L.ora_sts_fit.restype = C.c_int
+        L.ora_train_forward.argtypes = ([C.c_int] * 6 + [vp, vp, vp, vp, f32p, vp, i32p, i32p,
+                                        f64p, f64p, f64p, f64p, f64p, f64p])
+        L.ora_train_forward.restype = C.c_int
         L.ora_num_threads.restype = C.c_int
         _lib = L
     return _lib
@@ -196,6 +199,43 @@ def sts_fit(z, n_acc, grid, nbins=15):
     if rc != 0:
         raise ValueError(f"oracle sts_fit rejected its arguments (rc={rc})")
     return T, ece
+
+
+
+ALPHA = (0.1, 0.9, 1.0)  # (a_ce, a_tv, a_conf), Module F eq. (12) defaults
+
+
+def train_forward(U, h, W1, W2, w, target, x0, xstar, alpha=ALPHA):
+    """Training objective forward (Module F, eqs. 8-12) on teacher-forced blocks with the
+    Markov head.  target [R][gamma][V]; xstar [R][gamma] reference tokens (x*_0 = x0).
+    Returns dict(c_star, c, logq, tv [R][gamma]; loss [R][4] = L_ce, L_tv, L_conf, L)."""
+    U, h, W1, W2, target = (np.ascontiguousarray(a) for a in (U, h, W1, W2, target))
+    dt = _dt_of(U)
+    for a in (h, W1, W2, target):
+        if _dt_of(a) != dt:
+            raise TypeError("all big operands must share one dtype")
+    R, gamma, V = U.shape
+    rank = W1.shape[1]
+    d = h.shape[2]
+    assert W1.shape == (V, rank) and W2.shape == (rank, V) and h.shape[:2] == (R, gamma)
+    assert target.shape == (R, gamma, V)
+    w = _c(w, np.float32)
+    assert w.shape == (d + rank,)
+    x0 = _c(x0, np.int32)
+    xs = _c(xstar, np.int32)
+    assert x0.shape == (R,) and xs.shape == (R, gamma)
+    al = _c(alpha, np.float64)
+    assert al.shape == (3,)
+    cs, c, lq, tv = (np.zeros((R, gamma)) for _ in range(4))
+    loss = np.zeros((R, 4))
+    rc = lib().ora_train_forward(R, gamma, V, rank, d, dt, _vp(U), _vp(h), _vp(W1), _vp(W2),
+                                 _p(w, C.c_float), _vp(target), _p(x0, C.c_int32),
+                                 _p(xs, C.c_int32), _p(al, C.c_double), _p(cs, C.c_double),
+                                 _p(c, C.c_double), _p(lq, C.c_double), _p(tv, C.c_double),
+                                 _p(loss, C.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle train_forward rejected its arguments (rc={rc})")
+    return dict(c_star=cs, c=c, logq=lq, tv=tv, loss=loss)
 
 
 def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, trace=False):

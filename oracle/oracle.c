@@ -170,6 +170,9 @@ static double log_sum_exp(int n, const double *l) {
 
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
+/* log(1 + e^x), split so that e^x never overflows */
+static double softplus(double x) { return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x))); }
+
 /* l(v) = U_row(v) + sum_i vec[i] * W2[i][v]   (bias(x_{k-1}, .) = W1[x_{k-1}] W2, eq. (5);
  * for the RNN head vec = tanh(W_o z_k) and the product is W2^T vec, eq. (6)) */
 static void logits_row(int V, int rank, int dt, const void *U, size_t u_off, const void *W2,
@@ -296,6 +299,76 @@ int ora_draft_rnn(int R, int gamma, int V, int rank, int d, int dt, const void *
   if (!W_gco) return -1;
   return draft_common(R, gamma, V, rank, d, dt, U, h, W1, W2, W_gco, w, temps, x0, req_ids,
                       seed, cycle, x, c, zc, lse, logit_x, bias_rows, gap_blk, gap_in);
+}
+
+/* ------------------------------------------------------------------------------------
+ * Training objective, forward only (Module F, eqs. (8)-(12)), on teacher-forced blocks:
+ * the head's previous token at position k is the reference token x*_{k-1} of the target
+ * sequence (x*_0 = the anchor), so every position of a block is known up front.
+ *   q_k   = softmax(U_k + W1[x*_{k-1}] W2)      (the Markov head, eq. (5))
+ *   p_k   = softmax(target row k)
+ *   tv_k  = sum_v |p_k(v) - q_k(v)|,  c*_k = 1 - tv_k / 2            (eq. (8))
+ *   c_k   = sigma(w . [h_k ; W1[x*_{k-1}]])                          (eq. (7))
+ *   w_k   = exp(-(k-1)/gamma)
+ *   L_ce  = -sum_k w_k log q_k(x*_k)                                 (eq. (9))
+ *   L_tv  =  sum_k w_k tv_k                                          (eq. (10))
+ *   L_conf= -sum_k w_k [c*_k log c_k + (1 - c*_k) log(1 - c_k)]      (eq. (11))
+ *   L     = a_ce L_ce + a_tv L_tv + a_conf L_conf                    (eq. (12))
+ * per block (request); the batch objective is their mean.
+ * ------------------------------------------------------------------------------------ */
+int ora_train_forward(int R, int gamma, int V, int rank, int d, int dt, const void *U,
+                      const void *h, const void *W1, const void *W2, const float *w,
+                      const void *target, const int32_t *x0, const int32_t *xstar,
+                      const double *alpha, double *c_star, double *c, double *logq,
+                      double *tv_out, double *loss) {
+  if (check_dims(R, gamma, V, rank, d, dt) || !alpha) return -1;
+  for (int r = 0; r < R; ++r) {
+    if (x0[r] < 0 || x0[r] >= V) return -1;
+    for (int k = 0; k < gamma; ++k)
+      if (xstar[(size_t)r * gamma + k] < 0 || xstar[(size_t)r * gamma + k] >= V) return -1;
+  }
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < R; ++r) {
+    double *l = (double *)malloc(sizeof(double) * (size_t)V);
+    double *t = (double *)malloc(sizeof(double) * (size_t)V);
+    double *e = (double *)malloc(sizeof(double) * (size_t)rank);
+    double Lce = 0.0, Ltv = 0.0, Lconf = 0.0;
+    for (int k = 1; k <= gamma; ++k) {
+      const size_t rk = (size_t)r * (size_t)gamma + (size_t)(k - 1);
+      const int32_t prev = k == 1 ? x0[r] : xstar[rk - 1];
+      const int32_t xs = xstar[rk];
+      for (int i = 0; i < rank; ++i) e[i] = elem(W1, dt, (size_t)prev * (size_t)rank + i);
+      logits_row(V, rank, dt, U, rk * (size_t)V, W2, e, l);
+      const double Lq = log_sum_exp(V, l);
+      for (int v = 0; v < V; ++v) t[v] = elem(target, dt, rk * (size_t)V + (size_t)v);
+      const double Lp = log_sum_exp(V, t);
+      double tv = 0.0;
+      for (int v = 0; v < V; ++v) tv += fabs(exp(t[v] - Lp) - exp(l[v] - Lq));
+      const double cs = 1.0 - 0.5 * tv;
+      const double zk = confidence_logit(d, rank, dt, h, rk * (size_t)d, w, e);
+      const double ck = sigmoid(zk);
+      const double lq = l[xs] - Lq;
+      const double wk = exp(-(double)(k - 1) / (double)gamma);
+      Lce += -wk * lq;
+      Ltv += wk * tv;
+      /* log c = -softplus(-z), log(1 - c) = -softplus(z): the same logarithms, formed
+       * without the cancellation of 1 - c when c rounds to 1 */
+      Lconf += wk * (cs * softplus(-zk) + (1.0 - cs) * softplus(zk));
+      if (c_star) c_star[rk] = cs;
+      if (c) c[rk] = ck;
+      if (logq) logq[rk] = lq;
+      if (tv_out) tv_out[rk] = tv;
+    }
+    if (loss) {
+      loss[4 * (size_t)r + 0] = Lce;
+      loss[4 * (size_t)r + 1] = Ltv;
+      loss[4 * (size_t)r + 2] = Lconf;
+      loss[4 * (size_t)r + 3] = alpha[0] * Lce + alpha[1] * Ltv + alpha[2] * Lconf;
+    }
+    free(l); free(t); free(e);
+  }
+  return 0;
 }
 
 /* ------------------------------------------------------------------------------------

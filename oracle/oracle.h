@@ -111,6 +111,20 @@ int ora_draft_rnn(int R, int gamma, int V, int rank, int d, int dt, const void *
                   double *zc, double *lse, double *logit_x, double *bias_rows, double *gap_blk,
                   double *gap_in);
 
+/* Training objective forward (Module F, eqs. (8)-(12)) with the Markov head on
+ * teacher-forced blocks: position k's previous token is x*_{k-1} (x*_0 = x0[r]).
+ *   target [R][gamma][V] (dt): target logits of positions 1..gamma
+ *   xstar [R][gamma]: reference tokens x*_1..x*_gamma; alpha[3] = (a_ce, a_tv, a_conf)
+ * Outputs (each nullable), [R][gamma]: c_star = 1 - tv/2, c = sigma(w.[h;W1[x*_{k-1}]]),
+ *   logq = log q_k(x*_k), tv = ||p_k - q_k||_1;  loss [R][4] = (L_ce, L_tv, L_conf, L)
+ *   with position weights exp(-(k-1)/gamma).
+ * Returns 0, or -1 on a bad argument (a token out of range). */
+int ora_train_forward(int R, int gamma, int V, int rank, int d, int dt, const void *U,
+                      const void *h, const void *W1, const void *W2, const float *w,
+                      const void *target, const int32_t *x0, const int32_t *xstar,
+                      const double *alpha, double *c_star, double *c, double *logq,
+                      double *tv, double *loss);
+
 /* STS calibration (Module D): per-position temperatures fitted left to right on held-out
  * samples, each minimising the expected calibration error of the running product of the
  * scaled confidences, earlier positions fixed.
