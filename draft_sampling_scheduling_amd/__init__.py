@@ -24,7 +24,8 @@ EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov", "dspark_draft_
            "dspark_draft_rnn_workspace_bytes", "dspark_draft_rnn",
            "dspark_schedule_workspace_bytes", "dspark_schedule",
            "dspark_verify_workspace_bytes", "dspark_verify",
-           "dspark_sts_workspace_bytes", "dspark_sts_fit", "dspark_version")
+           "dspark_sts_workspace_bytes", "dspark_sts_fit",
+           "dspark_train_forward_workspace_bytes", "dspark_train_forward", "dspark_version")
 
 _lib = None
 
@@ -75,6 +76,12 @@ def lib():
         L.dspark_sts_workspace_bytes.restype = sz
         L.dspark_sts_fit.argtypes = [i, i, vp, vp, vp, i, i, vp, vp, vp, sz, vp]
         L.dspark_sts_fit.restype = i
+        L.dspark_train_forward_workspace_bytes.argtypes = [i] * 5
+        L.dspark_train_forward_workspace_bytes.restype = sz
+        f = C.c_float
+        L.dspark_train_forward.argtypes = ([i] * 6 + [vp] * 8 + [f, f, f] + [vp] * 6 +
+                                           [vp, sz, vp])
+        L.dspark_train_forward.restype = i
         L.dspark_version.restype = C.c_char_p
         _lib = L
     return _lib
@@ -299,4 +306,48 @@ def sts_fit(z, n_acc, grid, nbins=15, *, out=None, ws=None):
                               _p(out.get("ece")), _p(ws), ws.numel() * ws.element_size(),
                               _stream())
     _raise("dspark_sts_fit", rc)
+    return out
+
+
+ALPHA = (0.1, 0.9, 1.0)  # (a_ce, a_tv, a_conf): the loss mix of the training objective
+
+
+def train_forward_workspace_bytes(R, gamma, V, r, d) -> int:
+    return int(lib().dspark_train_forward_workspace_bytes(R, gamma, V, r, d))
+
+
+def train_forward(U, h, W1, W2t, w, target, x0, xstar, alpha=ALPHA, *, out=None, ws=None,
+                  status=None):
+    """Training-objective forward on teacher-forced blocks (Markov head, bf16 operands).
+    Returns dict(c_star, c, logq, tv [R][gamma]; loss [R][4] = L_ce, L_tv, L_conf, L)."""
+    torch = _torch()
+    _chk(U, "U")
+    R, gamma, V = U.shape
+    dt = _dt(U)
+    r = W1.shape[1]
+    d = h.shape[2]
+    _chk(h, "h", (R, gamma, d), U.dtype)
+    _chk(W1, "W1", (V, r), U.dtype)
+    _chk(W2t, "W2t", (V, r), U.dtype)
+    _chk(w, "w", (d + r,), torch.float32)
+    _chk(target, "target", (R, gamma, V), U.dtype)
+    _chk(x0, "x0", (R,), torch.int32)
+    _chk(xstar, "xstar", (R, gamma), torch.int32)
+    dev = U.device
+    if out is None:
+        out = {k: torch.empty((R, gamma), dtype=torch.float32, device=dev)
+               for k in ("c_star", "c", "logq", "tv")}
+        out["loss"] = torch.empty((R, 4), dtype=torch.float32, device=dev)
+    nbytes = train_forward_workspace_bytes(R, gamma, V, r, d)
+    if nbytes == 0:
+        raise DsparkError("dspark_train_forward_workspace_bytes", EINVAL)
+    ws = _ws(nbytes, dev, ws)
+    a = [float(x) for x in alpha]
+    rc = lib().dspark_train_forward(R, gamma, V, r, d, dt, _p(U), _p(h), _p(W1), _p(W2t),
+                                    _p(w), _p(target), _p(x0), _p(xstar), a[0], a[1], a[2],
+                                    _p(out.get("c_star")), _p(out.get("c")),
+                                    _p(out.get("logq")), _p(out.get("tv")),
+                                    _p(out.get("loss")), _p(status), _p(ws),
+                                    ws.numel() * ws.element_size(), _stream())
+    _raise("dspark_train_forward", rc)
     return out

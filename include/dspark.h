@@ -196,6 +196,36 @@ int dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, const void *t
                   size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * Training objective, forward (digest, Module F, eqs. (8)-(12)), Markov head, on
+ * teacher-forced blocks: position k of block q conditions on the reference token
+ * x*_{k-1} (x*_0 = x0[q], x*_k = xstar[q][k-1]), so the R * gamma rows are independent.
+ *   q_k    = softmax(U_k + W1[x*_{k-1}] W2);  p_k = softmax(target[q][k-1])
+ *   tv     = sum_v |p_k(v) - q_k(v)|;  c_star = 1 - tv / 2                  (eq. (8))
+ *   c      = sigmoid(w . [h_k ; W1[x*_{k-1}]])                              (eq. (7))
+ *   logq   = log q_k(x*_k)
+ *   w_k    = exp(-(k-1)/gamma)
+ *   loss[q] = {L_ce, L_tv, L_conf, L}:  L_ce = -sum_k w_k logq,  L_tv = sum_k w_k tv,
+ *            L_conf = sum_k w_k [c* softplus(-z) + (1 - c*) softplus(z)]
+ *            (= -sum_k w_k [c* log c + (1 - c*) log(1 - c)]),
+ *            L = a_ce L_ce + a_tv L_tv + a_conf L_conf   (the pages' mix: 0.1, 0.9, 1.0)
+ * Inputs (device): U, h, W1, W2t, w as in dspark_draft_markov; target [R][gamma][V] dt;
+ *   x0 [R], xstar [R][gamma] int32.  dt must be DSPARK_BF16 (float operands: EINVAL).
+ * Outputs (device, each nullable): c_star, c, logq, tv [R][gamma] float;
+ *   loss [R][4] float.  The batch objective is the mean of loss[:, 3].
+ * A token out of range sets DSPARK_FAULT_TOKEN (token 0 is used in its place).
+ * Workspace: ws_bytes >= dspark_train_forward_workspace_bytes(...) (0: sizes out of
+ * range; R * gamma * V * 2 must stay below 4 GiB).
+ * ------------------------------------------------------------------------------------ */
+size_t dspark_train_forward_workspace_bytes(int R, int gamma, int V, int r, int d);
+
+int dspark_train_forward(int R, int gamma, int V, int r, int d, dspark_dtype dt,
+                         const void *U, const void *h, const void *W1, const void *W2t,
+                         const float *w, const void *target, const int32_t *x0,
+                         const int32_t *xstar, float a_ce, float a_tv, float a_conf,
+                         float *c_star, float *c, float *logq, float *tv, float *loss,
+                         int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * STS calibration (digest, Module D): per-position temperatures for the confidence head,
  * fitted left to right on held-out cycles.  For k = 1..gamma in order, with T_1..T_{k-1}
  * fixed, T_k is the grid entry minimising

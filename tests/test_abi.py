@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(ds):
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(ds.lib(), n), n
     assert set(names) == set(ds.EXPORTS)
@@ -116,3 +116,22 @@ def test_sts_rejects_bad_arguments(ds):
     assert call(gamma=0) == ds.EINVAL
     assert call(gamma=65) == ds.EINVAL
     assert call(ws_bytes=ws - 1) == ds.EWORKSPACE
+
+
+def test_train_forward_rejects_bad_arguments(ds):
+    L = ds.lib()
+    ws = ds.train_forward_workspace_bytes(4, 4, 1024, 16, 64)
+    assert ws > 0
+    assert ds.train_forward_workspace_bytes(4, 4, 1001, 16, 64) == 0
+    assert ds.train_forward_workspace_bytes(2048, 8, 151936, 256, 4096) == 0  # >= 4 GiB rows
+
+    def call(dt=ds.BF16, V=1024, r=16, ws_bytes=ws, R=4):
+        return L.dspark_train_forward(R, 4, V, r, 64, dt, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, 0.1, 0.9, 1.0, None, None, None, None, None,
+                                      None, FAKE, ws_bytes, None)
+
+    assert call(dt=ds.F32) == ds.EINVAL
+    assert call(V=1020) == ds.EINVAL
+    assert call(r=24) == ds.EINVAL
+    assert call(ws_bytes=ws - 1) == ds.EWORKSPACE
+    assert call(R=0) == ds.OK
