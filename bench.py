@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c3", help="workload: c3 (headline) or c2")
+    ap.add_argument("--workload", default="cycle", choices=("cycle", "train", "sts"),
+                    help="cycle: the decode cycle (default); train: the training-objective "
+                         "forward on teacher-forced blocks; sts: the STS calibration fit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample")
@@ -208,6 +211,11 @@ def main():
               f"--gpus {args.gpus} / WORLD_SIZE={world} is not supported", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "train":
+        return bench_train(args)
+    if args.workload == "sts":
+        return bench_sts(args)
+
     import numpy as np
     import torch
 
@@ -364,6 +372,178 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         res["cpu_baseline"] = cpu_baseline(cfg, I, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+def _timed_calls(torch, fn, warmup, steps):
+    """Mean device time of fn() over `steps` calls on torch's current stream (events around
+    each call) and the wall time of the whole timed loop."""
+    import numpy as np
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])), wall * 1e3 / steps
+
+
+def bench_train(args):
+    """Training-objective forward (teacher-forced blocks, Module F) on the headline sizes:
+    R=256 blocks of gamma=8 positions, V=151936, r=256, d=4096, bf16."""
+    import numpy as np
+    import torch
+
+    import draft_sampling_scheduling_amd as ds
+    from draft_sampling_scheduling_amd import synth
+
+    ds.lib()
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    I = synth.inputs(cfg)
+    B = synth.train_batch(cfg)
+
+    def T(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    U, h, W1, w, x0 = T(I["U"]), T(I["h"]), T(I["W1"]), T(I["w"]), T(I["x0"])
+    W2t = T(np.ascontiguousarray(I["W2"].T))
+    target, xstar = T(B["target"]), T(B["xstar"])
+    R, G, V, r, d = cfg.R, cfg.gamma, cfg.V, cfg.r, cfg.d
+    gen_s = time.perf_counter() - t_gen
+    log(f"teacher-forced batch of {cfg.name} resident on the device ({gen_s:.1f} s)")
+    out = {k: torch.empty((R, G), dtype=torch.float32, device=dev)
+           for k in ("c_star", "c", "logq", "tv")}
+    out["loss"] = torch.empty((R, 4), dtype=torch.float32, device=dev)
+    ws = torch.empty(ds.train_forward_workspace_bytes(R, G, V, r, d), dtype=torch.uint8,
+                     device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def call():
+        ds.train_forward(U, h, W1, W2t, w, target, x0, xstar, out=out, ws=ws, status=status)
+
+    call_ms, ms_per_step = _timed_calls(torch, call, args.warmup, args.steps)
+    if int(status.item()) != 0:
+        raise SystemExit(f"device fault bits set: {int(status.item())}")
+    rows = R * G
+    # algorithmic bytes of one call: each sweep reads U, the target and W2t once (the W1
+    # rows are gathered per row); the merge reads the hidden states
+    sweep_bytes = 2 * rows * V * 2 + V * r * 2 + rows * r * 2
+    call_bytes = 2 * sweep_bytes + rows * d * 2
+    achieved = call_bytes / (call_ms * 1e-3) / 1e9
+    res = {
+        "metric": "training-objective forward rows/s (teacher-forced, R=256 gamma=8 "
+                  "V=151936); % of HBM roofline",
+        "value": rows / (ms_per_step * 1e-3),
+        "unit": "teacher-forced rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} teacher-forced blocks: Markov head R={R} gamma={G} "
+                               f"V={V} r={r} d={d}, bf16 operands; c*, L_ce, L_tv, L_conf",
+                   "R": R, "gamma": G, "V": V, "r": r, "d": d},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "dspark_train_forward (two sweeps, merge, final), whole call",
+                     "bytes_per_launch": call_bytes, "launch_us": call_ms * 1e3},
+        "mean_loss": float(out["loss"][:, 3].mean().item()),
+        "input_gen_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.lib()
+        threads = oracle.num_threads()
+
+        def run(S):
+            t0 = time.perf_counter()
+            oracle.train_forward(I["U"][:S], I["h"][:S], I["W1"], I["W2"], I["w"],
+                                 B["target"][:S], I["x0"][:S], B["xstar"][:S])
+            return time.perf_counter() - t0
+
+        t1 = run(threads)
+        S = int(threads * max(1.0, args.cpu_seconds / max(t1, 1e-3)))
+        S = max(threads, min(R, (S // threads) * threads))
+        t = run(S)
+        res["cpu_baseline"] = dict(
+            value=S * G / t, unit="teacher-forced rows/s", cores=threads, kind="oracle",
+            sample=f"the first {S} of {R} blocks of the same batch, fp64; {t:.1f} s wall")
+    print(json.dumps(res))
+
+
+STS_N = 1 << 20  # held-out samples: 4096 cycles of 256 requests
+STS_GRID = [round(0.2 + 0.1 * i, 2) for i in range(39)]  # 0.2 .. 4.0
+STS_BINS = 15
+
+
+def bench_sts(args):
+    """STS calibration fit (Module D) on 2^20 held-out samples of gamma=8 positions, 39
+    candidate temperatures, 15 bins."""
+    import numpy as np
+    import torch
+
+    import draft_sampling_scheduling_amd as ds
+    from draft_sampling_scheduling_amd import synth
+
+    ds.lib()
+    dev = torch.device("cuda:0")
+    temps = [1.6, 0.7, 1.0, 2.5, 1.2, 0.9, 1.4, 2.0]
+    z, n_acc = synth.sts_heldout(STS_N, temps, seed=1)
+    zt, nt = torch.from_numpy(z).to(dev), torch.from_numpy(n_acc).to(dev)
+    G = len(temps)
+    out = dict(T=torch.empty(G, dtype=torch.float32, device=dev),
+               ece=torch.empty(G, dtype=torch.float64, device=dev))
+    ws = torch.empty(ds.sts_workspace_bytes(STS_N, len(STS_GRID), STS_BINS), dtype=torch.uint8,
+                     device=dev)
+
+    def call():
+        ds.sts_fit(zt, nt, STS_GRID, STS_BINS, out=out, ws=ws)
+
+    call_ms, ms_per_step = _timed_calls(torch, call, args.warmup, args.steps)
+    # the definition's fp64 operations per (sample, candidate, position): z/T, exp, 1 + e,
+    # the reciprocal division, the running-product multiply, the bin scale, o - P and the
+    # fixed-point scale (divide and exp counted as one each)
+    evals = STS_N * len(STS_GRID) * G
+    achieved = evals * 8 / (call_ms * 1e-3) / 1e12
+    res = {
+        "metric": "STS calibration held-out samples/s (gamma=8, 39 temperatures, 15 bins)",
+        "value": STS_N / (ms_per_step * 1e-3),
+        "unit": "held-out samples/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"STS fit: N={STS_N} held-out samples, gamma={G}, "
+                               f"{len(STS_GRID)} candidate temperatures, {STS_BINS} bins",
+                   "N": STS_N, "gamma": G, "grid": len(STS_GRID), "nbins": STS_BINS},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": 78.6, "unit": "TFLOP/s",
+                     "frac": achieved / 78.6, "traffic": None,
+                     "kernel": "dspark_sts_fit (per position: bins, reduce, pick), whole call",
+                     "flops_per_eval": 8, "launch_us": call_ms * 1e3},
+        "T": [float(x) for x in out["T"].cpu().numpy()],
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.lib()
+        n = 1 << 14
+        t0 = time.perf_counter()
+        oracle.sts_fit(z[:n], n_acc[:n], np.asarray(STS_GRID, np.float32), STS_BINS)
+        t1 = time.perf_counter() - t0
+        n = int(min(STS_N, max(n, n * args.cpu_seconds / max(t1, 1e-3))))
+        t0 = time.perf_counter()
+        oracle.sts_fit(z[:n], n_acc[:n], np.asarray(STS_GRID, np.float32), STS_BINS)
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = dict(value=n / t, unit="held-out samples/s", cores=1,
+                                   kind="oracle",
+                                   sample=f"the first {n} of {STS_N} samples; {t:.1f} s wall")
     print(json.dumps(res))
 
 

@@ -74,21 +74,27 @@ __global__ __launch_bounds__(kStsThreads) void sts_bins_kernel(
   for (int i = threadIdx.x; i < cells; i += kStsThreads) out[i] = (long long)bins[i];
 }
 
-// one workgroup per 64 cells: lane = cell, the four waves split the rows
-__global__ __launch_bounds__(kStsThreads) void sts_reduce_kernel(
+// one workgroup per 64 cells: lane = cell, the 16 waves split the rows (independent
+// loads, several in flight per lane)
+constexpr int kStsReduceThreads = 1024;
+
+__global__ __launch_bounds__(kStsReduceThreads) void sts_reduce_kernel(
     int nwg, int cells, const long long* __restrict__ partials, long long* __restrict__ sums) {
-  __shared__ unsigned long long part[kStsThreads / kWave][kWave];
+  constexpr int kWaves = kStsReduceThreads / kWave;
+  __shared__ unsigned long long part[kWaves][kWave];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int cell = blockIdx.x * kWave + lane;
   unsigned long long acc = 0ull;
-  if (cell < cells)
-    for (int w = wave; w < nwg; w += kStsThreads / kWave)
+  if (cell < cells) {
+#pragma unroll 8
+    for (int w = wave; w < nwg; w += kWaves)
       acc += (unsigned long long)partials[(size_t)w * cells + cell];
+  }
   part[wave][lane] = acc;
   __syncthreads();
   if (wave == 0 && cell < cells) {
     unsigned long long s = 0ull;
-    for (int i = 0; i < kStsThreads / kWave; ++i) s += part[i][lane];
+    for (int i = 0; i < kWaves; ++i) s += part[i][lane];
     sums[cell] = (long long)s;
   }
 }
@@ -172,7 +178,7 @@ int dspark_sts_fit(int N, int gamma, const float* z, const int32_t* n_acc, const
   for (int k = 0; k < gamma; ++k) {
     sts_bins_kernel<<<nwg, kStsThreads, 0, stream>>>(N, gamma, k, z, n_acc, gv, G, nbins, T,
                                                     w.pref, w.partials);
-    sts_reduce_kernel<<<(cells + kWave - 1) / kWave, kStsThreads, 0, stream>>>(
+    sts_reduce_kernel<<<(cells + kWave - 1) / kWave, kStsReduceThreads, 0, stream>>>(
         nwg, cells, w.partials, w.sums);
     sts_pick_kernel<<<1, kStsMaxG, 0, stream>>>(N, k, G, nbins, w.sums, gv, T, ece);
   }
