@@ -70,6 +70,10 @@ def lib():
         L.ora_train_forward.argtypes = ([C.c_int] * 6 + [vp, vp, vp, vp, f32p, vp, i32p, i32p,
                                         f64p, f64p, f64p, f64p, f64p, f64p])
         L.ora_train_forward.restype = C.c_int
+        L.ora_decode_run.argtypes = ([C.c_int] * 7 + [vp, vp, vp, vp, f32p, f32p, vp, i32p,
+                                     C.c_int, C.c_float, f32p, C.c_int, C.c_int, C.c_uint64,
+                                     i32p, i32p, i64p])
+        L.ora_decode_run.restype = C.c_int
         L.ora_num_threads.restype = C.c_int
         _lib = L
     return _lib
@@ -236,6 +240,45 @@ def train_forward(U, h, W1, W2, w, target, x0, xstar, alpha=ALPHA):
     if rc != 0:
         raise ValueError(f"oracle train_forward rejected its arguments (rc={rc})")
     return dict(c_star=cs, c=c, logq=lq, tv=tv, loss=loss)
+
+
+
+FIXED, THRESHOLD = 3, 4  # length policies of the driver beyond the scheduler's modes
+
+
+def decode_run(Ub, Hb, W1, W2, w, Tb, x0, ncycles, policy=SYNC_BREAK, threshold=0.0,
+               sps=None, sps_B0=1, seed=0, temps=None):
+    """Multi-cycle decode on a toy chain (bigram target Tb [V][V], table backbone Ub
+    [V][gamma][V], Hb [V][gamma][d]).  Returns dict(tokens [R][ncycles*(gamma+1)],
+    n_emitted [R], tested [gamma], accepted [gamma], sum_ell, emitted, request_cycles)."""
+    Ub, Hb, W1, W2, Tb = (np.ascontiguousarray(a) for a in (Ub, Hb, W1, W2, Tb))
+    dt = _dt_of(Ub)
+    for a in (Hb, W1, W2, Tb):
+        if _dt_of(a) != dt:
+            raise TypeError("all big operands must share one dtype")
+    V, gamma, _ = Ub.shape
+    rank = W1.shape[1]
+    d = Hb.shape[2]
+    assert Ub.shape == (V, gamma, V) and Hb.shape[:2] == (V, gamma) and Tb.shape == (V, V)
+    assert W1.shape == (V, rank) and W2.shape == (rank, V)
+    w = _c(w, np.float32)
+    x0 = _c(x0, np.int32)
+    R = x0.shape[0]
+    sp = None if sps is None else _c(sps, np.float32)
+    tp = None if temps is None else _c(temps, np.float32)
+    tokens = np.zeros((R, ncycles * (gamma + 1)), np.int32)
+    n_em = np.zeros(R, np.int32)
+    st = np.zeros(2 * gamma + 3, np.int64)
+    rc = lib().ora_decode_run(R, gamma, V, rank, d, dt, ncycles, _vp(Ub), _vp(Hb), _vp(W1),
+                              _vp(W2), _p(w, C.c_float), _p(tp, C.c_float), _vp(Tb),
+                              _p(x0, C.c_int32), policy, threshold, _p(sp, C.c_float), sps_B0,
+                              0 if sp is None else sp.size, seed, _p(tokens, C.c_int32),
+                              _p(n_em, C.c_int32), _p(st, C.c_int64))
+    if rc != 0:
+        raise ValueError(f"oracle decode_run rejected its arguments (rc={rc})")
+    return dict(tokens=tokens, n_emitted=n_em, tested=st[:gamma], accepted=st[gamma:2 * gamma],
+                sum_ell=int(st[2 * gamma]), emitted=int(st[2 * gamma + 1]),
+                request_cycles=int(st[2 * gamma + 2]))
 
 
 def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, trace=False):

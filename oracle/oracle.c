@@ -372,6 +372,121 @@ int ora_train_forward(int R, int gamma, int V, int rank, int d, int dt, const vo
 }
 
 /* ------------------------------------------------------------------------------------
+ * Multi-cycle decode on a toy chain (digest, overall cycle; explainer, section 06).
+ * The target is a bigram model: its logits after token t are Tb[t] (V values).  The
+ * parallel backbone is a table: for anchor a, U_k = Ub[a][k-1] and h_k = Hb[a][k-1].
+ * One cycle, for every request with anchor a (the last emitted token):
+ *   draft x_1..x_gamma from a (Markov head, eqs. (4), (5), (7); cycle counter = cycle);
+ *   choose the lengths: Algorithm 1 and its production variants (policy 0..2; the lagged
+ *   variant uses the confidences of two cycles before, and the no-break search while
+ *   there are none), every drafted position (FIXED), or every position whose prefix
+ *   survival a_j = c_1 ... c_j (fp32, left to right) is at least `threshold` (THRESHOLD);
+ *   verify against the target rows Tb[a], Tb[x_1], ..., Tb[x_gamma];
+ *   emit the accepted drafts and the correction or bonus token; the last one is the next
+ *   anchor.
+ * Counters: stats[k-1] (k = 1..gamma) = request-cycles in which position k was tested
+ * (its prefix 1..k-1 accepted and k <= ell), stats[gamma + k-1] = those in which it was
+ * accepted, then sum of ell, tokens emitted, request-cycles.
+ * ------------------------------------------------------------------------------------ */
+int ora_decode_run(int R, int gamma, int V, int rank, int d, int dt, int ncycles,
+                   const void *Ub, const void *Hb, const void *W1, const void *W2,
+                   const float *w, const float *temps, const void *Tb, const int32_t *x0,
+                   int policy, float threshold, const float *sps, int sps_B0, int sps_len,
+                   uint64_t seed, int32_t *tokens, int32_t *n_emitted, int64_t *stats) {
+  if (check_dims(R, gamma, V, rank, d, dt) || R < 1 || ncycles < 0) return -1;
+  if (policy < ORA_SYNC_BREAK || policy > ORA_POLICY_THRESHOLD) return -1;
+  if (policy <= ORA_ASYNC_LAG2 && !sps) return -1;
+  for (int q = 0; q < R; ++q)
+    if (x0[q] < 0 || x0[q] >= V) return -1;
+  const size_t RG = (size_t)R * gamma, esz = dt == ORA_BF16 ? 2 : 4;
+  const int maxlen = ncycles * (gamma + 1);
+  char *U = (char *)malloc(esz * RG * (size_t)V);
+  char *h = (char *)malloc(esz * RG * (size_t)(d > 0 ? d : 1));
+  char *tg = (char *)malloc(esz * (size_t)R * (gamma + 1) * (size_t)V);
+  int32_t *anchor = (int32_t *)malloc(sizeof(int32_t) * R);
+  int32_t *x = (int32_t *)malloc(sizeof(int32_t) * RG);
+  int32_t *ell = (int32_t *)malloc(sizeof(int32_t) * R);
+  int32_t *n_acc = (int32_t *)malloc(sizeof(int32_t) * R);
+  int32_t *y = (int32_t *)malloc(sizeof(int32_t) * (size_t)R * (gamma + 1));
+  double *c = (double *)malloc(sizeof(double) * RG);
+  double *lse = (double *)malloc(sizeof(double) * RG);
+  double *lx = (double *)malloc(sizeof(double) * RG);
+  double *br = (double *)malloc(sizeof(double) * RG * rank);
+  double *cs = (double *)malloc(sizeof(double) * RG);
+  float *cf[3];
+  for (int i = 0; i < 3; ++i) cf[i] = (float *)malloc(sizeof(float) * RG);
+  int rc = 0;
+  memcpy(anchor, x0, sizeof(int32_t) * R);
+  for (int q = 0; q < R; ++q) n_emitted[q] = 0;
+  for (size_t i = 0; i < (size_t)R * maxlen; ++i) tokens[i] = -1;
+  for (int i = 0; i < 2 * gamma + 3; ++i) stats[i] = 0;
+
+  for (int cyc = 0; cyc < ncycles && rc == 0; ++cyc) {
+    /* backbone stand-in: the anchor's table rows */
+    for (int q = 0; q < R; ++q) {
+      const size_t a = (size_t)anchor[q];
+      memcpy(U + esz * (size_t)q * gamma * V, (const char *)Ub + esz * a * gamma * V,
+             esz * (size_t)gamma * V);
+      if (d > 0)
+        memcpy(h + esz * (size_t)q * gamma * d, (const char *)Hb + esz * a * gamma * d,
+               esz * (size_t)gamma * d);
+    }
+    rc = ora_draft_markov(R, gamma, V, rank, d, dt, U, h, W1, W2, w, temps, anchor, NULL, seed,
+                          (uint64_t)cyc, x, c, NULL, lse, lx, br, NULL, NULL);
+    if (rc) break;
+    float *ccur = cf[cyc % 3];
+    for (size_t i = 0; i < RG; ++i) ccur[i] = (float)c[i];
+    if (policy == ORA_POLICY_FIXED) {
+      for (int q = 0; q < R; ++q) ell[q] = gamma;
+    } else if (policy == ORA_POLICY_THRESHOLD) {
+      for (int q = 0; q < R; ++q) {
+        float run = 1.0f;
+        int l = 0;
+        for (int j = 1; j <= gamma; ++j) {
+          volatile float prod = (j == 1) ? ccur[(size_t)q * gamma] : run * ccur[(size_t)q * gamma + j - 1];
+          run = prod;
+          if (run >= threshold && l == j - 1) l = j;
+        }
+        ell[q] = l;
+      }
+    } else {
+      const int lag = policy == ORA_ASYNC_LAG2 && cyc >= 2;
+      const int mode = lag ? ORA_ASYNC_LAG2 : (policy == ORA_ASYNC_LAG2 ? ORA_GLOBAL : policy);
+      rc = ora_schedule(R, gamma, ccur, lag ? cf[(cyc - 2) % 3] : NULL, lag ? R : 0, sps,
+                        sps_B0, sps_len, mode, ell, NULL, NULL, NULL);
+      if (rc) break;
+    }
+    /* target rows Tb[a], Tb[x_1], ..., Tb[x_gamma] */
+    for (int q = 0; q < R; ++q)
+      for (int j = 0; j <= gamma; ++j) {
+        const size_t prev = (size_t)(j == 0 ? anchor[q] : x[(size_t)q * gamma + j - 1]);
+        memcpy(tg + esz * ((size_t)q * (gamma + 1) + j) * V, (const char *)Tb + esz * prev * V,
+               esz * (size_t)V);
+      }
+    rc = ora_verify(R, gamma, V, rank, dt, tg, U, W2, br, x, ell, NULL, seed, (uint64_t)cyc,
+                    n_acc, y, cs, NULL, NULL, NULL, NULL);
+    if (rc) break;
+    for (int q = 0; q < R; ++q) {
+      for (int k = 1; k <= ell[q]; ++k) {
+        if (n_acc[q] >= k - 1) stats[k - 1] += 1;
+        if (n_acc[q] >= k) stats[gamma + k - 1] += 1;
+      }
+      stats[2 * gamma] += ell[q];
+      stats[2 * gamma + 1] += n_acc[q] + 1;
+      stats[2 * gamma + 2] += 1;
+      for (int i = 0; i <= n_acc[q]; ++i)
+        tokens[(size_t)q * maxlen + n_emitted[q] + i] = y[(size_t)q * (gamma + 1) + i];
+      n_emitted[q] += n_acc[q] + 1;
+      anchor[q] = y[(size_t)q * (gamma + 1) + n_acc[q]];
+    }
+  }
+  free(U); free(h); free(tg); free(anchor); free(x); free(ell); free(n_acc); free(y);
+  free(c); free(lse); free(lx); free(br); free(cs);
+  for (int i = 0; i < 3; ++i) free(cf[i]);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------------------
  * STS calibration (Module D).  Each c_k is a conditional probability, so the probability
  * that the prefix through position k is accepted is the running product of c_1..c_k.
  * Left to right, position k gets the temperature (from the candidate grid) whose scaled

@@ -44,6 +44,12 @@ enum {
   ORA_ASYNC_LAG2 = 2  /* capacity from confidences two cycles old, top-K now */
 };
 
+/* length policies of the multi-cycle driver beyond the scheduler's three */
+enum {
+  ORA_POLICY_FIXED = 3,    /* verify every drafted position (scheduler off)       */
+  ORA_POLICY_THRESHOLD = 4 /* verify positions whose prefix survival >= threshold */
+};
+
 /* random streams (counter word 3 low nibble) */
 enum {
   ORA_S_DRAFT_BLK = 0, ORA_S_DRAFT_IN = 1, ORA_S_ACCEPT = 2,
@@ -124,6 +130,21 @@ int ora_train_forward(int R, int gamma, int V, int rank, int d, int dt, const vo
                       const void *target, const int32_t *x0, const int32_t *xstar,
                       const double *alpha, double *c_star, double *c, double *logq,
                       double *tv, double *loss);
+
+/* Multi-cycle decode on a toy chain: bigram target Tb [V][V] (logits after token t are
+ * row t), table backbone Ub [V][gamma][V] and Hb [V][gamma][d] (U_k, h_k for anchor a are
+ * row a, k-1).  policy: ORA_SYNC_BREAK / ORA_GLOBAL / ORA_ASYNC_LAG2 (sps as in
+ * ora_schedule; the lagged variant searches without the break until two cycles exist),
+ * ORA_POLICY_FIXED (ell = gamma) or ORA_POLICY_THRESHOLD (ell = the positions whose
+ * prefix survival is >= threshold).  Cycle c uses random-counter cycle c.
+ * Outputs: tokens [R][ncycles*(gamma+1)] (emitted tokens, -1 after the last), n_emitted
+ * [R], stats [2*gamma+3] = tested per position, accepted per position, sum of ell,
+ * tokens emitted, request-cycles.  Returns 0, -1 bad argument, -2 SPS range. */
+int ora_decode_run(int R, int gamma, int V, int rank, int d, int dt, int ncycles,
+                   const void *Ub, const void *Hb, const void *W1, const void *W2,
+                   const float *w, const float *temps, const void *Tb, const int32_t *x0,
+                   int policy, float threshold, const float *sps, int sps_B0, int sps_len,
+                   uint64_t seed, int32_t *tokens, int32_t *n_emitted, int64_t *stats);
 
 /* STS calibration (Module D): per-position temperatures fitted left to right on held-out
  * samples, each minimising the expected calibration error of the running product of the
