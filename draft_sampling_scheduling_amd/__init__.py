@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 
 F32, BF16 = 0, 1
 SYNC_BREAK, GLOBAL, ASYNC_LAG2 = 0, 1, 2
+FIXED, THRESHOLD = 3, 4  # decode-driver length policies beyond the scheduler's modes
 OK, EINVAL, ERANGE, EWORKSPACE, EDEVICE = 0, -1, -2, -3, -4
 FAULT_TOKEN, FAULT_CONF, FAULT_LEN = 1, 2, 4
 EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov", "dspark_draft_markov_timed",
@@ -25,7 +26,8 @@ EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov", "dspark_draft_
            "dspark_schedule_workspace_bytes", "dspark_schedule",
            "dspark_verify_workspace_bytes", "dspark_verify",
            "dspark_sts_workspace_bytes", "dspark_sts_fit",
-           "dspark_train_forward_workspace_bytes", "dspark_train_forward", "dspark_version")
+           "dspark_train_forward_workspace_bytes", "dspark_train_forward",
+           "dspark_decode_workspace_bytes", "dspark_decode_run", "dspark_version")
 
 _lib = None
 
@@ -82,6 +84,11 @@ def lib():
         L.dspark_train_forward.argtypes = ([i] * 6 + [vp] * 8 + [f, f, f] + [vp] * 6 +
                                            [vp, sz, vp])
         L.dspark_train_forward.restype = i
+        L.dspark_decode_workspace_bytes.argtypes = [i] * 6
+        L.dspark_decode_workspace_bytes.restype = sz
+        L.dspark_decode_run.argtypes = ([i] * 7 + [vp] * 8 + [i, f, vp, i, i, u64] + [vp] * 4 +
+                                        [vp, sz, vp])
+        L.dspark_decode_run.restype = i
         L.dspark_version.restype = C.c_char_p
         _lib = L
     return _lib
@@ -350,4 +357,50 @@ def train_forward(U, h, W1, W2t, w, target, x0, xstar, alpha=ALPHA, *, out=None,
                                     _p(out.get("loss")), _p(status), _p(ws),
                                     ws.numel() * ws.element_size(), _stream())
     _raise("dspark_train_forward", rc)
+    return out
+
+
+def decode_workspace_bytes(R, gamma, V, r, d, dt) -> int:
+    return int(lib().dspark_decode_workspace_bytes(R, gamma, V, r, d, dt))
+
+
+def decode_run(Ub, Hb, W1, W2t, w, Tb, x0, ncycles, policy=SYNC_BREAK, threshold=0.0,
+               sps=None, sps_B0=1, seed=0, temps=None, *, out=None, ws=None, status=None):
+    """Multi-cycle decode on a toy chain: bigram target Tb [V][V], table backbone Ub
+    [V][gamma][V] and Hb [V][gamma][d] (device tensors).  Returns dict(tokens
+    [R][ncycles*(gamma+1)], n_emitted [R], stats [2*gamma+3] int64)."""
+    torch = _torch()
+    _chk(Ub, "Ub")
+    V, gamma, _ = Ub.shape
+    dt = _dt(Ub)
+    r = W1.shape[1]
+    d = Hb.shape[2]
+    _chk(Ub, "Ub", (V, gamma, V))
+    _chk(Hb, "Hb", (V, gamma, d), Ub.dtype)
+    _chk(W1, "W1", (V, r), Ub.dtype)
+    _chk(W2t, "W2t", (V, r), Ub.dtype)
+    _chk(w, "w", (d + r,), torch.float32)
+    _chk(Tb, "Tb", (V, V), Ub.dtype)
+    _chk(x0, "x0", dtype=torch.int32)
+    R = x0.shape[0]
+    if temps is not None:
+        _chk(temps, "temps", (gamma,), torch.float32)
+    if sps is not None:
+        _chk(sps, "sps", dtype=torch.float32)
+    dev = Ub.device
+    if out is None:
+        out = dict(tokens=torch.empty((R, ncycles * (gamma + 1)), dtype=torch.int32, device=dev),
+                   n_emitted=torch.empty(R, dtype=torch.int32, device=dev),
+                   stats=torch.empty(2 * gamma + 3, dtype=torch.int64, device=dev))
+    nbytes = decode_workspace_bytes(R, gamma, V, r, d, dt)
+    if nbytes == 0:
+        raise DsparkError("dspark_decode_workspace_bytes", EINVAL)
+    ws = _ws(nbytes, dev, ws)
+    rc = lib().dspark_decode_run(R, gamma, V, r, d, dt, ncycles, _p(Ub), _p(Hb), _p(W1),
+                                 _p(W2t), _p(w), _p(temps), _p(Tb), _p(x0), policy,
+                                 float(threshold), _p(sps), sps_B0,
+                                 0 if sps is None else sps.numel(), seed, _p(out["tokens"]),
+                                 _p(out["n_emitted"]), _p(out["stats"]), _p(status), _p(ws),
+                                 ws.numel() * ws.element_size(), _stream())
+    _raise("dspark_decode_run", rc)
     return out

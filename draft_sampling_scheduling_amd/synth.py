@@ -261,3 +261,30 @@ def train_batch(cfg: Config) -> dict:
             max(target_noise_std(cfg, q), 0.1))
     xstar = np.argmax(T, axis=2).astype(np.int32)
     return dict(target=_encode(cfg, T), xstar=xstar)
+
+
+def toy_chain(V: int, gamma: int, r: int, d: int, R: int, seed: int, dtype: str = "bf16",
+              sps_alpha: float = 0.002) -> dict:
+    """A toy decode chain for the multi-cycle driver.  Target: a bigram model whose logits
+    after token t are Tb[t] = a Zipf(1.1)-ranked row (one ranking shared by all t) + N(0, 1).
+    Backbone stand-in: U_k for anchor a is Ub[a][k-1] = Tb[a] + N(0, (0.3 + 0.2 k)^2), a base
+    prediction that drifts from the anchor's next-token law further into the block; h rows
+    N(0, 1).  Head weights as the configs (std 1/sqrt(r); w std sqrt(1/(d+r))).  Anchors
+    uniform; SPS(B) = 1/(1 + sps_alpha B) for B = 1 .. R(gamma+1)."""
+    cfg = Config("toy", seed, R, gamma, V, r, d, dtype, "markov", "zipf", 1.0, None, 1.0,
+                 None, 1.0, "smooth", sps_alpha, 1, R * (gamma + 1), 0)
+    g = _rng(0x70, seed)
+    base = (-1.1 * np.log(np.arange(1, V + 1, dtype=np.float64))).astype(np.float32)
+    Tb = base[g.permutation(V)][None, :] + g.standard_normal((V, V), dtype=np.float32)
+    sig = (0.3 + 0.2 * np.arange(1, gamma + 1, dtype=np.float32))[None, :, None]
+    Ub = Tb[:, None, :] + g.standard_normal((V, gamma, V), dtype=np.float32) * sig
+    Hb = g.standard_normal((V, gamma, d), dtype=np.float32)
+    s = np.float32(1.0 / math.sqrt(r))
+    W1 = g.standard_normal((V, r), dtype=np.float32) * s
+    W2 = g.standard_normal((r, V), dtype=np.float32) * s
+    w = g.standard_normal(d + r, dtype=np.float32) * np.float32(math.sqrt(1.0 / (d + r)))
+    x0 = g.integers(0, V, R).astype(np.int32)
+    B = np.arange(1, R * (gamma + 1) + 1, dtype=np.float64)
+    return dict(Tb=_encode(cfg, Tb), Ub=_encode(cfg, Ub), Hb=_encode(cfg, Hb),
+                W1=_encode(cfg, W1), W2=_encode(cfg, W2), w=w, x0=x0,
+                sps=(1.0 / (1.0 + sps_alpha * B)).astype(np.float32), sps_B0=1)

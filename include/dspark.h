@@ -226,6 +226,50 @@ int dspark_train_forward(int R, int gamma, int V, int r, int d, dspark_dtype dt,
                          int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * Multi-cycle decode on a toy chain (digest, overall cycle; explainer, section 06), with
+ * the pages' diagnostics.  The target is a bigram model: its logits after token t are row
+ * t of Tb [V][V].  The parallel backbone is a table: for anchor a, U_k = Ub[a][k-1] and
+ * h_k = Hb[a][k-1] (Ub [V][gamma][V], Hb [V][gamma][d]).  Each cycle c (random-counter
+ * cycle c, key seed), for every request with anchor a (x0 at the start, then the last
+ * emitted token):
+ *   draft x_1..x_gamma (dspark_draft_markov, with temps);
+ *   lengths by policy: SYNC_BREAK / GLOBAL / ASYNC_LAG2 as dspark_schedule (the lagged
+ *     variant uses the confidences of cycle c-2, and the no-break search for c < 2);
+ *     FIXED: every drafted position (scheduler off); THRESHOLD: the leading positions
+ *     whose prefix survival c_1 ... c_j (fp32, left to right) is >= threshold;
+ *   verify against Tb[a], Tb[x_1], ..., Tb[x_gamma] (dspark_verify);
+ *   append the emitted tokens; the last becomes the anchor.
+ * Outputs (device): tokens [R][ncycles*(gamma+1)] int32 (emitted tokens, -1 after the
+ *   last), n_emitted [R], stats [2*gamma+3] int64: tested[k-1] = request-cycles in which
+ *   position k was tested (k <= ell and positions 1..k-1 accepted), accepted[k-1] (at
+ *   stats[gamma + k-1]) = those in which it was accepted, then the sum of ell, the tokens
+ *   emitted and the request-cycles.  accepted/tested is the per-position conditional
+ *   acceptance; sum of ell / request-cycles the mean verification budget.
+ * Inputs: W1, W2t, w, temps as in dspark_draft_markov; sps (device) as in dspark_schedule
+ *   (unused for FIXED and THRESHOLD; DSPARK_ERANGE if it does not cover R .. R(1+gamma)).
+ * Workspace: ws_bytes >= dspark_decode_workspace_bytes(R, gamma, V, r, d, dt).
+ * Tokens out of range set DSPARK_FAULT_TOKEN (token 0 is used in their place).  On an
+ * error return the outputs are undefined.
+ * ------------------------------------------------------------------------------------ */
+typedef enum {
+  DSPARK_DECODE_SYNC_BREAK = 0,
+  DSPARK_DECODE_GLOBAL = 1,
+  DSPARK_DECODE_ASYNC_LAG2 = 2,
+  DSPARK_DECODE_FIXED = 3,
+  DSPARK_DECODE_THRESHOLD = 4
+} dspark_decode_policy;
+
+size_t dspark_decode_workspace_bytes(int R, int gamma, int V, int r, int d, dspark_dtype dt);
+
+int dspark_decode_run(int R, int gamma, int V, int r, int d, dspark_dtype dt, int ncycles,
+                      const void *Ub, const void *Hb, const void *W1, const void *W2t,
+                      const float *w, const float *temps, const void *Tb, const int32_t *x0,
+                      dspark_decode_policy policy, float threshold, const float *sps,
+                      int sps_B0, int sps_len, uint64_t seed, int32_t *tokens,
+                      int32_t *n_emitted, int64_t *stats, int32_t *dev_status, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * STS calibration (digest, Module D): per-position temperatures for the confidence head,
  * fitted left to right on held-out cycles.  For k = 1..gamma in order, with T_1..T_{k-1}
  * fixed, T_k is the grid entry minimising

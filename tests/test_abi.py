@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(ds):
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(ds.lib(), n), n
     assert set(names) == set(ds.EXPORTS)
@@ -135,3 +135,23 @@ def test_train_forward_rejects_bad_arguments(ds):
     assert call(r=24) == ds.EINVAL
     assert call(ws_bytes=ws - 1) == ds.EWORKSPACE
     assert call(R=0) == ds.OK
+
+
+def test_decode_rejects_bad_arguments(ds):
+    L = ds.lib()
+    ws = ds.decode_workspace_bytes(4, 4, 1024, 16, 8, ds.BF16)
+    assert ws > 0
+    assert ds.decode_workspace_bytes(4, 4, 1020, 16, 8, ds.BF16) == 0
+    assert ds.decode_workspace_bytes(0, 4, 1024, 16, 8, ds.BF16) == 0
+
+    def call(policy=3, sps=None, sps_B0=1, sps_len=0, ws_bytes=ws, ncycles=2, dt=ds.BF16):
+        return L.dspark_decode_run(4, 4, 1024, 16, 8, dt, ncycles, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, None, FAKE, FAKE, policy, 0.0, sps, sps_B0, sps_len,
+                                   0, FAKE, FAKE, FAKE, None, FAKE, ws_bytes, None)
+
+    assert call(policy=5) == ds.EINVAL
+    assert call(policy=0) == ds.EINVAL                          # no SPS table
+    assert call(policy=0, sps=FAKE, sps_len=10) == ds.ERANGE    # must reach R(1+gamma) = 20
+    assert call(ws_bytes=ws - 1) == ds.EWORKSPACE
+    assert call(ncycles=-1) == ds.EINVAL
+    assert call(dt=7) == ds.EINVAL
