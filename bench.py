@@ -40,9 +40,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c3", help="workload: c3 (headline) or c2")
-    ap.add_argument("--workload", default="cycle", choices=("cycle", "train", "sts"),
+    ap.add_argument("--workload", default="cycle", choices=("cycle", "train", "sts", "decode"),
                     help="cycle: the decode cycle (default); train: the training-objective "
-                         "forward on teacher-forced blocks; sts: the STS calibration fit")
+                         "forward on teacher-forced blocks; sts: the STS calibration fit; "
+                         "decode: the multi-cycle driver on a toy chain")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample")
@@ -215,6 +216,8 @@ def main():
         return bench_train(args)
     if args.workload == "sts":
         return bench_sts(args)
+    if args.workload == "decode":
+        return bench_decode(args)
 
     import numpy as np
     import torch
@@ -544,6 +547,95 @@ def bench_sts(args):
         res["cpu_baseline"] = dict(value=n / t, unit="held-out samples/s", cores=1,
                                    kind="oracle",
                                    sample=f"the first {n} of {STS_N} samples; {t:.1f} s wall")
+    print(json.dumps(res))
+
+
+DEC = dict(R=256, gamma=8, V=32000, r=256, d=512, ncycles=16, alpha=0.0005)
+
+
+def bench_decode(args):
+    """Multi-cycle driver on a toy chain: R=256 requests, gamma=8, V=32000, r=256, d=512,
+    bf16, 16 cycles per step under Algorithm 1 with the break.  The chain's tables follow
+    the toy-chain law (Zipf-ranked bigram target + N(0, 1); backbone rows = the anchor's
+    target row + N(0, (0.3 + 0.2k)^2)) drawn on the device with a seeded torch generator."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import draft_sampling_scheduling_amd as ds
+
+    ds.lib()
+    R, G, V, r, d, nc = (DEC[k] for k in ("R", "gamma", "V", "r", "d", "ncycles"))
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    t_gen = time.perf_counter()
+    base = -1.1 * torch.log(torch.arange(1, V + 1, device=dev, dtype=torch.float32))
+    base = base[torch.randperm(V, device=dev, generator=gen)]
+    Tb = (base[None, :] + torch.randn((V, V), device=dev, generator=gen)).to(torch.bfloat16)
+    Ub = torch.empty((V, G, V), dtype=torch.bfloat16, device=dev)
+    for a0 in range(0, V, 1024):
+        a1 = min(V, a0 + 1024)
+        for k in range(G):
+            Ub[a0:a1, k] = (Tb[a0:a1].float() + (0.3 + 0.2 * (k + 1)) *
+                            torch.randn((a1 - a0, V), device=dev, generator=gen)).to(torch.bfloat16)
+    Hb = torch.randn((V, G, d), device=dev, generator=gen).to(torch.bfloat16)
+    s = 1.0 / math.sqrt(r)
+    W1 = (s * torch.randn((V, r), device=dev, generator=gen)).to(torch.bfloat16)
+    W2t = (s * torch.randn((V, r), device=dev, generator=gen)).to(torch.bfloat16)
+    w = math.sqrt(1.0 / (d + r)) * torch.randn(d + r, device=dev, generator=gen)
+    x0 = torch.randint(0, V, (R,), device=dev, generator=gen, dtype=torch.int32)
+    B = torch.arange(1, R * (G + 1) + 1, device=dev, dtype=torch.float64)
+    sps = (1.0 / (1.0 + DEC["alpha"] * B)).float()
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+    log(f"toy chain tables on the device ({gen_s:.1f} s)")
+    out = dict(tokens=torch.empty((R, nc * (G + 1)), dtype=torch.int32, device=dev),
+               n_emitted=torch.empty(R, dtype=torch.int32, device=dev),
+               stats=torch.empty(2 * G + 3, dtype=torch.int64, device=dev))
+    ws = torch.empty(ds.decode_workspace_bytes(R, G, V, r, d, ds.BF16), dtype=torch.uint8,
+                     device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def call():
+        ds.decode_run(Ub, Hb, W1, W2t, w, Tb, x0, nc, ds.SYNC_BREAK, sps=sps, sps_B0=1,
+                      seed=5, out=out, ws=ws, status=status)
+
+    call_ms, ms_per_step = _timed_calls(torch, call, args.warmup, args.steps)
+    if int(status.item()) != 0:
+        raise SystemExit(f"device fault bits set: {int(status.item())}")
+    st = out["stats"].cpu().numpy()
+    tested, acc = st[:G], st[G:2 * G]
+    sum_ell, emitted, rc = int(st[2 * G]), int(st[2 * G + 1]), int(st[2 * G + 2])
+    mean_ell = sum_ell / rc
+    # algorithmic bytes of one call (per cycle: the table gathers read and write their rows,
+    # gamma draft sweeps read U_k and W2, verification reads the scheduled target rows, the
+    # bonus rows and the U rows it re-forms q from, plus W2)
+    per_cycle = (2 * R * G * V * 2 + 2 * R * (G + 1) * V * 2 + G * (R * V * 2 + V * r * 2)
+                 + (R * mean_ell + R) * V * 2 + 2 * R * mean_ell * V * 2 + V * r * 2)
+    achieved = nc * per_cycle / (call_ms * 1e-3) / 1e9
+    res = {
+        "metric": "toy-chain decode emitted tokens/s (R=256 gamma=8 V=32000, 16 cycles per "
+                  "step, Algorithm 1 with the break)",
+        "value": emitted / (ms_per_step * 1e-3),
+        "unit": "emitted tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"toy chain decode: R={R} gamma={G} V={V} r={r} d={d}, "
+                               f"{nc} cycles, SYNC_BREAK, SPS(B)=1/(1+{DEC['alpha']}B)",
+                   "R": R, "gamma": G, "V": V, "r": r, "d": d, "cycles": nc},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "dspark_decode_run, whole call (all kernels of 16 cycles)",
+                     "bytes_per_launch": nc * per_cycle, "launch_us": call_ms * 1e3},
+        "cycles_per_s": nc / (ms_per_step * 1e-3),
+        "mean_ell": mean_ell,
+        "tokens_per_request_cycle": emitted / rc,
+        "conditional_acceptance": [float(a / t) if t else None for a, t in zip(acc, tested)],
+        "input_gen_s": gen_s,
+    }
     print(json.dumps(res))
 
 

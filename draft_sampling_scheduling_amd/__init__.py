@@ -27,7 +27,8 @@ EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov", "dspark_draft_
            "dspark_verify_workspace_bytes", "dspark_verify",
            "dspark_sts_workspace_bytes", "dspark_sts_fit",
            "dspark_train_forward_workspace_bytes", "dspark_train_forward",
-           "dspark_decode_workspace_bytes", "dspark_decode_run", "dspark_version")
+           "dspark_decode_workspace_bytes", "dspark_decode_run",
+           "dspark_sps_profile", "dspark_sps_interpolate", "dspark_version")
 
 _lib = None
 
@@ -89,6 +90,11 @@ def lib():
         L.dspark_decode_run.argtypes = ([i] * 7 + [vp] * 8 + [i, f, vp, i, i, u64] + [vp] * 4 +
                                         [vp, sz, vp])
         L.dspark_decode_run.restype = i
+        L.dspark_sps_profile.argtypes = ([i] * 5 + [vp] * 4 + [i] + [vp] * 3 + [i, vp, i] +
+                                         [vp] * 6 + [vp, sz, vp])
+        L.dspark_sps_profile.restype = i
+        L.dspark_sps_interpolate.argtypes = [i, vp, vp, i, i, vp]
+        L.dspark_sps_interpolate.restype = i
         L.dspark_version.restype = C.c_char_p
         _lib = L
     return _lib
@@ -403,4 +409,50 @@ def decode_run(Ub, Hb, W1, W2t, w, Tb, x0, ncycles, policy=SYNC_BREAK, threshold
                                  _p(out["n_emitted"]), _p(out["stats"]), _p(status), _p(ws),
                                  ws.numel() * ws.element_size(), _stream())
     _raise("dspark_decode_run", rc)
+    return out
+
+
+def sps_profile(target, U, W2t, bias_rows, x, lse, logit_x, B_list, reps=10, *, ws=None,
+                status=None):
+    """SPS(B) at the profiled batches B_list: the verification pass timed as the stand-in
+    engine (steps/s).  Operands as verify(); returns a numpy float32 array [len(B_list)].
+    Synchronises with the current stream."""
+    import numpy as np
+    torch = _torch()
+    _chk(U, "U")
+    R, gamma, V = U.shape
+    dt = _dt(U)
+    r = W2t.shape[1]
+    _chk(target, "target", (R, gamma + 1, V), U.dtype)
+    _chk(bias_rows, "bias_rows", (R, gamma, r))
+    bl = np.ascontiguousarray(np.asarray(B_list, dtype=np.int32))
+    sps = np.zeros(bl.size, np.float32)
+    dev = U.device
+    ell = torch.empty(R, dtype=torch.int32, device=dev)
+    n_acc = torch.empty(R, dtype=torch.int32, device=dev)
+    y = torch.empty((R, gamma + 1), dtype=torch.int32, device=dev)
+    cs = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    ws = _ws(verify_workspace_bytes(R, gamma, V, r), dev, ws)
+    rc = lib().dspark_sps_profile(R, gamma, V, r, dt, _p(target), _p(U), _p(W2t),
+                                  _p(bias_rows), _dt(bias_rows), _p(x), _p(lse), _p(logit_x),
+                                  bl.size, bl.ctypes.data_as(C.c_void_p), reps,
+                                  sps.ctypes.data_as(C.c_void_p), _p(ell), _p(n_acc), _p(y),
+                                  _p(cs), _p(status), _p(ws), ws.numel() * ws.element_size(),
+                                  _stream())
+    _raise("dspark_sps_profile", rc)
+    return sps
+
+
+def sps_interpolate(B_list, sps_at, B0, B1):
+    """The SPS table for B = B0 .. B1 from profiled points (host only)."""
+    import numpy as np
+    bl = np.ascontiguousarray(np.asarray(B_list, dtype=np.int32))
+    sa = np.ascontiguousarray(np.asarray(sps_at, dtype=np.float32))
+    if bl.shape != sa.shape:
+        raise ValueError("B_list and sps_at differ in length")
+    out = np.zeros(max(B1 - B0 + 1, 0), np.float32)
+    rc = lib().dspark_sps_interpolate(bl.size, bl.ctypes.data_as(C.c_void_p),
+                                      sa.ctypes.data_as(C.c_void_p), B0, B1,
+                                      out.ctypes.data_as(C.c_void_p))
+    _raise("dspark_sps_interpolate", rc)
     return out

@@ -1,0 +1,93 @@
+// sps.hip -- profiling the throughput curve SPS(B) (DSpark digest page, Module E: the
+// engine's steps per second against the verification batch B, measured once at start-up
+// and then looked up by the scheduler).  The verification pass of this library stands in
+// for the target engine: for each profiled B the scheduled lengths are spread so that
+// R + sum(ell) = B, dspark_verify runs `reps` times between two events, and
+// SPS(B) = reps / elapsed seconds.  The table for every B between the profiled points is
+// their linear interpolation.
+#include <hip/hip_runtime.h>
+
+#include "dev.h"
+#include "host.h"
+
+namespace dspark {
+
+// ell[q] = floor(n / R) + (q < n mod R) with n = B - R: the B - R verified rows spread as
+// evenly as possible, earlier requests first
+__global__ void __launch_bounds__(256) sps_lengths_kernel(int R, int gamma, int n,
+                                                          int32_t* __restrict__ ell) {
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= R) return;
+  const int l = n / R + (q < n % R ? 1 : 0);
+  ell[q] = l < gamma ? l : gamma;
+}
+
+}  // namespace dspark
+
+extern "C" {
+
+int dspark_sps_interpolate(int nB, const int* B_list, const float* sps_at, int B0, int B1,
+                           float* out) {
+  if (nB < 1 || !B_list || !sps_at || !out || B1 < B0) return DSPARK_EINVAL;
+  for (int i = 0; i < nB; ++i) {
+    if (!(sps_at[i] > 0.0f)) return DSPARK_EINVAL;
+    if (i > 0 && B_list[i] <= B_list[i - 1]) return DSPARK_EINVAL;
+  }
+  if (B0 < B_list[0] || B1 > B_list[nB - 1]) return DSPARK_ERANGE;
+  int seg = 0;
+  for (int B = B0; B <= B1; ++B) {
+    while (seg + 1 < nB && B_list[seg + 1] < B) ++seg;
+    if (B == B_list[seg] || seg + 1 >= nB) {
+      out[B - B0] = sps_at[seg];
+      continue;
+    }
+    const double t = (double)(B - B_list[seg]) / (double)(B_list[seg + 1] - B_list[seg]);
+    out[B - B0] = (float)((1.0 - t) * sps_at[seg] + t * sps_at[seg + 1]);
+  }
+  return DSPARK_OK;
+}
+
+int dspark_sps_profile(int R, int gamma, int V, int r, dspark_dtype dt, const void* target,
+                       const void* U, const void* W2t, const void* bias_rows,
+                       dspark_dtype bias_dt, const int32_t* x, const float* lse,
+                       const float* logit_x, int nB, const int* B_list, int reps,
+                       float* sps_at, int32_t* ell, int32_t* n_acc, int32_t* y, float* c_star,
+                       int32_t* dev_status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  using namespace dspark;
+  if (R < 1 || gamma < 1 || nB < 1 || reps < 1 || !B_list || !sps_at || !ell) return DSPARK_EINVAL;
+  for (int i = 0; i < nB; ++i) {
+    if (B_list[i] < R || (long)B_list[i] > (long)R * (1 + gamma)) return DSPARK_ERANGE;
+    if (i > 0 && B_list[i] <= B_list[i - 1]) return DSPARK_EINVAL;
+  }
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return DSPARK_EDEVICE;
+  }
+  int rc = DSPARK_OK;
+  for (int i = 0; i < nB && rc == DSPARK_OK; ++i) {
+    sps_lengths_kernel<<<(R + 255) / 256, 256, 0, stream>>>(R, gamma, B_list[i] - R, ell);
+    // one untimed pass (first-touch and launch set-up), then the timed ones
+    rc = dspark_verify(R, gamma, V, r, dt, target, U, W2t, bias_rows, bias_dt, x, lse, logit_x,
+                       ell, 0, 0, n_acc, y, c_star, dev_status, ws, ws_bytes, stream);
+    if (rc != DSPARK_OK) break;
+    if (hipEventRecord(e0, stream) != hipSuccess) rc = DSPARK_EDEVICE;
+    for (int k = 0; k < reps && rc == DSPARK_OK; ++k)
+      rc = dspark_verify(R, gamma, V, r, dt, target, U, W2t, bias_rows, bias_dt, x, lse,
+                         logit_x, ell, 0, (uint64_t)(k + 1), n_acc, y, c_star, dev_status, ws,
+                         ws_bytes, stream);
+    if (rc != DSPARK_OK) break;
+    float ms = 0.0f;
+    if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess || !(ms > 0.0f)) {
+      rc = DSPARK_EDEVICE;
+      break;
+    }
+    sps_at[i] = (float)(reps * 1000.0 / ms);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return rc;
+}
+
+}  // extern "C"

@@ -270,6 +270,33 @@ int dspark_decode_run(int R, int gamma, int V, int r, int d, dspark_dtype dt, in
                       size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * SPS(B) profiling (digest, Module E: the engine's steps per second against the
+ * verification batch B, profiled once at start-up, looked up at run time).  The
+ * verification pass stands in for the target engine.  For each B_list[i] (ascending,
+ * R <= B <= R(1+gamma)) the lengths are spread so that R + sum(ell) = B
+ * (ell[q] = floor((B-R)/R) + (q < (B-R) mod R)), dspark_verify runs once untimed and then
+ * `reps` times between two events on `stream`, and
+ *   sps_at[i] = reps / elapsed seconds   (HOST array [nB]).
+ * The verify operands are as in dspark_verify; ell [R] (device) receives the last lengths
+ * used; n_acc, y, c_star are verify's outputs (device, overwritten).  Unlike the other
+ * calls this one SYNCHRONISES with the stream (once per profiled B).
+ * DSPARK_ERANGE if a B lies outside [R, R(1+gamma)]; DSPARK_EINVAL for an unsorted list.
+ * ------------------------------------------------------------------------------------ */
+int dspark_sps_profile(int R, int gamma, int V, int r, dspark_dtype dt, const void *target,
+                       const void *U, const void *W2t, const void *bias_rows,
+                       dspark_dtype bias_dt, const int32_t *x, const float *lse,
+                       const float *logit_x, int nB, const int *B_list, int reps,
+                       float *sps_at, int32_t *ell, int32_t *n_acc, int32_t *y, float *c_star,
+                       int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The SPS table between profiled points (host only, no device): out[B - B0] for
+ * B = B0 .. B1 is the linear interpolation of sps_at over B_list (ascending, sps_at > 0);
+ * a B equal to a profiled point takes its value.  DSPARK_ERANGE unless
+ * B_list[0] <= B0 <= B1 <= B_list[nB-1]. */
+int dspark_sps_interpolate(int nB, const int *B_list, const float *sps_at, int B0, int B1,
+                           float *out);
+
+/* ------------------------------------------------------------------------------------
  * STS calibration (digest, Module D): per-position temperatures for the confidence head,
  * fitted left to right on held-out cycles.  For k = 1..gamma in order, with T_1..T_{k-1}
  * fixed, T_k is the grid entry minimising

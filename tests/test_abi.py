@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(ds):
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(ds.lib(), n), n
     assert set(names) == set(ds.EXPORTS)
@@ -155,3 +155,35 @@ def test_decode_rejects_bad_arguments(ds):
     assert call(ws_bytes=ws - 1) == ds.EWORKSPACE
     assert call(ncycles=-1) == ds.EINVAL
     assert call(dt=7) == ds.EINVAL
+
+
+def test_sps_interpolate(ds):
+    import numpy as np
+    out = ds.sps_interpolate([10, 14, 20], [4.0, 2.0, 1.0], 10, 20)
+    expect = [4.0, 3.5, 3.0, 2.5, 2.0, 2 - 1 / 6, 2 - 2 / 6, 1.5, 2 - 4 / 6, 2 - 5 / 6, 1.0]
+    np.testing.assert_allclose(out, expect, rtol=1e-6)
+    assert ds.sps_interpolate([5], [3.0], 5, 5).tolist() == [3.0]
+    np.testing.assert_allclose(ds.sps_interpolate([0, 8], [1.0, 9.0], 3, 5), [4.0, 5.0, 6.0])
+    for bad in (([10, 10], [1.0, 1.0]), ([10, 12], [1.0, 0.0])):
+        with pytest.raises(ds.DsparkError):
+            ds.sps_interpolate(*bad, 10, 10)
+    with pytest.raises(ds.DsparkError):
+        ds.sps_interpolate([10, 20], [2.0, 1.0], 9, 15)
+
+
+def test_sps_profile_rejects_bad_arguments(ds):
+    import numpy as np
+    L = ds.lib()
+
+    def call(B, R=4, gamma=2):
+        bl = np.asarray(B, np.int32)
+        out = np.zeros(len(B), np.float32)
+        return L.dspark_sps_profile(R, gamma, 1024, 16, ds.BF16, FAKE, FAKE, FAKE, FAKE,
+                                    ds.BF16, FAKE, FAKE, FAKE, len(B),
+                                    bl.ctypes.data_as(C.c_void_p), 3,
+                                    out.ctypes.data_as(C.c_void_p), FAKE, FAKE, FAKE, FAKE,
+                                    None, FAKE, 1 << 20, None)
+
+    assert call([3, 8]) == ds.ERANGE       # below R
+    assert call([4, 13]) == ds.ERANGE      # above R(1+gamma) = 12
+    assert call([8, 6]) == ds.EINVAL       # not ascending
