@@ -3,7 +3,8 @@
 //
 // The whole scheduler is one workgroup (1024 threads) working in LDS:
 //   1. prefix survival a_{q,j} = a_{q,j-1} * c_{q,j} in float, one request per thread;
-//   2. 64-bit keys (~bits(a) << 32 | q*gamma + j-1) sorted ascending (bitonic), which is
+//   2. 64-bit keys (~bits(a) << 32 | q*gamma + j-1) sorted ascending (bitonic, in registers
+//      and shuffles up to a wave's span, through LDS beyond), which is
 //      descending a with ties broken by q, then j -- a is non-negative, so its bit pattern
 //      orders like its value, and the j order keeps every request's admitted set a prefix;
 //   3. an exact integer prefix sum of floor(a * 2^32): tau of every prefix of the order is
@@ -13,6 +14,8 @@
 //      first non-improving n minus one (break), first maximiser (no break), or the
 //      capacity of the lagged batch (two-step lag);
 //   5. ell_q = number of q's entries among the first n.
+#include <type_traits>
+
 #include "dev.h"
 #include "host.h"
 
@@ -37,96 +40,201 @@ __device__ __forceinline__ unsigned long long incr_of_key(unsigned long long key
 // smallest power of two >= x (x >= 1)
 __device__ __forceinline__ int pow2_ceil(int x) { return x <= 1 ? 1 : 1 << (32 - __clz(x - 1)); }
 
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int d) {
+  const int lo = __shfl_xor((int)(uint32_t)v, d, kWave);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), d, kWave);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// the key of lane ^ d for d < 32: a swizzle in xor mode (and-mask 31, xor-mask d) moves
+// both halves without an address operand
+template <int D>
+__device__ __forceinline__ unsigned long long swz_xor_u64(unsigned long long v) {
+  constexpr int kPat = (D << 10) | 0x1F;
+  const int lo = __builtin_amdgcn_ds_swizzle((int)(uint32_t)v, kPat);
+  const int hi = __builtin_amdgcn_ds_swizzle((int)(uint32_t)(v >> 32), kPat);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// the key of lane ^ D for D = 1, 2: a quad permutation on the DPP network (no LDS pipe)
+template <int D>
+__device__ __forceinline__ unsigned long long dpp_xor_u64(unsigned long long v) {
+  constexpr int kCtrl = D == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), kCtrl, 0xF, 0xF, false);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// compare-exchange seen from one side: the kept key is the smaller of (x, y) when keep_min,
+// else the larger (one compare, one 64-bit select)
+__device__ __forceinline__ unsigned long long cx_keep(unsigned long long x, unsigned long long y,
+                                                      bool keep_min) {
+  return ((y < x) == keep_min) ? y : x;
+}
+
+// Bitonic sort of npad keys (a power of two, npad <= 1024 * KP), ascending, starting at
+// stage kstart (blocks of kstart / 2 already sorted, alternately ascending and descending).
+// Thread t holds keys t*KP .. t*KP + KP-1 in registers: partners less than KP apart are in
+// the same thread, less than 64*KP apart in the same wave (one shuffle per key), farther
+// through LDS (two buffers used in turn, so each such step needs a single barrier).
+// Threads past npad / KP hold nothing but join the barriers.
+template <int KP>
+__device__ void sched_bitonic(unsigned long long (&key)[KP], int npad, int kstart,
+                              unsigned long long* buf0, unsigned long long* buf1) {
+  const int t = threadIdx.x;
+  const int i0 = t * KP;
+  const bool active = i0 < npad;
+  int which = 0;
+  // one in-wave step at lane distance D (compile time), when the stage has it
+  auto wave_step = [&](auto dc, int k) {
+    constexpr int D = decltype(dc)::value;
+    const int j = D * KP;
+    if (j >= k) return;
+    const bool keep_min = ((i0 & j) == 0) == ((i0 & k) == 0);
+#pragma unroll
+    for (int s = 0; s < KP; ++s) {
+      const unsigned long long y = D == 32 ? shfl_xor_u64(key[s], 32)
+                                   : (D <= 2 ? dpp_xor_u64<D>(key[s]) : swz_xor_u64<D>(key[s]));
+      key[s] = cx_keep(key[s], y, keep_min);
+    }
+  };
+  for (int k = kstart; k <= npad; k <<= 1) {
+    // partners a wave or more apart: through LDS
+    for (int j = k >> 1; j >= kWave * KP; j >>= 1) {
+      unsigned long long* b = which ? buf1 : buf0;
+      if (active)
+#pragma unroll
+        for (int s = 0; s < KP; ++s) b[i0 + s] = key[s];
+      __syncthreads();
+      const bool keep_min = ((i0 & j) == 0) == ((i0 & k) == 0);
+      if (active)
+#pragma unroll
+        for (int s = 0; s < KP; ++s) key[s] = cx_keep(key[s], b[(i0 + s) ^ j], keep_min);
+      which ^= 1;
+    }
+    // partners in the same wave (j >= KP and k > j lie above the slot bits, so one
+    // direction serves all KP keys)
+    wave_step(std::integral_constant<int, 32>{}, k);
+    wave_step(std::integral_constant<int, 16>{}, k);
+    wave_step(std::integral_constant<int, 8>{}, k);
+    wave_step(std::integral_constant<int, 4>{}, k);
+    wave_step(std::integral_constant<int, 2>{}, k);
+    wave_step(std::integral_constant<int, 1>{}, k);
+    // partners in the same thread
+#pragma unroll
+    for (int j = KP / 2; j > 0; j >>= 1) {
+      if (j >= k) continue;
+#pragma unroll
+      for (int s = 0; s < KP; ++s) {
+        const int p = s ^ j;
+        if (p > s) {
+          const bool up = ((i0 + s) & k) == 0;
+          const unsigned long long x = key[s], y = key[p];
+          const bool sw = (x > y) == up;
+          key[s] = sw ? y : x;
+          key[p] = sw ? x : y;
+        }
+      }
+    }
+  }
+}
+
+template <int KP>
+__device__ void sched_sort_lds(int npad, int kstart, SchedShared sh) {
+  unsigned long long key[KP];
+  const int t = threadIdx.x;
+  const bool active = t * KP < npad;
+#pragma unroll
+  for (int s = 0; s < KP; ++s) key[s] = active ? sh.key[t * KP + s] : ~0ull;
+  __syncthreads();  // every key is in registers before the buffers are reused
+  sched_bitonic<KP>(key, npad, kstart, sh.pre, sh.key);
+  __syncthreads();
+  if (active)
+#pragma unroll
+    for (int s = 0; s < KP; ++s) sh.key[t * KP + s] = key[s];
+  __syncthreads();
+}
+
+// inclusive scan of v over the workgroup (wave scans, then the wave totals)
+__device__ __forceinline__ unsigned long long block_scan_u64(unsigned long long v,
+                                                             unsigned long long* wsum) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int lo = __shfl_up((int)(uint32_t)v, o, kWave);
+    const int hi = __shfl_up((int)(uint32_t)(v >> 32), o, kWave);
+    const unsigned long long up = ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+    if (lane >= o) v += up;
+  }
+  if (lane == kWave - 1) wsum[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    unsigned long long x = lane < kSchedThreads / kWave ? wsum[lane] : 0ull;
+#pragma unroll
+    for (int o = 1; o < kSchedThreads / kWave; o <<= 1) {
+      const int lo = __shfl_up((int)(uint32_t)x, o, kWave);
+      const int hi = __shfl_up((int)(uint32_t)(x >> 32), o, kWave);
+      const unsigned long long up = ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+      if (lane >= o) x += up;
+    }
+    if (lane < kSchedThreads / kWave) wsum[lane] = x;
+  }
+  __syncthreads();
+  const unsigned long long base = wave > 0 ? wsum[wave - 1] : 0ull;
+  __syncthreads();  // wsum is reused by the next scan
+  return v + base;
+}
+
 // steps 1-3 for one batch of confidences; returns the candidate count |E|.  *npad_io is the
-// sorted length on entry (bitonic layout) and on return (the layout actually used).
+// sorted length on entry (the padded layout) and on return (the layout actually used).
 //
-// Each request's keys already ascend (a falls along j, ties keep j order), so when the
-// padded layout fits, the order is R runs merged pairwise: round r merges runs of length
-// P * 2^r, every key finding its place by one binary search in the partner run (keys are
-// unique; the even run counts partner keys below it, the odd run those not above it, which
-// also keeps the padding keys of the two runs apart).  Otherwise a bitonic sort.
+// Each request's keys already ascend (a falls along j, ties keep j order).  When the padded
+// run layout fits, request q's keys sit at [q * P, q * P + P) with the odd runs reversed,
+// which is the state a bitonic sort reaches after its stage P, so the sort starts at 2P;
+// otherwise the keys sit at q*gamma + j - 1 and the sort starts from pairs.
 __device__ int sched_sort_scan(int R, int gamma, const float* __restrict__ c, float* a_out,
                                int* npad_io, SchedShared sh, unsigned long long* red_u64,
                                int* red_i, int32_t* status) {
-  (void)(R * gamma);
   const int P = pow2_ceil(gamma), Rp = pow2_ceil(R);
-  const bool merge = (long)Rp * P <= *npad_io;  // both buffers hold *npad_io keys
-  const int npad = merge ? Rp * P : *npad_io;
+  const bool runs = (long)Rp * P <= *npad_io;
+  const int npad = runs ? Rp * P : *npad_io;
   *npad_io = npad;
-  // merge layout: request q's run at [q * P, q * P + P) of the source buffer (sh.pre)
-  unsigned long long* src = merge ? sh.pre : sh.key;
-  for (int i = threadIdx.x; i < npad; i += kSchedThreads) src[i] = ~0ull;
+  for (int i = threadIdx.x; i < npad; i += kSchedThreads) sh.key[i] = ~0ull;
   __syncthreads();
   for (int q = threadIdx.x; q < R; q += kSchedThreads) {
+    const float* cq = c + (size_t)q * gamma;
     float run = 1.0f;
-    for (int j = 0; j < gamma; ++j) {
-      float cj = c[(size_t)q * gamma + j];
-      if (!(cj >= 0.0f && cj <= 1.0f)) {
-        raise_fault(status, DSPARK_FAULT_CONF);
-        cj = (cj > 1.0f) ? 1.0f : 0.0f;  // NaN and negatives -> 0
+    for (int j0 = 0; j0 < gamma; j0 += 8) {
+      float cv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cv[u] = cq[j0 + u < gamma ? j0 + u : gamma - 1];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        if (j >= gamma) break;
+        float cj = cv[u];
+        if (!(cj >= 0.0f && cj <= 1.0f)) {
+          raise_fault(status, DSPARK_FAULT_CONF);
+          cj = (cj > 1.0f) ? 1.0f : 0.0f;  // NaN and negatives -> 0
+        }
+        run = (j == 0) ? cj : __fmul_rn(run, cj);
+        const int idx = q * gamma + j;
+        if (a_out) a_out[idx] = run;
+        const int pos = runs ? q * P + ((q & 1) ? P - 1 - j : j) : idx;
+        sh.key[pos] = (run > 0.0f)
+                          ? (((unsigned long long)(~__float_as_uint(run)) << 32) | (unsigned)idx)
+                          : ~0ull;
       }
-      run = (j == 0) ? cj : __fmul_rn(run, cj);
-      const int idx = q * gamma + j;
-      if (a_out) a_out[idx] = run;
-      src[merge ? q * P + j : idx] =
-          (run > 0.0f) ? (((unsigned long long)(~__float_as_uint(run)) << 32) | (unsigned)idx)
-                       : ~0ull;
     }
   }
   __syncthreads();
-
-  if (merge) {
-    unsigned long long* in = sh.pre;
-    unsigned long long* out = sh.key;
-    for (int L = P; L < npad; L <<= 1) {
-      for (int i = threadIdx.x; i < npad; i += kSchedThreads) {
-        const unsigned long long k = in[i];
-        const int run0 = i & ~(2 * L - 1);  // first run of the pair
-        const bool odd = (i & L) != 0;
-        const int pos = i & (L - 1);
-        const unsigned long long* other = in + run0 + (odd ? 0 : L);
-        // number of partner keys below k (even run) or not above k (odd run)
-        int lo = 0, len = L;
-        while (len > 0) {
-          const int half = len >> 1;
-          const unsigned long long o = other[lo + half];
-          if (odd ? (o <= k) : (o < k)) {
-            lo += half + 1;
-            len -= half + 1;
-          } else {
-            len = half;
-          }
-        }
-        out[run0 + pos + lo] = k;
-      }
-      __syncthreads();
-      unsigned long long* t = in;
-      in = out;
-      out = t;
-    }
-    if (in != sh.key) {  // the sorted keys belong in sh.key
-      for (int i = threadIdx.x; i < npad; i += kSchedThreads) sh.key[i] = in[i];
-      __syncthreads();
-    }
-  }
-
-  // bitonic sort, ascending (when the merge layout does not fit)
-  for (int k = 2; !merge && k <= npad; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < npad; i += kSchedThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long x = sh.key[i], y = sh.key[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            sh.key[i] = y;
-            sh.key[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
+  const int kstart = runs ? 2 * P : 2;
+  if (npad <= 2048)
+    sched_sort_lds<2>(npad, kstart, sh);
+  else if (npad <= 4096)
+    sched_sort_lds<4>(npad, kstart, sh);
+  else
+    sched_sort_lds<8>(npad, kstart, sh);
 
   // |E| = index of the first padding key
   if (threadIdx.x == 0) *red_i = npad;
@@ -147,15 +255,8 @@ __device__ int sched_sort_scan(int R, int gamma, const float* __restrict__ c, fl
       sh.pre[i] = run;
     }
   }
-  red_u64[threadIdx.x] = (lo < npad) ? run : 0ull;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    const unsigned long long v = (threadIdx.x >= off) ? red_u64[threadIdx.x - off] : 0ull;
-    __syncthreads();
-    red_u64[threadIdx.x] += v;
-    __syncthreads();
-  }
-  const unsigned long long base = threadIdx.x > 0 ? red_u64[threadIdx.x - 1] : 0ull;
+  const unsigned long long incl = block_scan_u64(lo < npad ? run : 0ull, red_u64);
+  const unsigned long long base = incl - (lo < npad ? run : 0ull);
   if (lo < npad)
     for (int i = lo; i < lo + per; ++i) sh.pre[i] += base;
   __syncthreads();
@@ -178,22 +279,31 @@ __device__ int sched_argmax(int R, int nE, const float* __restrict__ sps, int sp
       bi = n;
     }
   }
-  red_d[threadIdx.x] = best;
-  red_i[threadIdx.x] = bi;
-  __syncthreads();
-  for (int off = kSchedThreads / 2; off > 0; off >>= 1) {
-    if (threadIdx.x < off) {
-      const double t2 = red_d[threadIdx.x + off];
-      const int i2 = red_i[threadIdx.x + off];
-      const double t1 = red_d[threadIdx.x];
-      const int i1 = red_i[threadIdx.x];
-      if (t2 > t1 || (t2 == t1 && i2 < i1)) {
-        red_d[threadIdx.x] = t2;
-        red_i[threadIdx.x] = i2;
-      }
+  // wave, then workgroup: the largest Theta, ties to the smaller n
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const double t2 = __shfl_xor(best, o, kWave);
+    const int i2 = __shfl_xor(bi, o, kWave);
+    if (t2 > best || (t2 == best && i2 < bi)) {
+      best = t2;
+      bi = i2;
     }
-    __syncthreads();
   }
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  if (lane == 0) {
+    red_d[wave] = best;
+    red_i[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kSchedThreads / kWave; ++w)
+      if (red_d[w] > best || (red_d[w] == best && red_i[w] < bi)) {
+        best = red_d[w];
+        bi = red_i[w];
+      }
+    red_i[0] = bi;
+  }
+  __syncthreads();
   const int n = red_i[0];
   __syncthreads();
   return n;
@@ -204,15 +314,22 @@ __device__ int sched_first_drop(int R, int nE, const float* __restrict__ sps, in
                                 const SchedShared& sh, int* red_i) {
   if (threadIdx.x == 0) *red_i = 0x7fffffff;
   __syncthreads();
+  int first = 0x7fffffff;  // this thread's first drop (n increases within a thread)
   for (int n = 1 + threadIdx.x; n <= nE; n += kSchedThreads) {
     const double t1 = theta_of(tau_at(R, sh, n), sps[R + n - sps_B0]);
     const double t0 = theta_of(tau_at(R, sh, n - 1), sps[R + n - 1 - sps_B0]);
-    if (!(t1 > t0)) atomicMin(red_i, n);
+    if (!(t1 > t0)) {
+      first = n;
+      break;
+    }
   }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0 && first != 0x7fffffff) atomicMin(red_i, first);
   __syncthreads();
-  const int first = *red_i;
+  const int f = *red_i;
   __syncthreads();
-  return first == 0x7fffffff ? nE : first - 1;
+  return f == 0x7fffffff ? nE : f - 1;
 }
 
 __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(
