@@ -216,7 +216,8 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
   const int32_t tprev = checked_token(prev[(size_t)q * prev_stride], V, status);
   const T* e = W1 + (size_t)tprev * r;
 
-  // first level: normaliser and winning block over the ranges' partials
+  // first level: normaliser and winning block over the ranges' partials (per wave: the
+  // largest reference, then one rescale per lane and a plain sum)
   float M = -INFINITY, S = 0.0f, G = -INFINITY;
   int Bk = 0x7fffffff;
   for (int i = tid; i < nranges; i += kCombineThreads) {
@@ -229,10 +230,11 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
       Bk = pb;
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(M, o, kWave), s2 = __shfl_xor(S, o, kWave);
-    lse_merge(M, S, m2, s2);
+  {
+    const float Mw = wave_max(M);
+    S = (M == -INFINITY) ? 0.0f : S * __expf(M - Mw);
+    S = wave_sum(S);
+    M = Mw;
   }
   wave_argmax(G, Bk);
   if (lane == 0) red[wave] = make_float4(M, S, G, __int_as_float(Bk));
@@ -259,6 +261,7 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
   const int v = Bk * kVB + lane;
   const float u = (wave == 0 && v < V) ? ld<T>(U, (size_t)q * gamma * V + (size_t)(k - 1) * V + v) : 0.0f;
   float part = 0.0f;
+  float gn = 0.0f;  // in-block Gumbel noise (wave 0), formed while the block's rows load
   if (v < V) {
     const T* wr = W2t + (size_t)v * r;
     // r <= 256: at most 8 chunks per wave, all loads in flight together
@@ -274,6 +277,7 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
         ld8<T>(e + ch * 8, bv[it]);
       }
     }
+    if (wave == 0) gn = gumbel_of(Rng(seed, cycle).word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v));
 #pragma unroll
     for (int it = 0; it < 8; ++it)
       if (wave + kWaves * it < r / 8)
@@ -300,9 +304,7 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) acc += dotp[i][lane];
     const float l = (v < V) ? u + acc : -INFINITY;
-    const Rng rng(seed, cycle);
-    float score = (v < V) ? l + gumbel_of(rng.word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v))
-                          : -INFINITY;
+    float score = (v < V) ? l + gn : -INFINITY;
     int idx = v;
     wave_argmax(score, idx);
     const float lx = __shfl(l, idx - Bk * kVB, kWave);
