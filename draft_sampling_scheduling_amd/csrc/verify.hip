@@ -223,12 +223,14 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
     }
     mx = wave_max(mx);
     const float ref = mx == -INFINITY ? 0.0f : mx * kLog2e;
-    // random words of the window's 16 block groups: lane l < 16 holds group bw/4 + l
-    uint4 wds = make_uint4(0, 0, 0, 0);
-    if (bonus)
-      wds = rng.block(kStreamBonusBlk, (uint32_t)q, (uint32_t)j, (uint32_t)((bw >> 2) + (lane & 15)));
-    float S = 0.0f, G = -INFINITY;
-    int Bk = 0x7fffffff;
+    // bonus row: lane l owns block bw + l (its Gumbel noise, and its sum gathered from the
+    // chunk that holds it)
+    float gb = 0.0f;
+    if (bonus) {
+      const uint32_t b = (uint32_t)(bw + lane);
+      gb = gumbel_of(pick_word(rng.block(kStreamBonusBlk, (uint32_t)q, (uint32_t)j, b >> 2), b & 3u));
+    }
+    float S = 0.0f, bmine = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float x[8];
@@ -238,18 +240,18 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
       for (int e = 0; e < 8; ++e) sb += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -ref));
       S += sb;
       if (bonus) {
-        const float bs = sum8(sb);
-        const int m = lane >> 3, b = bw + 8 * c + m;
-        const int src = 2 * c + (m >> 2);  // lane holding group b / 4
-        const uint4 gw = make_uint4(__shfl(wds.x, src, kWave), __shfl(wds.y, src, kWave),
-                                    __shfl(wds.z, src, kWave), __shfl(wds.w, src, kWave));
-        const bool lead = (lane & 7) == 0 && b < nblocks && bs > 0.0f;
-        const float Gb = lead ? (ref + __builtin_amdgcn_logf(bs)) * kLn2 + gumbel_of(pick_word(gw, (uint32_t)b & 3u))
-                              : -INFINITY;
-        if (Gb > G) {  // blocks visited in increasing order per lane
-          G = Gb;
-          Bk = b;
-        }
+        // block 8c + m sums over lanes 8m .. 8m+7; lane 8c + m takes it from lane 8m
+        const float bs = __shfl(sum8(sb), 8 * (lane & 7), kWave);
+        bmine = (lane >> 3) == c ? bs : bmine;
+      }
+    }
+    float G = -INFINITY;
+    int Bk = 0x7fffffff;
+    if (bonus) {
+      const int b = bw + lane;
+      if (b < nblocks && bmine > 0.0f) {
+        G = (ref + __builtin_amdgcn_logf(bmine)) * kLn2 + gb;
+        Bk = b;
       }
     }
     S = wave_sum(S);
