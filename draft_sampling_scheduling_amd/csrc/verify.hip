@@ -20,6 +20,8 @@
 //           (stream 3);
 //   final   one workgroup of four waves per request: c* for every verified row, then the
 //           second level of the correction (stream 4) or of the bonus (stream 6).
+#include <type_traits>
+
 #include "dev.h"
 #include "host.h"
 #include "sweep.h"
@@ -205,55 +207,69 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
     const int q = info.x, j = info.y;
     const bool bonus = info.z != 0;
     const int bw = tile * kLseThreads + wave * kWave;  // first block of this wave
-    // chunk c widened on demand (twice: for the max, then for the sums), which keeps the
-    // register footprint at two raw items
-    auto chunk = [&](int c, float (&x)[8]) {
-      cur.widen_one(c, x);
-      const int v = (bw + 8 * c + (lane >> 3)) * kVB + 8 * (lane & 7);
+    // The item's arithmetic, with ids past V masked only in a window that reaches the end
+    // of the row (MASK); every other window skips the per-element selects.
+    float mx, ref, S, G;
+    int Bk;
+    auto item_math = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      // chunk c widened on demand (twice: for the max, then for the sums), which keeps the
+      // register footprint at two raw items
+      auto chunk = [&](int c, float (&x)[8]) {
+        cur.widen_one(c, x);
+        if (MASK) {
+          const int v = (bw + 8 * c + (lane >> 3)) * kVB + 8 * (lane & 7);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = v < V ? x[e] : -INFINITY;
-    };
-    float mx = -INFINITY;
+          for (int e = 0; e < 8; ++e) x[e] = v < V ? x[e] : -INFINITY;
+        }
+      };
+      mx = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float x[8];
-      chunk(c, x);
+      for (int c = 0; c < 8; ++c) {
+        float x[8];
+        chunk(c, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    }
-    mx = wave_max(mx);
-    const float ref = mx == -INFINITY ? 0.0f : mx * kLog2e;
-    // bonus row: lane l owns block bw + l (its Gumbel noise, and its sum gathered from the
-    // chunk that holds it)
-    float gb = 0.0f;
-    if (bonus) {
-      const uint32_t b = (uint32_t)(bw + lane);
-      gb = gumbel_of(pick_word(rng.block(kStreamBonusBlk, (uint32_t)q, (uint32_t)j, b >> 2), b & 3u));
-    }
-    float S = 0.0f, bmine = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float x[8];
-      chunk(c, x);
-      float sb = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sb += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -ref));
-      S += sb;
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[e]);
+      }
+      mx = wave_max(mx);
+      ref = mx == -INFINITY ? 0.0f : mx * kLog2e;
+      // bonus row: lane l owns block bw + l (its Gumbel noise, and its sum gathered from
+      // the chunk that holds it)
+      float gb = 0.0f;
       if (bonus) {
-        // block 8c + m sums over lanes 8m .. 8m+7; lane 8c + m takes it from lane 8m
-        const float bs = __shfl(sum8(sb), 8 * (lane & 7), kWave);
-        bmine = (lane >> 3) == c ? bs : bmine;
+        const uint32_t b = (uint32_t)(bw + lane);
+        gb = gumbel_of(pick_word(rng.block(kStreamBonusBlk, (uint32_t)q, (uint32_t)j, b >> 2), b & 3u));
       }
-    }
-    float G = -INFINITY;
-    int Bk = 0x7fffffff;
-    if (bonus) {
-      const int b = bw + lane;
-      if (b < nblocks && bmine > 0.0f) {
-        G = (ref + __builtin_amdgcn_logf(bmine)) * kLn2 + gb;
-        Bk = b;
+      float bmine = 0.0f;
+      S = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float x[8];
+        chunk(c, x);
+        float sb = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sb += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -ref));
+        S += sb;
+        if (bonus) {
+          // block 8c + m sums over lanes 8m .. 8m+7; lane 8c + m takes it from lane 8m
+          const float bs = __shfl(sum8(sb), 8 * (lane & 7), kWave);
+          bmine = (lane >> 3) == c ? bs : bmine;
+        }
       }
-    }
+      G = -INFINITY;
+      Bk = 0x7fffffff;
+      if (bonus) {
+        const int b = bw + lane;
+        if (b < nblocks && bmine > 0.0f) {
+          G = (ref + __builtin_amdgcn_logf(bmine)) * kLn2 + gb;
+          Bk = b;
+        }
+      }
+    };
+    if ((bw + kWave) * kVB <= V)
+      item_math(std::false_type{});
+    else
+      item_math(std::true_type{});
     S = wave_sum(S);
     float M = mx == -INFINITY ? -INFINITY : ref * kLn2;
     wave_argmax(G, Bk);
