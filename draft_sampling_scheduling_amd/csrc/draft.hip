@@ -29,11 +29,20 @@ __global__ void __launch_bounds__(256) conf_h_kernel(int rows, int d, const T* _
   if (row >= rows) return;
   const T* hr = h + (size_t)row * d;
   float acc = 0.0f;
-  for (int i = lane * 8; i < d; i += 64 * 8) {
-    float x[8];
-    ld8<T>(hr + i, x);
+  // four 8-element chunks per lane in flight together (clamped addresses, masked sums)
+  for (int i0 = lane * 8; i0 < d; i0 += 4 * 64 * 8) {
+    float x[4][8], wv[4][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(w[i + j], x[j], acc);
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 64 * 8 < d ? i0 + u * 64 * 8 : i0;
+      ld8<T>(hr + i, x[u]);
+      ld8<float>(w + i, wv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * 64 * 8 < d)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = fmaf(wv[u][j], x[u][j], acc);
   }
   acc = wave_sum(acc);
   if (lane == 0) zh[row] = acc;
