@@ -20,10 +20,34 @@ namespace dspark {
 // ---------------------------------------------------------------------------------------
 // w_h . h_k for every (request, position): one wave per row of h
 // ---------------------------------------------------------------------------------------
+// the sweep's packed B rows for step 1: row q's chunk j = W1[x0[q]][8j .. 8j+8)
+__device__ __forceinline__ void bpack_gather_one(int gid, int R, int r, int V,
+                                                 const int32_t* __restrict__ x0,
+                                                 const uint16_t* __restrict__ W1, uint4* bpack,
+                                                 int32_t* status) {
+  const int cpr = r / 8;  // chunks per row
+  if (gid >= R * cpr) return;
+  const int q = gid / cpr, j = gid - q * cpr;
+  const int32_t t = checked_token(x0[q], V, status);
+  bpack[bpack_index(q, j, r / 16)] = reinterpret_cast<const uint4*>(W1 + (size_t)t * r)[j];
+}
+
+__global__ void __launch_bounds__(256) bpack_gather_kernel(int R, int r, int V,
+                                                           const int32_t* __restrict__ x0,
+                                                           const uint16_t* __restrict__ W1,
+                                                           uint4* bpack, int32_t* status) {
+  bpack_gather_one(blockIdx.x * 256 + threadIdx.x, R, r, V, x0, W1, bpack, status);
+}
+
 template <class T>
 __global__ void __launch_bounds__(256) conf_h_kernel(int rows, int d, const T* __restrict__ h,
                                                      const float* __restrict__ w,
-                                                     float* __restrict__ zh) {
+                                                     float* __restrict__ zh, int R, int r,
+                                                     int V, const int32_t* __restrict__ x0,
+                                                     const uint16_t* __restrict__ W1,
+                                                     uint4* bpack, int32_t* status) {
+  // the step-1 packed B rows ride along (bf16 Markov head only)
+  if (bpack) bpack_gather_one(blockIdx.x * 256 + threadIdx.x, R, r, V, x0, W1, bpack, status);
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -61,6 +85,7 @@ struct DraftSweepParams {
   int prev_stride;
   const uint16_t* W1;    // Markov B rows: W1[x_{k-1}]
   const float* orow;     // RNN B rows: tanh(W_o z_k), [R][r] float
+  const uint4* bpack;    // Markov B rows W1[x_{k-1}] in the sweep's packed order
   int r;
   uint32_t k;            // position, 1-based
   uint64_t seed, cycle;
@@ -92,6 +117,7 @@ struct DraftEpi {
     const int32_t t = checked_token(p.prev[(size_t)row * p.prev_stride], p.V, p.status);
     return p.W1 + (size_t)t * p.r;
   }
+  __device__ static const uint4* bpack(const Params& p) { return RNN ? nullptr : p.bpack; }
   __device__ static const uint16_t* sbase(const Params& p, int) { return p.U; }
   __device__ static uint32_t srow(const Params& p, int, int row) {
     return (uint32_t)((size_t)row * p.ustride);
@@ -214,11 +240,12 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
     const float* __restrict__ zh, const int32_t* prev, int prev_stride,
     const float* __restrict__ orow, const float4* __restrict__ partials, int nranges,
     uint32_t k, uint64_t seed, uint64_t cycle, int32_t* x, float* c, float* zout, float* lse,
-    float* logit_x, void* bias_rows, int32_t* status) {
+    float* logit_x, void* bias_rows, uint4* bpack, int32_t* status) {
   constexpr int kWaves = kCombineThreads / kWave;
   __shared__ float4 red[kWaves];
   __shared__ float dotp[kWaves][kWave];
   __shared__ float zred[kWaves];
+  __shared__ int s_pick;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t rk = (size_t)q * gamma + (k - 1);
   // the previous token's embedding row (independent of the partials)
@@ -332,7 +359,16 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
       if (zout) zout[rk] = z;
       lse[rk] = M + __logf(S);
       logit_x[rk] = lx;
+      s_pick = idx;
     }
+  }
+  if (sizeof(T) == 2 && !RNN && bpack) {
+    // W1[x_k] in the next sweep's packed order, one 16-byte chunk per thread
+    __syncthreads();
+    const int pick = s_pick;
+    if (tid < r / 8)
+      bpack[bpack_index(q, tid, r / 16)] =
+          reinterpret_cast<const uint4*>(W1 + (size_t)pick * r)[tid];
   }
 }
 
@@ -441,6 +477,7 @@ static int nranges_for(int V, int ngroups) {
 struct DraftWs {
   float* zh;
   float4* partials;
+  uint4* bpack;  // Markov: the next sweep's B rows in packed order
   float* Gh;
   float* s;
   float* orow;
@@ -457,6 +494,8 @@ static DraftWs carve_draft(void* ws, int R, int gamma, int V, int r, int d, bool
     w.Gh = cv.take<float>((size_t)R * gamma * 3 * r);
     w.s = cv.take<float>((size_t)R * r);
     w.orow = cv.take<float>((size_t)R * r);
+  } else {
+    w.bpack = cv.take<uint4>((size_t)bpack_rows(R) * r / 8);
   }
   (void)d;
   w.bytes = cv.bytes();
@@ -478,10 +517,16 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
   constexpr bool BF = sizeof(T) == 2;
   const int rows = R * gamma;
 
+  uint4* bpack = (BF && !rnn) ? ws.bpack : nullptr;
+  const uint16_t* W1b = reinterpret_cast<const uint16_t*>(W1_);
   if (d > 0) {
-    conf_h_kernel<T><<<(rows + 3) / 4, 256, 0, stream>>>(rows, d, h, w, ws.zh);
+    conf_h_kernel<T><<<(rows + 3) / 4, 256, 0, stream>>>(rows, d, h, w, ws.zh, R, r, V, x0, W1b,
+                                                         bpack, status);
   } else {
     fill_kernel<<<(rows + 255) / 256, 256, 0, stream>>>(ws.zh, (size_t)rows, 0.0f);
+    if (bpack)
+      bpack_gather_kernel<<<(R * (r / 8) + 255) / 256, 256, 0, stream>>>(R, r, V, x0, W1b,
+                                                                          bpack, status);
   }
   if (rnn) {
     const int r3 = 3 * r, K = 2 * r + d;
@@ -531,6 +576,7 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
       p.prev_stride = ps;
       p.W1 = reinterpret_cast<const uint16_t*>(W1);
       p.orow = ws.orow;
+      p.bpack = bpack;
       p.r = r;
       p.k = (uint32_t)k;
       p.seed = seed;
@@ -555,11 +601,13 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
     if (rnn)
       draft_combine_kernel<T, true><<<R, kCombineThreads, 0, stream>>>(
           R, gamma, V, r, d, U, W1, W2t, w, temps, ws.zh, prev, ps, ws.orow, ws.partials,
-          nranges, (uint32_t)k, seed, cycle, x, c, z, lse, logit_x, bias_rows, status);
+          nranges, (uint32_t)k, seed, cycle, x, c, z, lse, logit_x, bias_rows, nullptr,
+          status);
     else
       draft_combine_kernel<T, false><<<R, kCombineThreads, 0, stream>>>(
           R, gamma, V, r, d, U, W1, W2t, w, temps, ws.zh, prev, ps, nullptr, ws.partials,
-          nranges, (uint32_t)k, seed, cycle, x, c, z, lse, logit_x, bias_rows, status);
+          nranges, (uint32_t)k, seed, cycle, x, c, z, lse, logit_x, bias_rows,
+          k < gamma ? bpack : nullptr, status);
   }
   return launch_status();
 }

@@ -86,6 +86,16 @@ __device__ __forceinline__ void range_blocks(const SweepGeom& g, int range, int&
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// 16-byte chunk index of row q's chunk j (elements 8j .. 8j+7) in the packed B layout for
+// r = 16 * nks: 32-row blocks of nks * 64 chunks, k-step major, lane (n, h) minor
+__host__ __device__ __forceinline__ size_t bpack_index(int q, int j, int nks) {
+  return (size_t)(q >> 5) * (size_t)(nks * 64) + (size_t)((j >> 1) * 64 + (j & 1) * 32 + (q & 31));
+}
+// rows the packed B buffer holds for R rows (whole row groups, so every wave's block exists)
+__host__ __device__ __forceinline__ int bpack_rows(int R) {
+  return (R + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
+}
+
 // hi/lo bf16 split of 8 floats: x = hi + lo to ~16 significant bits
 __device__ __forceinline__ void split8(const float (&x)[8], uint4& hi, uint4& lo) {
   uint32_t h[4], l[4];
@@ -170,6 +180,10 @@ __device__ __forceinline__ void half_lse(float& m, float& s) {
 //   static bool group_live(const Params&, int row0)         rows exist in this group
 //   static int  nrows(const Params&)                        exact row count (device)
 //   static const void* brow(const Params&, int row)         B row of a live row
+//   static const uint4* bpack(const Params&)                 the B rows in packed order,
+//        or null (then brow is used): for row group g, wave w and k-step ks, lane l's
+//        16-byte fragment sits at chunk (4g + w) * NKS * 64 + ks * 64 + l, so each k-step
+//        is one coalesced 1 KB load per wave (see bpack_index)
 //   static const uint16_t* sbase(const Params&, int s)      stream s array
 //   static uint32_t srow(const Params&, int s, int row)     element offset of a live row
 //   static void init(const Params&, State&, int row)        row < 0: not a live row
@@ -349,25 +363,33 @@ __global__ void __launch_bounds__(kSweepThreads, 2)
     // first step waits for one tile rather than D
     if (t0 < t1) issue(t0, 0);
 
-    // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row
-    const void* brow = live ? Epi::brow(ep, row) : nullptr;
+    // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row; from the packed
+    // copy when the epilogue has one (coalesced; rows past the end read padding)
+    const uint4* bpk = SPLIT ? nullptr : Epi::bpack(ep);
+    if (bpk) {
+      const uint4* src = bpk + (size_t)(group_row0 / 32 + wave) * (NKS * kWave) + lane;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      uint4 hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
-      if (live) {
-        const int k0 = 16 * ks + 8 * h;
-        if (SPLIT) {
-          const float* p = reinterpret_cast<const float*>(brow) + k0;
-          const float4 a = *reinterpret_cast<const float4*>(p);
-          const float4 c = *reinterpret_cast<const float4*>(p + 4);
-          const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-          split8(x, hi, lo);
-        } else {
-          hi = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(brow) + k0);
+      for (int ks = 0; ks < NKS; ++ks) bh[ks] = as_bf16x8(src[ks * kWave]);
+    } else {
+      const void* brow = live ? Epi::brow(ep, row) : nullptr;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint4 hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
+        if (live) {
+          const int k0 = 16 * ks + 8 * h;
+          if (SPLIT) {
+            const float* p = reinterpret_cast<const float*>(brow) + k0;
+            const float4 a = *reinterpret_cast<const float4*>(p);
+            const float4 c = *reinterpret_cast<const float4*>(p + 4);
+            const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+            split8(x, hi, lo);
+          } else {
+            hi = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(brow) + k0);
+          }
         }
+        bh[ks] = as_bf16x8(hi);
+        if (SPLIT) bl[SPLIT ? ks : 0] = as_bf16x8(lo);
       }
-      bh[ks] = as_bf16x8(hi);
-      if (SPLIT) bl[SPLIT ? ks : 0] = as_bf16x8(lo);
     }
     Epi::init(ep, st, live ? row : -1);
 

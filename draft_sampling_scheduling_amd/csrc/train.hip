@@ -45,6 +45,7 @@ struct TrainRowsBase {
   __device__ static const void* brow(const Params& p, int row) {
     return p.W1 + (size_t)train_prev(p, row) * p.r;
   }
+  __device__ static const uint4* bpack(const Params&) { return nullptr; }
   __device__ static const uint16_t* sbase(const Params& p, int s) {
     return s == 0 ? p.U : p.target;
   }

@@ -397,6 +397,7 @@ struct VerifyEpi {
     if (SPLIT) return static_cast<const float*>(p.brows) + off;
     return static_cast<const uint16_t*>(p.brows) + off;
   }
+  __device__ static const uint4* bpack(const Params&) { return nullptr; }
   __device__ static const uint16_t* sbase(const Params& p, int s) { return s == 0 ? p.U : p.target; }
   __device__ static uint32_t srow(const Params& p, int s, int row) {
     const int2 qj = p.ws.rowB[row];
