@@ -27,6 +27,7 @@ struct TrainSweepParams {
   float4* part1;           // [rows][nranges]: (ref_q ln2, S_q, ref_p ln2, S_p)
   float* part2;            // [rows][nranges]: partial sum |p - q|
   const float2* lse;       // [rows]: (lse_q, lse_p) for sweep 2
+  const uint4* bpack;      // W1[x*_{k-1}] of every row in the sweep's packed order
   int32_t* status;
 };
 
@@ -45,7 +46,7 @@ struct TrainRowsBase {
   __device__ static const void* brow(const Params& p, int row) {
     return p.W1 + (size_t)train_prev(p, row) * p.r;
   }
-  __device__ static const uint4* bpack(const Params&) { return nullptr; }
+  __device__ static const uint4* bpack(const Params& p) { return p.bpack; }
   __device__ static const uint16_t* sbase(const Params& p, int s) {
     return s == 0 ? p.U : p.target;
   }
@@ -145,6 +146,17 @@ struct TrainTvEpi : TrainRowsBase {
     p.part2[(size_t)row * p.nranges + range] = tv;
   }
 };
+
+// the B rows of both sweeps, W1[x*_{k-1}] per row, in the sweep's packed order
+__global__ void __launch_bounds__(256) train_pack_kernel(TrainSweepParams p, uint4* bpack) {
+  const int cpr = p.r / 8;
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  if (gid >= p.nrows * cpr) return;
+  const int row = gid / cpr, ch = gid - row * cpr;
+  const int32_t t = train_prev(p, row);
+  bpack[bpack_index(row, ch, p.r / 16)] =
+      reinterpret_cast<const uint4*>(p.W1 + (size_t)t * p.r)[ch];
+}
 
 constexpr int kTrainMergeRows = 4;  // one wave per row
 
@@ -251,6 +263,7 @@ __global__ void __launch_bounds__(kTrainFinalThreads) train_final_kernel(
 }
 
 struct TrainWs {
+  uint4* bpack;
   float4* part1;
   float* part2;
   float2* lse;
@@ -270,6 +283,7 @@ inline int train_nranges(int V) {
 inline TrainWs train_carve(void* base, int rows, int nranges) {
   Carve cv(base);
   TrainWs w;
+  w.bpack = cv.take<uint4>((size_t)bpack_rows(rows) * 32);  // r <= 256: 32 chunks per row
   w.part1 = cv.take<float4>((size_t)rows * nranges);
   w.part2 = cv.take<float>((size_t)rows * nranges);
   w.lse = cv.take<float2>((size_t)rows);
@@ -331,7 +345,9 @@ int dspark_train_forward(int R, int gamma, int V, int r, int d, dspark_dtype dt,
   p.part2 = wsl.part2;
   p.lse = wsl.lse;
   p.status = dev_status;
+  p.bpack = wsl.bpack;
   const SweepGeom g = make_geom(rows, V, r, static_cast<const uint16_t*>(W2t), nranges);
+  train_pack_kernel<<<(rows * (r / 8) + 255) / 256, 256, 0, stream>>>(p, wsl.bpack);
   launch_sweep<false, TrainLseEpi>(g, p, stream);
   train_merge_kernel<<<(rows + kTrainMergeRows - 1) / kTrainMergeRows, 64 * kTrainMergeRows, 0,
                        stream>>>(p, d, static_cast<const uint16_t*>(h),

@@ -43,10 +43,11 @@ struct VerifyWs {
   float2* bonus;   // [R] (best G, block) of the bonus row
   int* jstar;      // [R] first rejected position, 0 = none
   float4* partials;  // [R*gamma][nranges]: (sum |p-q|, best G, block, residual mass)
+  uint4* bpack;      // list-B bias rows (bf16) in the sweep's packed order, or null
   size_t bytes;
 };
 
-static VerifyWs carve_verify(void* ws, int R, int gamma, int V) {
+static VerifyWs carve_verify(void* ws, int R, int gamma, int V, int r) {
   Carve cv(ws);
   VerifyWs w{};
   w.hdr = cv.take<int>(4);
@@ -60,6 +61,7 @@ static VerifyWs carve_verify(void* ws, int R, int gamma, int V) {
   w.jstar = cv.take<int>((size_t)R);
   const int nblocks = (V + kVB - 1) / kVB;
   w.partials = cv.take<float4>((size_t)R * gamma * (nblocks < kMaxRanges ? nblocks : kMaxRanges));
+  w.bpack = cv.take<uint4>((size_t)bpack_rows(R * gamma) * r / 8);
   w.bytes = cv.bytes();
   return w;
 }
@@ -299,10 +301,30 @@ template <class T>
 __global__ void __launch_bounds__(64) verify_decide_kernel(
     int R, int gamma, int V, const T* __restrict__ target, const int32_t* __restrict__ x,
     const float* __restrict__ lse, const float* __restrict__ logit_x, const int32_t* ell,
-    VerifyWs ws, uint64_t seed, uint64_t cycle, int32_t* n_acc, int32_t* y, int32_t* status) {
+    VerifyWs ws, uint64_t seed, uint64_t cycle, int32_t* n_acc, int32_t* y, int32_t* status,
+    const uint16_t* __restrict__ brows, int r) {
   // one wave per request; lane j - 1 tests position j (gamma <= 64)
   const int q = blockIdx.x, lane = threadIdx.x, j = lane + 1;
   const int L = clamp_len(ell[q], gamma);
+  if (brows) {
+    // the sweep's B rows for this request's list-B rows, in its packed order: half-waves
+    // take one row each, lane & 31 its 16-byte chunk; four row pairs in flight per pass
+    const int ob = ws.offB[q], cpr = r / 8, ch = lane & 31;
+    for (int j0 = 0; j0 < L; j0 += 8) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int jr = j0 + 2 * u + (lane >> 5);
+        const int jc = jr < L ? jr : 0;
+        v[u] = reinterpret_cast<const uint4*>(brows + ((size_t)q * gamma + jc) * r)[ch < cpr ? ch : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int jr = j0 + 2 * u + (lane >> 5);
+        if (jr < L && ch < cpr) ws.bpack[bpack_index(ob + jr, ch, r / 16)] = v[u];
+      }
+    }
+  }
   // target normaliser of rows 1..L+1 from their lse items (in item order, so ties keep the
   // lowest block); the bonus row's winning block
   const int tiles = lse_tiles(V);
@@ -397,7 +419,7 @@ struct VerifyEpi {
     if (SPLIT) return static_cast<const float*>(p.brows) + off;
     return static_cast<const uint16_t*>(p.brows) + off;
   }
-  __device__ static const uint4* bpack(const Params&) { return nullptr; }
+  __device__ static const uint4* bpack(const Params& p) { return SPLIT ? nullptr : p.ws.bpack; }
   __device__ static const uint16_t* sbase(const Params& p, int s) { return s == 0 ? p.U : p.target; }
   __device__ static uint32_t srow(const Params& p, int s, int row) {
     const int2 qj = p.ws.rowB[row];
@@ -732,8 +754,11 @@ static int verify_run(int R, int gamma, int V, int r, const void* target_, const
     verify_lse_kernel<T><<<items < cap ? items : cap, kLseThreads, 0, stream>>>(
         R, gamma, V, target, ell, ws, seed, cycle);
   }
-  verify_decide_kernel<T><<<R, 64, 0, stream>>>(
-      R, gamma, V, target, x, lse, logit_x, ell, ws, seed, cycle, n_acc, y, status);
+  // bf16 bias rows go to the sweep in its packed order (float ones, split hi + lo, do not)
+  const uint16_t* brows16 =
+      (BF && !SPLIT) ? reinterpret_cast<const uint16_t*>(brows_) : nullptr;
+  verify_decide_kernel<T><<<R, 64, 0, stream>>>(R, gamma, V, target, x, lse, logit_x, ell, ws,
+                                                seed, cycle, n_acc, y, status, brows16, r);
 
   const int rows_max = R * gamma;
   int nranges;
@@ -777,7 +802,7 @@ extern "C" {
 
 size_t dspark_verify_workspace_bytes(int R, int gamma, int V, int r) {
   if (!dspark::dims_ok(R, gamma, V, r, 0)) return 0;
-  return dspark::carve_verify(nullptr, R, gamma, V).bytes;
+  return dspark::carve_verify(nullptr, R, gamma, V, r).bytes;
 }
 
 int dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, const void* target,
@@ -799,9 +824,9 @@ int dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, const void* t
   // the bf16 sweep addresses U and target rows with 32-bit byte offsets
   if (dt == DSPARK_BF16 && (uint64_t)R * (gamma + 1) * V * 2 >= ((uint64_t)1 << 32))
     return DSPARK_EINVAL;
-  if (ws_bytes < carve_verify(nullptr, R, gamma, V).bytes) return DSPARK_EWORKSPACE;
+  if (ws_bytes < carve_verify(nullptr, R, gamma, V, r).bytes) return DSPARK_EWORKSPACE;
   if (!aligned16(ws)) return DSPARK_EINVAL;
-  const VerifyWs lay = carve_verify(ws, R, gamma, V);
+  const VerifyWs lay = carve_verify(ws, R, gamma, V, r);
   if (dt == DSPARK_BF16) {
     if (bias_dt == DSPARK_BF16)
       return verify_run<uint16_t, uint16_t>(R, gamma, V, r, target, U, W2t, bias_rows, x, lse,
