@@ -565,7 +565,9 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
       rnn_step_kernel<T><<<R, 256, sh, stream>>>(R, gamma, V, r, d, W1, Wg, ws.Gh, prev, ps,
                                                  (uint32_t)k, ws.s, ws.orow, status);
     }
-    if (evb && evb[k - 1]) (void)hipEventRecord(evb[k - 1], stream);
+    // the timed variant: the bf16 sweep's dispatch timestamps its own start and end
+    hipEvent_t e0 = (evb && eve) ? evb[k - 1] : nullptr, e1 = (evb && eve) ? eve[k - 1] : nullptr;
+    if (!BF && e0 && e1) (void)hipEventRecord(e0, stream);
     if (BF) {
       DraftSweepParams p{};
       p.U = reinterpret_cast<const uint16_t*>(U) + (size_t)(k - 1) * V;
@@ -585,9 +587,9 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
       p.nranges = nranges;
       p.status = status;
       if (rnn)
-        launch_sweep<true, DraftEpi<true>>(g, p, stream);
+        launch_sweep<true, DraftEpi<true>>(g, p, stream, e0, e1);
       else
-        launch_sweep<false, DraftEpi<false>>(g, p, stream);
+        launch_sweep<false, DraftEpi<false>>(g, p, stream, e0, e1);
     } else {
       const int nblocks = (V + kVB - 1) / kVB;
       dim3 grid(nranges, R);
@@ -597,7 +599,7 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
           reinterpret_cast<const float*>(W2t), (uint32_t)k, seed, cycle, ws.partials, nranges,
           nblocks, status);
     }
-    if (eve && eve[k - 1]) (void)hipEventRecord(eve[k - 1], stream);
+    if (!BF && e0 && e1) (void)hipEventRecord(e1, stream);
     if (rnn)
       draft_combine_kernel<T, true><<<R, kCombineThreads, 0, stream>>>(
           R, gamma, V, r, d, U, W1, W2t, w, temps, ws.zh, prev, ps, ws.orow, ws.partials,

@@ -26,6 +26,8 @@
 //     two 16-byte LDS reads per streamed operand.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "dev.h"
 
 namespace dspark {
@@ -500,8 +502,11 @@ inline size_t device_max_lds() {
   return (size_t)cache[dev];
 }
 
+// ev0/ev1 (both or neither): events the dispatch itself timestamps at the kernel's start
+// and end, so their elapsed time is the kernel's own duration
 template <int NKS, bool SPLIT, int NSTAGE, class Epi>
-inline void launch_sweep_nks(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s) {
+inline void launch_sweep_nks(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s,
+                             hipEvent_t ev0, hipEvent_t ev1) {
   auto kern = sweep_kernel<NKS, SPLIT, NSTAGE, Epi>;
   const size_t sh = sweep_lds_bytes(g.r, Epi::kStreams, NSTAGE);
   static bool attr = false;
@@ -510,27 +515,33 @@ inline void launch_sweep_nks(const SweepGeom& g, const typename Epi::Params& p, 
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
     attr = true;
   }
-  kern<<<g.nranges * g.gsplit, kSweepThreads, sh, s>>>(g, p);
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL(kern, dim3(g.nranges * g.gsplit), dim3(kSweepThreads), (uint32_t)sh, s,
+                          ev0, ev1, 0, g, p);
+  else
+    kern<<<g.nranges * g.gsplit, kSweepThreads, sh, s>>>(g, p);
 }
 
 // launch with NKS = r / 16 fixed at compile time (r in {16, 32, 64, 128, 256}) and three
 // pipeline stages when two workgroups still fit one CU's LDS, else two
 template <int NKS, bool SPLIT, class Epi>
-inline void launch_sweep_stages(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s) {
+inline void launch_sweep_stages(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s,
+                                hipEvent_t ev0, hipEvent_t ev1) {
   if (2 * sweep_lds_bytes(g.r, Epi::kStreams, 3) <= device_max_lds())
-    launch_sweep_nks<NKS, SPLIT, 3, Epi>(g, p, s);
+    launch_sweep_nks<NKS, SPLIT, 3, Epi>(g, p, s, ev0, ev1);
   else
-    launch_sweep_nks<NKS, SPLIT, 2, Epi>(g, p, s);
+    launch_sweep_nks<NKS, SPLIT, 2, Epi>(g, p, s, ev0, ev1);
 }
 
 template <bool SPLIT, class Epi>
-inline void launch_sweep(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s) {
+inline void launch_sweep(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s,
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
   switch (g.nks) {
-    case 1: launch_sweep_stages<1, SPLIT, Epi>(g, p, s); break;
-    case 2: launch_sweep_stages<2, SPLIT, Epi>(g, p, s); break;
-    case 4: launch_sweep_stages<4, SPLIT, Epi>(g, p, s); break;
-    case 8: launch_sweep_stages<8, SPLIT, Epi>(g, p, s); break;
-    default: launch_sweep_stages<16, SPLIT, Epi>(g, p, s);
+    case 1: launch_sweep_stages<1, SPLIT, Epi>(g, p, s, ev0, ev1); break;
+    case 2: launch_sweep_stages<2, SPLIT, Epi>(g, p, s, ev0, ev1); break;
+    case 4: launch_sweep_stages<4, SPLIT, Epi>(g, p, s, ev0, ev1); break;
+    case 8: launch_sweep_stages<8, SPLIT, Epi>(g, p, s, ev0, ev1); break;
+    default: launch_sweep_stages<16, SPLIT, Epi>(g, p, s, ev0, ev1);
   }
 }
 

@@ -117,10 +117,12 @@ int dspark_draft_markov(int R, int gamma, int V, int r, int d, dspark_dtype dt,
                         size_t ws_bytes, hipStream_t stream);
 
 /* Benchmark hook: exactly dspark_draft_markov, and additionally records ev_begin[k-1] and
- * ev_end[k-1] (events the caller created, gamma of each) on `stream` immediately before
- * and after the vocabulary-sweep kernel of draft position k, so that kernel can be timed
- * alone with hipEventElapsedTime; a NULL entry (in both arrays) skips that position.
- * DSPARK_EINVAL if either array is NULL. */
+ * ev_end[k-1] (events the caller created, gamma of each) at the start and end of the
+ * vocabulary-sweep kernel of draft position k, so that kernel can be timed alone with
+ * hipEventElapsedTime: with bf16 operands the events are attached to the sweep's own
+ * dispatch (its start and completion timestamps); with float operands they are recorded
+ * on `stream` immediately before and after it.  A NULL entry (in either array) skips that
+ * position.  DSPARK_EINVAL if either array is NULL. */
 int dspark_draft_markov_timed(int R, int gamma, int V, int r, int d, dspark_dtype dt,
                               const void *U, const void *h, const void *W1, const void *W2t,
                               const float *w, const float *temps, const int32_t *x0,
