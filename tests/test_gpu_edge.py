@@ -1,0 +1,70 @@
+"""Edge shapes through the C ABI against the oracle: vocabularies smaller than one 64-id
+block (the sweep's unpipelined ragged block is the only block), a single request and a
+single position, the smallest rank, and d = 0 (no hidden-state term in the confidence)."""
+import numpy as np
+import pytest
+
+from draft_sampling_scheduling_amd import synth
+from tests.gpu_util import N, T, compare_draft, excuse_budget
+from tests.test_gpu_verify import _compare, _inputs
+
+pytestmark = pytest.mark.gpu
+
+EDGE = [
+    ("V8-R1-g1", "c2", dict(R=1, gamma=1, V=8, r=16, d=8)),
+    ("V40-R3-g2", "c2", dict(R=3, gamma=2, V=40, r=16, d=8)),
+    ("V72-R5-g3-d0", "c2", dict(R=5, gamma=3, V=72, r=32, d=0)),
+    ("V136-R130-g1", "c2", dict(R=130, gamma=1, V=136, r=16, d=8)),
+]
+
+
+@pytest.fixture(scope="module")
+def ds():
+    import draft_sampling_scheduling_amd as ds
+    ds.lib()
+    return ds
+
+
+@pytest.mark.parametrize("name,base,kw", EDGE, ids=[c[0] for c in EDGE])
+def test_draft_and_verify_edge(ora, ds, name, base, kw):
+    cfg = synth.scaled(synth.CONFIGS[base], **kw)
+    print(f"{name}: draft", flush=True)
+    I = synth.inputs(cfg)
+    W2t = np.ascontiguousarray(I["W2"].T)
+    o = ora.draft_markov(I["U"], I["h"], I["W1"], I["W2"], I["w"], I["x0"], 1, 2)
+    g = ds.draft_markov(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(I["x0"]), 1, 2)
+    g = {k: N(v) for k, v in g.items()}
+    g["bias_rows"] = synth.bf16_to_f32(g["bias_rows"])
+    compared, excused = compare_draft(o, g, name)
+    assert excused <= excuse_budget(compared)
+    print(f"{name}: verify", flush=True)
+    I, d, target, ell = _inputs(ora, cfg, 3, "full")
+    ov = ora.verify(target, I["U"], I["W2"], d["bias_rows"], d["x"], ell, seed=0, cycle=3)
+    brows = synth.encode(cfg, d["bias_rows"].astype(np.float32))
+    gv = ds.verify(T(target), T(I["U"]), T(W2t), T(brows), T(d["x"]),
+                   T(d["lse"].astype(np.float32)), T(d["logit_x"].astype(np.float32)), T(ell),
+                   seed=0, cycle=3)
+    gv = {k: N(v) for k, v in gv.items()}
+    excused = _compare(ov, gv, d, ell, cfg.gamma, name)
+    assert excused <= excuse_budget(int(ell.sum()) + cfg.R)
+
+
+@pytest.mark.parametrize("name,base,kw", EDGE, ids=[c[0] for c in EDGE])
+def test_train_forward_edge(ora, ds, name, base, kw):
+    from tests.test_gpu_train import ALPHA, _compare as tcompare, _gpu
+    cfg = synth.scaled(synth.CONFIGS[base], **kw)
+    I = synth.inputs(cfg)
+    B = synth.train_batch(cfg)
+    o = ora.train_forward(I["U"], I["h"], I["W1"], I["W2"], I["w"], B["target"], I["x0"],
+                          B["xstar"], ALPHA)
+    tcompare(o, _gpu(ds, I, B), slice(None), name)
+
+
+def test_schedule_single_request(ora, ds):
+    c = np.array([[0.7]], np.float32)
+    sps = np.array([1.0, 0.9], np.float32)  # B = 1, 2
+    for mode in (0, 1):
+        ref = ora.schedule(c, sps, 1, mode)
+        g = ds.schedule(T(c), T(sps), 1, mode)
+        assert np.array_equal(N(g["ell"]), ref["ell"]), mode
+        assert np.array_equal(N(g["a"]), ref["a"].astype(np.float32))
