@@ -40,10 +40,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c3", help="workload: c3 (headline) or c2")
-    ap.add_argument("--workload", default="cycle", choices=("cycle", "train", "sts", "decode"),
+    ap.add_argument("--workload", default="cycle",
+                    choices=("cycle", "train", "sts", "decode", "rnn"),
                     help="cycle: the decode cycle (default); train: the training-objective "
                          "forward on teacher-forced blocks; sts: the STS calibration fit; "
-                         "decode: the multi-cycle driver on a toy chain")
+                         "decode: the multi-cycle driver on a toy chain; rnn: the RNN-head "
+                         "draft at R=256, gamma=16, V=129280")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample")
@@ -218,6 +220,8 @@ def main():
         return bench_sts(args)
     if args.workload == "decode":
         return bench_decode(args)
+    if args.workload == "rnn":
+        return bench_rnn(args)
 
     import numpy as np
     import torch
@@ -634,6 +638,78 @@ def bench_decode(args):
         "mean_ell": mean_ell,
         "tokens_per_request_cycle": emitted / rc,
         "conditional_acceptance": [float(a / t) if t else None for a, t in zip(acc, tested)],
+        "input_gen_s": gen_s,
+    }
+    print(json.dumps(res))
+
+
+def bench_rnn(args):
+    """RNN-head draft (eq. (6)) on its workload: R=256 requests, gamma=16, V=129280, r=256,
+    d=4096, bf16 operands (float bias rows, entered as hi + lo bf16 terms).  Random operands
+    drawn on the device (the timing does not depend on their values)."""
+    import math
+
+    import torch
+
+    import draft_sampling_scheduling_amd as ds
+    from draft_sampling_scheduling_amd import synth
+
+    ds.lib()
+    cfg = synth.CONFIGS["c5"]
+    R, G, V, r, d = cfg.R, cfg.gamma, cfg.V, cfg.r, cfg.d
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(55)
+    t_gen = time.perf_counter()
+
+    def rnd(shape, std):
+        return (std * torch.randn(shape, device=dev, generator=gen)).to(torch.bfloat16)
+
+    U = rnd((R, G, V), 1.0)
+    h = rnd((R, G, d), 1.0)
+    W1 = rnd((V, r), 1.0 / math.sqrt(r))
+    W2t = rnd((V, r), 1.0 / math.sqrt(r))
+    Wg = rnd((3 * r, 2 * r + d), 1.0 / math.sqrt(2 * r + d))
+    w = math.sqrt(1.0 / (d + r)) * torch.randn(d + r, device=dev, generator=gen)
+    x0 = torch.randint(0, V, (R,), device=dev, generator=gen, dtype=torch.int32)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+    out = dict(x=torch.empty((R, G), dtype=torch.int32, device=dev),
+               c=torch.empty((R, G), dtype=torch.float32, device=dev),
+               lse=torch.empty((R, G), dtype=torch.float32, device=dev),
+               logit_x=torch.empty((R, G), dtype=torch.float32, device=dev),
+               bias_rows=torch.empty((R, G, r), dtype=torch.float32, device=dev))
+    ws = torch.empty(ds.draft_rnn_workspace_bytes(R, G, V, r, d), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def call():
+        ds.draft_rnn(U, h, W1, W2t, Wg, w, x0, SEED, CYCLE, out=out, ws=ws, status=status)
+
+    call_ms, ms_per_step = _timed_calls(torch, call, args.warmup, args.steps)
+    if int(status.item()) != 0:
+        raise SystemExit(f"device fault bits set: {int(status.item())}")
+    # algorithmic bytes of one draft: per position the sweep reads U_k, W2 and the float bias
+    # rows; the h-part projection reads h and W_gco's h columns once; the per-step RNN update
+    # reads W_gco's [s; e] columns and W1 rows
+    sweep = R * V * 2 + V * r * 2 + R * r * 4
+    call_bytes = (G * sweep + R * G * d * 2 + 3 * r * d * 2
+                  + G * (3 * r * 2 * r * 2 + R * r * 2))
+    achieved = call_bytes / (call_ms * 1e-3) / 1e9
+    res = {
+        "metric": "RNN-head draft tokens/s (R=256 gamma=16 V=129280); % of HBM roofline",
+        "value": R * G / (ms_per_step * 1e-3),
+        "unit": "drafted tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"c5 RNN head: R={R} gamma={G} V={V} r={r} d={d}, bf16 operands, "
+                               "float bias rows; draft only",
+                   "R": R, "gamma": G, "V": V, "r": r, "d": d},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "dspark_draft_rnn, whole call (h projection, 16 x (RNN step, "
+                               "sweep, combine))",
+                     "bytes_per_launch": call_bytes, "launch_us": call_ms * 1e3},
         "input_gen_s": gen_s,
     }
     print(json.dumps(res))

@@ -462,6 +462,115 @@ __global__ void __launch_bounds__(256) rnn_step_kernel(int R, int gamma, int V, 
   }
 }
 
+// The [s; e] columns of W_gco regrouped for the batched step: chunk (k8, o) holds
+// W_gco[o][8 k8 .. 8 k8 + 8), so a workgroup's threads (consecutive outputs) read one
+// contiguous 16-byte chunk each per 8 inputs.
+__global__ void __launch_bounds__(256) rnn_wpack_kernel(int r, int ldw,
+                                                        const uint16_t* __restrict__ Wg,
+                                                        uint4* __restrict__ Wp) {
+  const int r3 = 3 * r, nk8 = 2 * r / 8;
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  if (gid >= r3 * nk8) return;
+  const int k8 = gid / r3, o = gid - k8 * r3;
+  Wp[gid] = *reinterpret_cast<const uint4*>(Wg + (size_t)o * ldw + 8 * k8);
+}
+
+constexpr int kRnnReq = 4;     // requests per workgroup of the batched step
+constexpr int kRnnUnits = 64;  // units per workgroup (r >= 64), else r
+constexpr int kRnnKSplit = 4;  // input quarters, one thread group each
+
+// The RNN step for kRnnReq requests and a slice of U units.  Threads form kRnnKSplit
+// groups of 3U; thread t of group p computes output o = (t / U) * r + u0 + t % U (gate,
+// candidate or output row of unit u0 + t % U) over the p-th quarter of the 2r inputs, for
+// all the workgroup's requests, so each weight chunk is read once for all of them.  The
+// quarters are added in order, then one thread per (request, unit) applies the
+// nonlinearities.  s is double-buffered across steps (s_in -> s_out), since other
+// workgroups still read s_{k-1} of these requests.
+__global__ void __launch_bounds__(kRnnKSplit * 3 * kRnnUnits) rnn_step_batched_kernel(
+    int R, int gamma, int V, int r, const uint16_t* __restrict__ W1,
+    const uint4* __restrict__ Wp, const float* __restrict__ Gh, const int32_t* prev,
+    int prev_stride, uint32_t k, const float* __restrict__ s_in, float* __restrict__ s_out,
+    float* __restrict__ orow, int32_t* status) {
+  // z [kRnnReq][2r], then partial G [kRnnKSplit][kRnnReq][3U]
+  extern __shared__ float sh[];
+  const int U = r < kRnnUnits ? r : kRnnUnits;
+  const int q0 = blockIdx.x * kRnnReq, u0 = blockIdx.y * U;
+  const int nq = R - q0 < kRnnReq ? R - q0 : kRnnReq;
+  float* z = sh;
+  float* G = sh + kRnnReq * 2 * r;
+  const int t = threadIdx.x;
+  __shared__ int toks[kRnnReq];
+  if (t < kRnnReq)
+    toks[t] = t < nq ? checked_token(prev[(size_t)(q0 + t) * prev_stride], V, status) : 0;
+  __syncthreads();
+  // z_se = [s_{k-1}; W1[x_{k-1}]] of the workgroup's requests, four values per item
+  for (int i = t; i < kRnnReq * r / 4; i += blockDim.x) {
+    const int qq = (4 * i) / r, c = 4 * i - qq * r;
+    const bool live = qq < nq;
+    const int q = live ? q0 + qq : q0;
+    const float4 sv = *reinterpret_cast<const float4*>(s_in + (size_t)q * r + c);
+    const uint2 ev = *reinterpret_cast<const uint2*>(W1 + (size_t)toks[qq] * r + c);
+    float* zs = z + qq * 2 * r + c;
+    zs[0] = live ? sv.x : 0.0f;
+    zs[1] = live ? sv.y : 0.0f;
+    zs[2] = live ? sv.z : 0.0f;
+    zs[3] = live ? sv.w : 0.0f;
+    zs[r + 0] = live ? bf16lo(ev.x) : 0.0f;
+    zs[r + 1] = live ? bf16hi(ev.x) : 0.0f;
+    zs[r + 2] = live ? bf16lo(ev.y) : 0.0f;
+    zs[r + 3] = live ? bf16hi(ev.y) : 0.0f;
+  }
+  __syncthreads();
+  const int part = t / (3 * U), tt = t - part * 3 * U;
+  const int g = tt / U, u = u0 + tt - g * U, o = g * r + u;
+  const int r3 = 3 * r, nk8 = 2 * r / 8, per = nk8 / kRnnKSplit;  // per >= 1 (r >= 16)
+  float acc[kRnnReq];
+#pragma unroll
+  for (int qq = 0; qq < kRnnReq; ++qq) acc[qq] = 0.0f;
+  for (int kb = part * per; kb < (part + 1) * per; kb += 2) {
+    // two weight chunks in flight per pass (per is even for r >= 32; r = 16 takes one)
+    uint4 wv[2];
+#pragma unroll
+    for (int v2 = 0; v2 < 2; ++v2) {
+      const int kk = kb + v2 < (part + 1) * per ? kb + v2 : kb;
+      wv[v2] = Wp[(size_t)kk * r3 + o];
+    }
+#pragma unroll
+    for (int v2 = 0; v2 < 2; ++v2) {
+      if (kb + v2 >= (part + 1) * per) break;
+      float a[8];
+      a[0] = bf16lo(wv[v2].x); a[1] = bf16hi(wv[v2].x); a[2] = bf16lo(wv[v2].y); a[3] = bf16hi(wv[v2].y);
+      a[4] = bf16lo(wv[v2].z); a[5] = bf16hi(wv[v2].z); a[6] = bf16lo(wv[v2].w); a[7] = bf16hi(wv[v2].w);
+#pragma unroll
+      for (int qq = 0; qq < kRnnReq; ++qq) {
+        const float* zq = z + qq * 2 * r + 8 * (kb + v2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[qq] = fmaf(a[j], zq[j], acc[qq]);
+      }
+    }
+  }
+#pragma unroll
+  for (int qq = 0; qq < kRnnReq; ++qq) G[(part * kRnnReq + qq) * 3 * U + tt] = acc[qq];
+  __syncthreads();
+  for (int i = t; i < nq * U; i += blockDim.x) {
+    const int qq = i / U, uu = i - qq * U, q = q0 + qq, unit = u0 + uu;
+    const float* gh = Gh + ((size_t)q * gamma + (k - 1)) * 3 * r;
+    float gv[3];
+#pragma unroll
+    for (int gi = 0; gi < 3; ++gi) {
+      float a = gh[gi * r + unit];
+#pragma unroll
+      for (int pp = 0; pp < kRnnKSplit; ++pp) a += G[(pp * kRnnReq + qq) * 3 * U + gi * U + uu];
+      gv[gi] = a;
+    }
+    const float gt = 1.0f / (1.0f + expf(-gv[0]));
+    const float cand = tanhf(gv[1]);
+    const float out = tanhf(gv[2]);
+    orow[(size_t)q * r + unit] = out;
+    s_out[(size_t)q * r + unit] = gt * z[qq * 2 * r + unit] + (1.0f - gt) * cand;
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------------------
@@ -480,7 +589,9 @@ struct DraftWs {
   uint4* bpack;  // Markov: the next sweep's B rows in packed order
   float* Gh;
   float* s;
+  float* s2;     // RNN state, the other buffer of the step's ping-pong
   float* orow;
+  uint4* wpack;  // RNN [s; e] weights regrouped for the batched step
   size_t bytes;
 };
 
@@ -493,7 +604,9 @@ static DraftWs carve_draft(void* ws, int R, int gamma, int V, int r, int d, bool
   if (rnn) {
     w.Gh = cv.take<float>((size_t)R * gamma * 3 * r);
     w.s = cv.take<float>((size_t)R * r);
+    w.s2 = cv.take<float>((size_t)R * r);
     w.orow = cv.take<float>((size_t)R * r);
+    w.wpack = cv.take<uint4>((size_t)(2 * r / 8) * 3 * r);
   } else {
     w.bpack = cv.take<uint4>((size_t)bpack_rows(R) * r / 8);
   }
@@ -545,6 +658,11 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
       fill_kernel<<<(unsigned)((n3 + 255) / 256), 256, 0, stream>>>(ws.Gh, n3, 0.0f);
     }
     fill_kernel<<<(R * r + 255) / 256, 256, 0, stream>>>(ws.s, (size_t)R * r, 0.0f);  // s_0 = 0
+    if (BF) {
+      const int n = (2 * r / 8) * 3 * r;
+      rnn_wpack_kernel<<<(n + 255) / 256, 256, 0, stream>>>(
+          r, K, reinterpret_cast<const uint16_t*>(Wg), ws.wpack);
+    }
   }
 
   SweepGeom g{};
@@ -560,7 +678,16 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
   for (int k = 1; k <= gamma; ++k) {
     const int32_t* prev = (k == 1) ? x0 : x + (k - 2);
     const int ps = (k == 1) ? 1 : gamma;
-    if (rnn) {
+    if (rnn && BF) {
+      const int U = r < kRnnUnits ? r : kRnnUnits;
+      const size_t sh = sizeof(float) * kRnnReq * (2 * r + kRnnKSplit * 3 * U);
+      const dim3 grid((R + kRnnReq - 1) / kRnnReq, r / U);
+      float* s_in = (k & 1) ? ws.s : ws.s2;  // s_0 sits in ws.s
+      float* s_out = (k & 1) ? ws.s2 : ws.s;
+      rnn_step_batched_kernel<<<grid, kRnnKSplit * 3 * U, sh, stream>>>(
+          R, gamma, V, r, reinterpret_cast<const uint16_t*>(W1), ws.wpack, ws.Gh, prev, ps,
+          (uint32_t)k, s_in, s_out, ws.orow, status);
+    } else if (rnn) {
       const size_t sh = sizeof(float) * 5 * r;
       rnn_step_kernel<T><<<R, 256, sh, stream>>>(R, gamma, V, r, d, W1, Wg, ws.Gh, prev, ps,
                                                  (uint32_t)k, ws.s, ws.orow, status);
