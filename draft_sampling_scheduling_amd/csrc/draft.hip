@@ -376,35 +376,120 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
 // RNN head (eq. (6)).  Gh[q][k][o] = sum_i W_gco[o][2r + i] h_k[i] for all k up front;
 // per step: G = W_gco[:, :2r] [s; e] + Gh, gate/candidate/output nonlinearities, s update.
 // ---------------------------------------------------------------------------------------
-// Gh = h W_h^T: [rows][d] x [3r][d]^T -> [rows][3r] fp32.  One wave per 32x32 tile on the
-// matrix cores, fragments straight from global memory (K-contiguous rows on both sides).
-__global__ void __launch_bounds__(64) rnn_hproj_bf16_kernel(int rows, int d, int r3, int ldw,
-                                                            const uint16_t* __restrict__ h,
-                                                            const uint16_t* __restrict__ Wh,
-                                                            float* __restrict__ Gh) {
-  const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
-  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;  // m: output unit, n: row
-  const int orow = m0 + n, hrow = n0 + n;
-  f32x16 acc;
+// Gh = h W_h^T: [rows][d] x [3r][d]^T -> [rows][3r] fp32, on the matrix cores.
+// A workgroup computes a 128-row x 96-output tile over one half of the inputs (split-K: the
+// halves go to two partial buffers, added by the step kernel, so the sum has a fixed order
+// and needs no atomics).  Its four waves own 32 rows each and all three 32-output blocks.
+// The inputs advance in chunks of 64 through a two-stage LDS ring, copied straight from
+// global memory with global_load_lds_dwordx4: one copy moves 8 whole 128-byte row segments
+// (8 lanes per row), and row rho of the stage keeps its 16-byte piece c in slot
+// c ^ (rho % 8), so the MFMA fragment reads (lane l: row l % 32, piece 2 ks + l / 32) of
+// 8 consecutive lanes fall on 8 different slots: conflict-free ds_read_b128.  Wave w copies
+// rows 8w .. 8w + 8 of every 32-row block of h and W_h.  Rows and outputs past the end are
+// clamped to the last one (their results are not stored); inputs past d occur only in the
+// last chunk, are read clamped and zeroed in registers.  Tiles that share rows are placed
+// on one XCD (workgroup b runs on XCD b % 8), so h comes from HBM about once.
+constexpr int kHpRows = 128, kHpOut = 96, kHpKC = 64, kHpKS = kHpKC / 16;
+constexpr int kHpStageBytes = (kHpRows + kHpOut) * kHpKC * 2;  // 28 KB
+constexpr int kHpSplit = 2;
+
+template <bool MASK>
+__device__ __forceinline__ void hproj_chunk(const uint8_t* buf, int wave, int lane, int kc,
+                                            int d, f32x16 (&acc)[3]) {
+  const int rl = lane & 31, sw = lane & 7;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-  for (int k0 = 0; k0 < d; k0 += 16) {
-    const bool kin = k0 + 8 * hh < d;  // d % 8 == 0: an 8-wide chunk is wholly in or out
-    const uint4 a = (orow < r3 && kin)
-                        ? *reinterpret_cast<const uint4*>(Wh + (size_t)orow * ldw + k0 + 8 * hh)
-                        : make_uint4(0, 0, 0, 0);
-    const uint4 bq = (hrow < rows && kin)
-                         ? *reinterpret_cast<const uint4*>(h + (size_t)hrow * d + k0 + 8 * hh)
-                         : make_uint4(0, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bq), acc, 0, 0, 0);
-  }
-  // accumulator: row m = 8(j/4) + 4*hh + (j%4) (output unit), column n (h row)
-  if (hrow < rows) {
+  for (int ks = 0; ks < kHpKS; ++ks) {
+    const int slot = 16 * ((2 * ks + (lane >> 5)) ^ sw);
+    uint4 bf = *reinterpret_cast<const uint4*>(buf + (32 * wave + rl) * 128 + slot);
+    uint4 af[3];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int m = m0 + 8 * (j >> 2) + 4 * hh + (j & 3);
-      if (m < r3) Gh[(size_t)hrow * r3 + m] = acc[j];
+    for (int ob = 0; ob < 3; ++ob)
+      af[ob] = *reinterpret_cast<const uint4*>(buf + (kHpRows + 32 * ob + rl) * 128 + slot);
+    if (MASK && kc + 16 * ks + 8 * (lane >> 5) >= d) {
+      bf = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int ob = 0; ob < 3; ++ob) af[ob] = make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int ob = 0; ob < 3; ++ob)
+      acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[ob]), as_bf16x8(bf),
+                                                          acc[ob], 0, 0, 0);
+  }
+}
+
+__global__ void __launch_bounds__(256, 2) rnn_hproj_bf16_kernel(
+    int rows, int d, int r3, int ldw, int nN, int per_xcd, const uint16_t* __restrict__ h,
+    const uint16_t* __restrict__ Wh, float* __restrict__ Gh) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kHpStageBytes];
+  const int nM = (rows + kHpRows - 1) / kHpRows;
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (t >= nM * nN * kHpSplit) return;
+  const int split = t % kHpSplit, tn = (t / kHpSplit) % nN, tm = t / (kHpSplit * nN);
+  const int row0 = tm * kHpRows, o0 = tn * kHpOut;
+  const int nchunks = (d + kHpKC - 1) / kHpKC, cper = (nchunks + kHpSplit - 1) / kHpSplit;
+  const int c0 = split * cper;
+  const int c1 = c0 + cper < nchunks ? c0 + cper : nchunks;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, ln = lane & 31, hh = lane >> 5;
+
+  // copy lane: row 8 wave + lane / 8 of each 32-row block, piece (lane % 8) ^ (lane / 8)
+  const int crow = 8 * wave + (lane >> 3), cpiece = (lane & 7) ^ (lane >> 3);
+  uint32_t hoff[4], woff[3];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = row0 + 32 * i + crow < rows ? row0 + 32 * i + crow : rows - 1;
+    hoff[i] = (uint32_t)row * (uint32_t)d * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int o = o0 + 32 * i + crow < r3 ? o0 + 32 * i + crow : r3 - 1;
+    woff[i] = (uint32_t)o * (uint32_t)ldw * 2u;
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int c, int sb) {
+    int k = c * kHpKC + 8 * cpiece;
+    if (k > d - 8) k = d - 8;
+    const uint32_t kb = (uint32_t)k * 2u;
+    const uint32_t base = lds0 + sb * kHpStageBytes + (8 * wave) * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16s(h, hoff[i] + kb, base + (32 * i) * 128);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) dma16s(Wh, woff[i] + kb, base + (kHpRows + 32 * i) * 128);
+  };
+
+  f32x16 acc[3];
+#pragma unroll
+  for (int ob = 0; ob < 3; ++ob)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[ob][j] = 0.0f;
+
+  if (c0 < c1) issue(c0, 0);
+  for (int c = c0; c < c1; ++c) {
+    const int sb = (c - c0) & 1;
+    vm_wait<0>();     // this wave's copies of chunk c have landed
+    stage_barrier();  // everyone's have; everyone is done reading chunk c - 1
+    if (c + 1 < c1) issue(c + 1, sb ^ 1);
+    const uint8_t* buf = lds + sb * kHpStageBytes;
+    if ((c + 1) * kHpKC > d)
+      hproj_chunk<true>(buf, wave, lane, c * kHpKC, d, acc);
+    else
+      hproj_chunk<false>(buf, wave, lane, c * kHpKC, d, acc);
+  }
+
+  // accumulator: output o0 + 32 ob + 8 (j / 4) + 4 hh + j % 4, row row0 + 32 wave + ln
+  const int row = row0 + 32 * wave + ln;
+  if (row < rows) {
+    float* dst = Gh + (size_t)split * rows * r3 + (size_t)row * r3;
+#pragma unroll
+    for (int ob = 0; ob < 3; ++ob)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int o = o0 + 32 * ob + 8 * jj + 4 * hh;  // r3 % 4 == 0: a group is in or out
+        if (o < r3)
+          *reinterpret_cast<float4*>(dst + o) =
+              make_float4(acc[ob][4 * jj], acc[ob][4 * jj + 1], acc[ob][4 * jj + 2],
+                          acc[ob][4 * jj + 3]);
+      }
   }
 }
 
@@ -555,10 +640,11 @@ __global__ void __launch_bounds__(kRnnKSplit * 3 * kRnnUnits) rnn_step_batched_k
   for (int i = t; i < nq * U; i += blockDim.x) {
     const int qq = i / U, uu = i - qq * U, q = q0 + qq, unit = u0 + uu;
     const float* gh = Gh + ((size_t)q * gamma + (k - 1)) * 3 * r;
+    const float* gh1 = gh + (size_t)R * gamma * 3 * r;  // the second K half
     float gv[3];
 #pragma unroll
     for (int gi = 0; gi < 3; ++gi) {
-      float a = gh[gi * r + unit];
+      float a = gh[gi * r + unit] + gh1[gi * r + unit];
 #pragma unroll
       for (int pp = 0; pp < kRnnKSplit; ++pp) a += G[(pp * kRnnReq + qq) * 3 * U + gi * U + uu];
       gv[gi] = a;
@@ -602,7 +688,7 @@ static DraftWs carve_draft(void* ws, int R, int gamma, int V, int r, int d, bool
   const int nblocks = (V + kVB - 1) / kVB;
   w.partials = cv.take<float4>((size_t)R * (nblocks < kMaxRanges ? nblocks : kMaxRanges));
   if (rnn) {
-    w.Gh = cv.take<float>((size_t)R * gamma * 3 * r);
+    w.Gh = cv.take<float>((size_t)kHpSplit * R * gamma * 3 * r);  // bf16: two K halves
     w.s = cv.take<float>((size_t)R * r);
     w.s2 = cv.take<float>((size_t)R * r);
     w.orow = cv.take<float>((size_t)R * r);
@@ -645,16 +731,18 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
     const int r3 = 3 * r, K = 2 * r + d;
     if (d > 0) {
       if (BF) {
-        dim3 grid((rows + 31) / 32, (r3 + 31) / 32);
-        rnn_hproj_bf16_kernel<<<grid, 64, 0, stream>>>(
-            rows, d, r3, K, reinterpret_cast<const uint16_t*>(h),
+        const int nN = (r3 + kHpOut - 1) / kHpOut;
+        const int tiles = (rows + kHpRows - 1) / kHpRows * nN * kHpSplit;
+        const int per = (tiles + 7) / 8;
+        rnn_hproj_bf16_kernel<<<8 * per, 256, 0, stream>>>(
+            rows, d, r3, K, nN, per, reinterpret_cast<const uint16_t*>(h),
             reinterpret_cast<const uint16_t*>(Wg) + 2 * r, ws.Gh);
       } else {
         dim3 grid((r3 + 63) / 64, rows);
         rnn_hproj_f32_kernel<T><<<grid, 64, 0, stream>>>(rows, d, r3, K, h, Wg + 2 * r, ws.Gh);
       }
     } else {
-      const size_t n3 = (size_t)rows * r3;
+      const size_t n3 = (size_t)kHpSplit * rows * r3;  // both partial buffers
       fill_kernel<<<(unsigned)((n3 + 255) / 256), 256, 0, stream>>>(ws.Gh, n3, 0.0f);
     }
     fill_kernel<<<(R * r + 255) / 256, 256, 0, stream>>>(ws.s, (size_t)R * r, 0.0f);  // s_0 = 0
@@ -755,6 +843,9 @@ static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_d
     return DSPARK_EINVAL;
   if (d > 0 && !h) return DSPARK_EINVAL;
   if (rnn && !Wg) return DSPARK_EINVAL;
+  // the bf16 h projection addresses h with 32-bit byte offsets
+  if (rnn && dt == DSPARK_BF16 && (uint64_t)R * gamma * d * 2 >= ((uint64_t)1 << 32))
+    return DSPARK_EINVAL;
   // the bf16 sweep addresses U rows with 32-bit byte offsets
   if (dt == DSPARK_BF16 && (uint64_t)R * gamma * V * 2 >= ((uint64_t)1 << 32)) return DSPARK_EINVAL;
   if (!aligned16(U) || !aligned16(h) || !aligned16(W1) || !aligned16(W2t) || !aligned16(Wg) ||

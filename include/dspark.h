@@ -134,7 +134,8 @@ int dspark_draft_markov_timed(int R, int gamma, int V, int r, int d, dspark_dtyp
 /* RNN head, eq. (6): W_gco [3r][2r + d] dt stacks the gate, candidate and output
  * projections (row blocks in that order; columns ordered [s ; W1 row ; h]; no biases);
  * s_0 = 0.  The bias row of step k is tanh(W_o z_k) with z_k holding s_{k-1}; c uses eq.
- * (7) with W1[x_{k-1}] unchanged.  bias_rows is float [R][gamma][r]. */
+ * (7) with W1[x_{k-1}] unchanged.  bias_rows is float [R][gamma][r].  With bf16
+ * operands, h (R * gamma * d * 2 bytes) must also stay below 4 GiB (DSPARK_EINVAL). */
 size_t dspark_draft_rnn_workspace_bytes(int R, int gamma, int V, int r, int d);
 
 int dspark_draft_rnn(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void *U,

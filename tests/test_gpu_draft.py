@@ -60,6 +60,12 @@ RNN_CASES = [
     ("rnn-f32", "c5", dict(R=6, gamma=4, V=1024, r=16, d=64, dtype="f32")),
     ("rnn-bf16", "c5", dict(R=40, gamma=4, V=4096, r=64, d=128)),
     ("rnn-bf16-r256", "c5", dict(R=140, gamma=3, V=2048, r=256, d=256)),
+    # h projection: d not a multiple of the 64-input chunk (masked last chunk), rows not a
+    # multiple of the 128-row tile, one chunk only (the second K half empty), no h at all
+    ("rnn-bf16-d200", "c5", dict(R=7, gamma=5, V=1024, r=32, d=200)),
+    ("rnn-bf16-d8", "c5", dict(R=3, gamma=2, V=512, r=16, d=8)),
+    ("rnn-bf16-d0", "c5", dict(R=9, gamma=3, V=1024, r=32, d=0)),
+    ("rnn-bf16-rows260", "c5", dict(R=65, gamma=4, V=1024, r=128, d=328)),
 ]
 
 
