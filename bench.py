@@ -152,11 +152,34 @@ def cpu_baseline(cfg, I, target_seconds):
         dt, _ = run(S)
         t += dt
         reps += 1
+    # the same oracle on one thread: single requests, repeated for a few seconds
+    oracle.set_num_threads(1)
+    t1, reps1 = 0.0, 0
+    try:
+        while reps1 == 0 or t1 < min(3.0, target_seconds / 4):
+            dt, _ = run(1)
+            t1 += dt
+            reps1 += 1
+    finally:
+        oracle.set_num_threads(threads)
     return dict(value=reps * S * cfg.gamma / t, unit="drafted tokens/s", cores=threads,
                 kind="oracle",
                 sample=f"{reps} x the first {S} of {cfg.R} requests of the same workload: draft "
                        f"(gamma={cfg.gamma}, V={cfg.V}, fp64), schedule (early stop) and verify; "
-                       f"{t:.1f} s wall (target stand-in built untimed)")
+                       f"{t:.1f} s wall (target stand-in built untimed)",
+                value_1thread=reps1 * cfg.gamma / t1,
+                sample_1thread=f"{reps1} x request 0 on one thread, {t1:.1f} s wall",
+                cpu_model=cpu_model(), nproc=len(os.sched_getaffinity(0)))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 COPY_PROBE_BYTES = 1 << 29
@@ -315,7 +338,7 @@ def main():
     sweep_ms = np.mean([elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in timed])
 
     # stage breakdown, outside the timed region (its events add gaps of their own)
-    nb = min(5, args.steps)
+    nb = min(20, args.steps)
     sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
     for i in range(nb):
         step(None, sev[i])
@@ -323,6 +346,7 @@ def main():
     t_draft = np.mean([e[0].elapsed_time(e[1]) for e in sev])
     t_sched = np.mean([e[1].elapsed_time(e[2]) for e in sev])
     t_ver = np.mean([e[2].elapsed_time(e[3]) for e in sev])
+    cycle_median = float(np.median([e[0].elapsed_time(e[3]) for e in sev]))
     if args.copy_probe:
         # a plain device copy of known size, for scaling the HBM byte counters
         a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
@@ -341,6 +365,9 @@ def main():
     achieved = sweep_bytes / (sweep_ms * 1e-3) / 1e9
     n_a, n_b = int(ell.sum()) + R, int(ell.sum())
     cycle_bytes = (G * sweep_bytes + R * G * d * 2) + (n_a * V * 2 + n_b * V * 2 + V * r * 2)
+    # the stricter view of the draft: W2 counted once per cycle (the last-level cache can
+    # hold it), so only U_k, the W1 rows and h count per step
+    draft_bytes_w2_once = G * (R * V * 2 + R * r * 2) + V * r * 2 + R * G * d * 2
     traffic = None
     if args.config == "c3" and os.path.exists(TRAFFIC_JSON):
         try:
@@ -372,6 +399,8 @@ def main():
                      "bytes_per_launch": sweep_bytes, "launch_us": sweep_ms * 1e3},
         "emitted_tokens_per_s": emitted / (ms_per_step * 1e-3),
         "stage_ms": {"draft": t_draft, "schedule": t_sched, "verify": t_ver},
+        "cycle_ms_median": cycle_median,
+        "draft_hbm_frac_w2_once": draft_bytes_w2_once / (t_draft * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "cycle_hbm_frac": cycle_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "verified_rows": n_b, "accepted": int(n_acc.sum()), "mean_ell": float(ell.mean()),
         "input_gen_s": gen_s,

@@ -75,6 +75,8 @@ def lib():
                                      i32p, i32p, i64p])
         L.ora_decode_run.restype = C.c_int
         L.ora_num_threads.restype = C.c_int
+        L.ora_set_num_threads.argtypes = [C.c_int]
+        L.ora_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -101,6 +103,10 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return lib().ora_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().ora_set_num_threads(int(n))
 
 
 def philox(ctr, key) -> np.ndarray:

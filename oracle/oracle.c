@@ -44,6 +44,14 @@ int ora_num_threads(void) {
 #endif
 }
 
+void ora_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------------------
  * Philox4x32-10 (Salmon et al., SC'11, section on the Philox family).
  * One round maps (x0,x1,x2,x3) with round key (k0,k1) to

@@ -188,6 +188,8 @@ int ora_verify(int R, int gamma, int V, int rank, int dt, const void *target,
 
 /* Number of OpenMP threads the oracle uses (1 when built without OpenMP). */
 int ora_num_threads(void);
+/* Sets the number of OpenMP threads of later calls (n >= 1; no effect without OpenMP). */
+void ora_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
