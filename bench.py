@@ -751,7 +751,8 @@ def log(msg: str) -> None:
 def kernel_sha() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("dev.h", "sweep.h", "draft.hip"):
+    # the draft sweep kernel's whole source: the sweep template, its epilogue, the helpers
+    for f in ("dev.h", "sweep.h", "draft_epi.h"):
         h.update(open(os.path.join(ROOT, "draft_sampling_scheduling_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
