@@ -1,7 +1,9 @@
 """Parity at the full workload sizes, through the same entry points and launch
 configuration bench.py times: the headline workload (R=256, gamma=8, V=151936, r=256,
-d=4096, bf16) end to end (draft, schedule, verify) and the RNN-head workload's draft
-(R=256, gamma=16, V=129280).  The oracle runs the whole workload on the host (a few seconds
+d=4096, bf16) end to end (draft, schedule, verify), the RNN-head workload's draft
+(R=256, gamma=16, V=129280) and the largest workload's draft (R=512, gamma=16, V=151936,
+d=5120: U is 2.49 GB, near the 4 GiB reach of the sweep's 32-bit offsets, and every
+workgroup takes two row groups).  The oracle runs the whole workload on the host (a few seconds
 on the machine's cores); every request is compared by the same rules as the scaled tests."""
 import numpy as np
 import pytest
@@ -94,4 +96,15 @@ def test_c5_rnn_draft_full(ora, ds):
     g = _gpu_draft(ds, cfg, I, rnn=True)
     compared, excused = compare_draft(o, g, "c5-full")
     print(f"c5 draft: compared {compared}, excused {excused}")
+    assert excused <= excuse_budget(compared)
+
+
+def test_c4_draft_full(ora, ds):
+    cfg = synth.CONFIGS["c4"]
+    I = synth.inputs(cfg)
+    print(f"c4 draft: R={cfg.R} gamma={cfg.gamma} V={cfg.V} d={cfg.d}", flush=True)
+    o = ora.draft_markov(I["U"], I["h"], I["W1"], I["W2"], I["w"], I["x0"], 0, CYCLE)
+    g = _gpu_draft(ds, cfg, I)
+    compared, excused = compare_draft(o, g, "c4-full")
+    print(f"c4 draft: compared {compared}, excused {excused}")
     assert excused <= excuse_budget(compared)
