@@ -133,19 +133,37 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
   __shared__ float4 red[kWaves];
   __shared__ float dotp[kWaves][kWave];
   __shared__ float zred[kWaves];
-  __shared__ int s_pick;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t rk = (size_t)q * gamma + (k - 1);
+  // this thread's first range partial and the previous token, loaded before anything waits
+  const float4* prow = partials + (size_t)q * nranges;
+  const float4 pr0 =
+      tid < nranges ? prow[tid] : make_float4(0.0f, 0.0f, 0.0f, __int_as_float(0x7fffffff));
   // the previous token's embedding row (independent of the partials)
   const int32_t tprev = checked_token(prev[(size_t)q * prev_stride], V, status);
   const T* e = W1 + (size_t)tprev * r;
+  // confidence head, embedding part: w_e . W1[x_{k-1}], and the bias row this step used
+  // (for verification): both depend on x_{k-1} only, so they overlap the partials' loads
+  {
+    float ze = 0.0f;
+    for (int i = tid; i < r; i += kCombineThreads) ze = fmaf(w[d + i], ld<T>(e, i), ze);
+    ze = wave_sum(ze);
+    if (lane == 0) zred[wave] = ze;
+    if (RNN) {
+      float* br = static_cast<float*>(bias_rows) + rk * r;
+      for (int i = tid; i < r; i += kCombineThreads) br[i] = orow[(size_t)q * r + i];
+    } else {
+      T* br = static_cast<T*>(bias_rows) + rk * r;
+      for (int i = tid; i < r; i += kCombineThreads) br[i] = e[i];
+    }
+  }
 
   // first level: normaliser and winning block over the ranges' partials (per wave: the
   // largest reference, then one rescale per lane and a plain sum)
   float M = -INFINITY, S = 0.0f, G = -INFINITY;
   int Bk = 0x7fffffff;
   for (int i = tid; i < nranges; i += kCombineThreads) {
-    const float4 pr = partials[(size_t)q * nranges + i];
+    const float4 pr = i == tid ? pr0 : prow[i];
     const int pb = __float_as_int(pr.w);
     if (pb == 0x7fffffff) continue;
     lse_merge(M, S, pr.x, pr.y);
@@ -209,19 +227,6 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
         for (int j = 0; j < 8; ++j) part = fmaf(bv[it][j], a[it][j], part);
   }
   dotp[wave][lane] = part;
-  // confidence head, embedding part: w_e . W1[x_{k-1}]
-  float ze = 0.0f;
-  for (int i = tid; i < r; i += kCombineThreads) ze = fmaf(w[d + i], ld<T>(e, i), ze);
-  ze = wave_sum(ze);
-  if (lane == 0) zred[wave] = ze;
-  // the bias row this step used, for verification
-  if (RNN) {
-    float* br = static_cast<float*>(bias_rows) + rk * r;
-    for (int i = tid; i < r; i += kCombineThreads) br[i] = orow[(size_t)q * r + i];
-  } else {
-    T* br = static_cast<T*>(bias_rows) + rk * r;
-    for (int i = tid; i < r; i += kCombineThreads) br[i] = e[i];
-  }
   __syncthreads();
   if (wave == 0) {
     float acc = 0.0f;
@@ -230,7 +235,11 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
     const float l = (v < V) ? u + acc : -INFINITY;
     float score = (v < V) ? l + gn : -INFINITY;
     int idx = v;
-    wave_argmax(score, idx);
+    wave_argmax(score, idx);  // every lane of the wave holds the pick
+    if (sizeof(T) == 2 && !RNN && bpack && lane < r / 8)
+      // W1[x_k] in the next sweep's packed order, one 16-byte chunk per lane
+      bpack[bpack_index(q, lane, r / 16)] =
+          reinterpret_cast<const uint4*>(W1 + (size_t)idx * r)[lane];
     const float lx = __shfl(l, idx - Bk * kVB, kWave);
     float z = zh[rk];
 #pragma unroll
@@ -247,16 +256,7 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
       if (zout) zout[rk] = z;
       lse[rk] = M + __logf(S);
       logit_x[rk] = lx;
-      s_pick = idx;
     }
-  }
-  if (sizeof(T) == 2 && !RNN && bpack) {
-    // W1[x_k] in the next sweep's packed order, one 16-byte chunk per thread
-    __syncthreads();
-    const int pick = s_pick;
-    if (tid < r / 8)
-      bpack[bpack_index(q, tid, r / 16)] =
-          reinterpret_cast<const uint4*>(W1 + (size_t)pick * r)[tid];
   }
 }
 
