@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/dspark.h"
 
 namespace dspark {
@@ -24,18 +26,45 @@ inline bool dims_ok(int R, int gamma, int V, int r, int d) {
 // 16-byte alignment of the operands read with vector loads (null passes)
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// compute units of the current device (cached per device id)
-inline int device_cus() {
-  static int cache[64] = {0};
+// Device attributes are cached per device id in relaxed atomics: concurrent first calls
+// may both query the runtime, and store the same value.
+inline int cached_device_attribute(std::atomic<int> (&cache)[64], hipDeviceAttribute_t attr,
+                                   int fallback) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  if (dev < 64) cache[dev] = cus;
-  return cus;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fallback;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) v = fallback;
+  if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// compute units of the current device
+inline int device_cus() {
+  static std::atomic<int> cache[64];
+  return cached_device_attribute(cache, hipDeviceAttributeMultiprocessorCount, 256);
+}
+
+// LDS the current device allows one workgroup
+inline size_t device_max_lds() {
+  static std::atomic<int> cache[64];
+  return (size_t)cached_device_attribute(cache, hipDeviceAttributeMaxSharedMemoryPerBlock, 65536);
+}
+
+// Raises a kernel's dynamic-LDS ceiling to `bytes` on the current device, once per device
+// (`done` is the kernel's own set of devices already raised).
+inline void ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_relaxed) & bit)) return;
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) ==
+          hipSuccess &&
+      bit)
+    done.fetch_or(bit, std::memory_order_relaxed);
 }
 
 // bump allocator over the caller's workspace (256-byte aligned slices)

@@ -422,13 +422,9 @@ int dspark_schedule(int R, int gamma, const float* c, const float* c_lag, int R_
   const int npad_lag = lag ? pow2_at_least(R_lag * gamma) : 2;
   const int np = npad > npad_lag ? npad : npad_lag;
   const size_t sh = (size_t)2 * np * sizeof(unsigned long long);
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(schedule_kernel),
-                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)(2 * kMaxSchedN * sizeof(unsigned long long)));
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  ensure_dynamic_lds(reinterpret_cast<const void*>(schedule_kernel),
+                     (int)(2 * kMaxSchedN * sizeof(unsigned long long)), lds_raised);
   schedule_kernel<<<1, kSchedThreads, sh, stream>>>(R, gamma, c, lag ? c_lag : nullptr,
                                                     lag ? R_lag : 0, sps, sps_B0, (int)mode,
                                                     npad, npad_lag, ell, a, stats, dev_status);

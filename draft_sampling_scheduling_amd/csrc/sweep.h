@@ -29,6 +29,7 @@
 #include <hip/hip_ext.h>
 
 #include "dev.h"
+#include "host.h"
 
 namespace dspark {
 
@@ -487,21 +488,6 @@ inline SweepGeom make_geom(int nrows, int V, int r, const uint16_t* W2t, int tar
   return g;
 }
 
-// LDS the device allows one workgroup (cached per device)
-inline size_t device_max_lds() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
-  if (cache[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-        v <= 0)
-      v = 65536;
-    cache[dev] = v;
-  }
-  return (size_t)cache[dev];
-}
-
 // ev0/ev1 (both or neither): events the dispatch itself timestamps at the kernel's start
 // and end, so their elapsed time is the kernel's own duration
 template <int NKS, bool SPLIT, int NSTAGE, class Epi>
@@ -509,12 +495,8 @@ inline void launch_sweep_nks(const SweepGeom& g, const typename Epi::Params& p, 
                              hipEvent_t ev0, hipEvent_t ev1) {
   auto kern = sweep_kernel<NKS, SPLIT, NSTAGE, Epi>;
   const size_t sh = sweep_lds_bytes(g.r, Epi::kStreams, NSTAGE);
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
-    attr = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)sh, lds_raised);
   if (ev0 && ev1)
     hipExtLaunchKernelGGL(kern, dim3(g.nranges * g.gsplit), dim3(kSweepThreads), (uint32_t)sh, s,
                           ev0, ev1, 0, g, p);

@@ -31,8 +31,9 @@
  *   - Size limits (DSPARK_EINVAL otherwise): V % 8 == 0; r in {16,32,64,128,256};
  *     d % 8 == 0; 1 <= gamma <= 64; R >= 0 (R == 0 is a no-op); R*gamma <= 8192 for the
  *     scheduler; with bf16 operands U and the target logits below 4 GiB each.
- *   - Thread safety: no global mutable state; concurrent calls on different streams with
- *     disjoint outputs and workspaces are safe.
+ *   - Thread safety: the only global state is per-device caches of device attributes and
+ *     of kernel launch settings, kept in atomics; concurrent calls on different streams
+ *     with disjoint outputs and workspaces are safe.
  */
 #ifndef DSPARK_H
 #define DSPARK_H
