@@ -54,17 +54,19 @@ __global__ void __launch_bounds__(256) conf_h_kernel(int rows, int d, const T* _
   if (row >= rows) return;
   const T* hr = h + (size_t)row * d;
   float acc = 0.0f;
-  // four 8-element chunks per lane in flight together (clamped addresses, masked sums)
-  for (int i0 = lane * 8; i0 < d; i0 += 4 * 64 * 8) {
-    float x[4][8], wv[4][8];
+  // eight 8-element chunks per lane in flight together (a whole row of d = 4096 in one
+  // round trip; clamped addresses, masked sums)
+  constexpr int kDepth = 8;
+  for (int i0 = lane * 8; i0 < d; i0 += kDepth * 64 * 8) {
+    float x[kDepth][8], wv[kDepth][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kDepth; ++u) {
       const int i = i0 + u * 64 * 8 < d ? i0 + u * 64 * 8 : i0;
       ld8<T>(hr + i, x[u]);
       ld8<float>(w + i, wv[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kDepth; ++u)
       if (i0 + u * 64 * 8 < d)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc = fmaf(wv[u][j], x[u][j], acc);

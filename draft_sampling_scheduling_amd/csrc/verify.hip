@@ -28,9 +28,10 @@
 
 namespace dspark {
 
-constexpr int kLseThreads = 256;  // lse pass: one thread per 64-id block, 256 blocks per item
+constexpr int kLseThreads = 256;  // lse pass: four independent waves per workgroup
 
-__host__ __device__ inline int lse_tiles(int V) { return ((V + kVB - 1) / kVB + kLseThreads - 1) / kLseThreads; }
+// the lse pass works in wave items: 64 consecutive 64-id blocks (4096 ids) of one row
+__host__ __device__ inline int lse_witems(int V) { return ((V + kVB - 1) / kVB + kWave - 1) / kWave; }
 
 struct VerifyWs {
   int* hdr;        // [0] = |A|, [1] = |B|
@@ -39,7 +40,7 @@ struct VerifyWs {
   int4* rowA;      // [R*(gamma+1)] (q, j, 1 if j is the bonus row, 0)
   int2* rowB;      // [R*gamma]
   float* lset;     // [R*(gamma+1)] target log-sum-exp of list-A rows
-  float4* lpart;   // [R*(gamma+1)][lse_tiles(V)] (max, sum exp, best G, block) per item
+  float4* lpart;   // [R*(gamma+1)][lse_witems(V)] (max, sum exp, best G, block) per item
   float2* bonus;   // [R] (best G, block) of the bonus row
   int* jstar;      // [R] first rejected position, 0 = none
   float4* partials;  // [R*gamma][nranges]: (sum |p-q|, best G, block, residual mass)
@@ -56,7 +57,7 @@ static VerifyWs carve_verify(void* ws, int R, int gamma, int V, int r) {
   w.rowA = cv.take<int4>((size_t)R * (gamma + 1));
   w.rowB = cv.take<int2>((size_t)R * gamma);
   w.lset = cv.take<float>((size_t)R * (gamma + 1));
-  w.lpart = cv.take<float4>((size_t)R * (gamma + 1) * lse_tiles(V));
+  w.lpart = cv.take<float4>((size_t)R * (gamma + 1) * lse_witems(V));
   w.bonus = cv.take<float2>((size_t)R);
   w.jstar = cv.take<int>((size_t)R);
   const int nblocks = (V + kVB - 1) / kVB;
@@ -171,21 +172,22 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
                                                                  uint64_t seed, uint64_t cycle) {
   constexpr float kLog2e = 1.4426950408889634f;
   constexpr float kLn2 = 0.69314718055994531f;
-  __shared__ float4 red[kLseThreads / kWave];
-  const int tiles = lse_tiles(V);
-  const int nitems = ws.hdr[0] * tiles;
+  const int per_row = lse_witems(V);
+  const int nitems = ws.hdr[0] * per_row;
   const int nblocks = (V + kVB - 1) / kVB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int G0 = gridDim.x;
+  const int lane = threadIdx.x & 63;
+  // every wave is an independent worker over the wave items (no barriers, no LDS): the
+  // next item's descriptor loads while the current one streams
+  const int gw = blockIdx.x * (kLseThreads / kWave) + (threadIdx.x >> 6);
+  const int W = gridDim.x * (kLseThreads / kWave);
   const Rng rng(seed, cycle);
-  // Wave w of an item covers blocks tile*256 + 64w .. + 64 in 8 coalesced rounds: in round
+  // Wave item wi of a row covers blocks 64 wi .. 64 wi + 64 in 8 coalesced rounds: in round
   // c lane l holds chunk l & 7 of block 8c + l/8.  One reference serves the whole window
   // (its largest logit), so the row needs no per-block max; on the bonus row the block sums
   // are 8-lane reductions on the DPP network.
   auto offsets = [&](int item, int4 inf, const T*& row, int (&v)[8]) {
-    const int tile = item % tiles;
     row = target + ((size_t)inf.x * (gamma + 1) + (inf.y - 1)) * V;
-    const int bw = tile * kLseThreads + wave * kWave;
+    const int bw = (item % per_row) * kWave;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       v[c] = (bw + 8 * c + (lane >> 3)) * kVB + 8 * (lane & 7);
@@ -194,9 +196,9 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
   };
   const int4 dflt = make_int4(0, 1, 0, 0);
   // the row descriptor of the next item is fetched while the current one streams
-  int4 info = blockIdx.x < nitems ? ws.rowA[blockIdx.x / tiles] : dflt;
-  for (int item = blockIdx.x; item < nitems; item += G0) {
-    const int4 info1 = item + G0 < nitems ? ws.rowA[(item + G0) / tiles] : dflt;
+  int4 info = gw < nitems ? ws.rowA[gw / per_row] : dflt;
+  for (int item = gw; item < nitems; item += W) {
+    const int4 info1 = item + W < nitems ? ws.rowA[(item + W) / per_row] : dflt;
     LseRaw<T> cur;
     {
       const T* row;
@@ -205,10 +207,9 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
       cur.load(row, v);
     }
     __builtin_amdgcn_sched_barrier(0);  // all eight loads go out before their first use
-    const int tile = item % tiles;
     const int q = info.x, j = info.y;
     const bool bonus = info.z != 0;
-    const int bw = tile * kLseThreads + wave * kWave;  // first block of this wave
+    const int bw = (item % per_row) * kWave;  // first block of this wave item
     // The item's arithmetic, with ids past V masked only in a window that reaches the end
     // of the row (MASK); every other window skips the per-element selects.
     float mx, ref, S, G;
@@ -273,23 +274,9 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
     else
       item_math(std::true_type{});
     S = wave_sum(S);
-    float M = mx == -INFINITY ? -INFINITY : ref * kLn2;
+    const float M = mx == -INFINITY ? -INFINITY : ref * kLn2;
     wave_argmax(G, Bk);
-    if (lane == 0) red[wave] = make_float4(M, S, G, __int_as_float(Bk));
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int w = 1; w < kLseThreads / kWave; ++w) {
-        const float4 o = red[w];
-        lse_merge(M, S, o.x, o.y);
-        const int ob = __float_as_int(o.w);
-        if (o.z > G || (o.z == G && ob < Bk)) {
-          G = o.z;
-          Bk = ob;
-        }
-      }
-      ws.lpart[item] = make_float4(M, S, G, __int_as_float(Bk));
-    }
-    __syncthreads();  // red is reused by the next item
+    if (lane == 0) ws.lpart[item] = make_float4(M, S, G, __int_as_float(Bk));
     info = info1;
   }
 }
@@ -306,6 +293,21 @@ __global__ void __launch_bounds__(64) verify_decide_kernel(
   // one wave per request; lane j - 1 tests position j (gamma <= 64)
   const int q = blockIdx.x, lane = threadIdx.x, j = lane + 1;
   const int L = clamp_len(ell[q], gamma);
+  // the acceptance test's operands first (they do not depend on the normalisers, so this
+  // chain of loads overlaps the packing and the merges below): x_j, its target logit,
+  // log q_j(x_j) and the uniform
+  bool bad = false;
+  int xj = 0;
+  float tv = 0.0f, lq = 0.0f, u_acc = 0.0f;
+  if (j <= L) {
+    const size_t rj = (size_t)q * gamma + (j - 1);
+    const int32_t t = x[rj];
+    bad = t < 0 || t >= V;
+    xj = bad ? 0 : t;
+    tv = ld<T>(target, ((size_t)q * (gamma + 1) + (j - 1)) * V + xj);
+    lq = logit_x[rj] - lse[rj];  // log q_j(x_j)
+    u_acc = uniform_of(Rng(seed, cycle).word(kStreamAccept, (uint32_t)q, (uint32_t)j, 0u));
+  }
   if (brows) {
     // the sweep's B rows for this request's list-B rows, in its packed order: half-waves
     // take one row each, lane & 31 its 16-byte chunk; four row pairs in flight per pass
@@ -325,25 +327,37 @@ __global__ void __launch_bounds__(64) verify_decide_kernel(
       }
     }
   }
-  // target normaliser of rows 1..L+1 from their lse items (in item order, so ties keep the
-  // lowest block); the bonus row's winning block
-  const int tiles = lse_tiles(V);
+  // target normaliser of rows 1..L+1 from their lse items, lane jj - 1 taking row jj: all of
+  // a row's items in flight together (up to 40 per pass: one round trip for rows of up to
+  // 40 x 4096 ids), then the largest maximum and one rescaled sum, so the exponentials are
+  // independent; the best (G, block) with ties to the lowest block; the bonus row's winner
+  const int tiles = lse_witems(V);
   float lset_j = 0.0f;
   for (int jj = j; jj <= L + 1; jj += kWave) {
     const int i = ws.offA[q] + jj - 1;
     float M = -INFINITY, S = 0.0f, G = -INFINITY;
     int Bk = 0x7fffffff;
-    for (int pc0 = 0; pc0 < tiles; pc0 += 8) {
-      float4 o[8];  // eight items in flight together (clamped, unconditional loads)
+    constexpr int kPass = 40;
+    for (int pc0 = 0; pc0 < tiles; pc0 += kPass) {
+      float4 o[kPass];  // clamped, unconditional loads
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < kPass; ++u)
         o[u] = ws.lpart[(size_t)i * tiles + (pc0 + u < tiles ? pc0 + u : tiles - 1)];
+      // predicates, not breaks: the loops stay fully unrolled over registers
+      float mp = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (pc0 + u >= tiles) break;
-        lse_merge(M, S, o[u].x, o[u].y);
+      for (int u = 0; u < kPass; ++u)
+        if (pc0 + u < tiles) mp = fmaxf(mp, o[u].x);
+      const float ref = mp == -INFINITY ? 0.0f : mp;
+      float sp = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kPass; ++u)
+        if (pc0 + u < tiles && o[u].x != -INFINITY) sp += o[u].y * __expf(o[u].x - ref);
+      lse_merge(M, S, mp, sp);
+#pragma unroll
+      for (int u = 0; u < kPass; ++u) {
         const int ob = __float_as_int(o[u].w);
-        if (o[u].z > G || (o[u].z == G && ob < Bk)) {
+        if (pc0 + u < tiles && (o[u].z > G || (o[u].z == G && ob < Bk))) {
           G = o[u].z;
           Bk = ob;
         }
@@ -354,20 +368,10 @@ __global__ void __launch_bounds__(64) verify_decide_kernel(
     if (jj == j) lset_j = ls;
     if (jj == L + 1) ws.bonus[q] = make_float2(G, __int_as_float(Bk));
   }
-  const Rng rng(seed, cycle);
-  bool reject = false, bad = false;
-  int xj = 0;
+  bool reject = false;
   if (j <= L) {
-    const size_t rj = (size_t)q * gamma + (j - 1);
-    const int32_t t = x[rj];
-    bad = t < 0 || t >= V;
-    xj = bad ? 0 : t;
-    const float tv = ld<T>(target, ((size_t)q * (gamma + 1) + (j - 1)) * V + xj);
-    const float lp = tv - lset_j;                          // log p_j(x_j)
-    const float lq = logit_x[rj] - lse[rj];              // log q_j(x_j)
-    const float ratio = __expf(lp - lq);
-    const float u = uniform_of(rng.word(kStreamAccept, (uint32_t)q, (uint32_t)j, 0u));
-    reject = !(u < ratio);
+    const float lp = tv - lset_j;  // log p_j(x_j)
+    reject = !(u_acc < __expf(lp - lq));
   }
   // the tests run in order: the first rejection ends them
   const unsigned long long rm = __ballot(reject);
@@ -750,8 +754,8 @@ static int verify_run(int R, int gamma, int V, int r, const void* target_, const
   verify_prep_kernel<<<1, 1024, 0, stream>>>(R, gamma, ell, ws, status);
   {
     // persistent grid over the items of list A (its length is known on the device only)
-    const int items = R * (gamma + 1) * lse_tiles(V), cap = 4 * device_cus();
-    verify_lse_kernel<T><<<items < cap ? items : cap, kLseThreads, 0, stream>>>(
+    const int wgs = (R * (gamma + 1) * lse_witems(V) + 3) / 4, cap = 4 * device_cus();
+    verify_lse_kernel<T><<<wgs < cap ? wgs : cap, kLseThreads, 0, stream>>>(
         R, gamma, V, target, ell, ws, seed, cycle);
   }
   // bf16 bias rows go to the sweep in its packed order (float ones, split hi + lo, do not)
