@@ -106,12 +106,43 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ----------------------------------------------------------------------------------------
-// wave reductions (wave64)
+// wave reductions (wave64), every lane ending with the result.  The partner values come
+// from the cross-lane network rather than LDS permutes: DPP quad permutes (lanes 1 and 2
+// apart), the DPP 8- and 16-lane mirrors (after the quad steps each lane holds its quad's
+// result, so pairing lane i with 7 - i, then with 15 - i, joins disjoint groups), a swizzle
+// for lanes 16 apart inside each half, and the 32-lane swap.  Each step combines a lane's
+// value with its partner's under a commutative operation, so all lanes compute the same
+// tree and hold bit-identical results.  Call with the whole wave active.
 // ----------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t xlane_dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t xlane_swz16(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (0x10 << 10) | 0x1F);
+}
+// value of the partner lane at butterfly step STEP (0..4: 1, 2, mirror 8, mirror 16, 16)
+template <int STEP>
+__device__ __forceinline__ uint32_t xlane_partner(uint32_t x) {
+  if (STEP == 0) return xlane_dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  if (STEP == 1) return xlane_dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if (STEP == 2) return xlane_dpp<0x141>(x);  // row_half_mirror
+  if (STEP == 3) return xlane_dpp<0x140>(x);  // row_mirror
+  return xlane_swz16(x);                      // lane ^ 16 inside each half
+}
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, __uint_as_float(xlane_partner<0>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(xlane_partner<1>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(xlane_partner<2>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(xlane_partner<3>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(xlane_partner<4>(__float_as_uint(v))));
+  // the swap gives every lane the lower half's value and the upper half's, in that order
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -119,9 +150,7 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // merge of two (max, sum of exp(l - max)) pairs; -inf maxima carry zero mass (branch-free)
@@ -132,17 +161,25 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mm;
 }
 
-// argmax with ties to the lower index, across the wave
+// argmax with ties to the lower index, across the wave (the same network as wave_reduce;
+// value and index travel together, and the order is total, so every lane ends alike)
 __device__ __forceinline__ void wave_argmax(float& val, int& idx) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(val, o, kWave);
-    const int i2 = __shfl_xor(idx, o, kWave);
+  auto take = [&](float v2, int i2) {
     if (v2 > val || (v2 == val && i2 < idx)) {
       val = v2;
       idx = i2;
     }
-  }
+  };
+  take(__uint_as_float(xlane_partner<0>(__float_as_uint(val))), (int)xlane_partner<0>((uint32_t)idx));
+  take(__uint_as_float(xlane_partner<1>(__float_as_uint(val))), (int)xlane_partner<1>((uint32_t)idx));
+  take(__uint_as_float(xlane_partner<2>(__float_as_uint(val))), (int)xlane_partner<2>((uint32_t)idx));
+  take(__uint_as_float(xlane_partner<3>(__float_as_uint(val))), (int)xlane_partner<3>((uint32_t)idx));
+  take(__uint_as_float(xlane_partner<4>(__float_as_uint(val))), (int)xlane_partner<4>((uint32_t)idx));
+  const auto rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(val), __float_as_uint(val), false, false);
+  const auto ri = __builtin_amdgcn_permlane32_swap((uint32_t)idx, (uint32_t)idx, false, false);
+  val = __uint_as_float(rv[0]);
+  idx = (int)ri[0];
+  take(__uint_as_float(rv[1]), (int)ri[1]);
 }
 
 // plain fill (used instead of memset so that captured graphs hold only kernels)
