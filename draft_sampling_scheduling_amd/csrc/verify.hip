@@ -194,11 +194,13 @@ __global__ void __launch_bounds__(kLseThreads) verify_lse_kernel(int R, int gamm
       v[c] = v[c] < V ? v[c] : V - 8;  // clamped, unconditional loads (V % 8 == 0)
     }
   };
-  const int4 dflt = make_int4(0, 1, 0, 0);
-  // the row descriptor of the next item is fetched while the current one streams
-  int4 info = gw < nitems ? ws.rowA[gw / per_row] : dflt;
+  // the row descriptor of the next item is fetched while the current one streams (clamped
+  // index: an unconditional global load)
+  if (gw >= nitems) return;
+  int4 info = ws.rowA[gw / per_row];
   for (int item = gw; item < nitems; item += W) {
-    const int4 info1 = item + W < nitems ? ws.rowA[(item + W) / per_row] : dflt;
+    const int nxt = item + W < nitems ? item + W : item;
+    const int4 info1 = ws.rowA[nxt / per_row];
     LseRaw<T> cur;
     {
       const T* row;
