@@ -547,6 +547,131 @@ __global__ void __launch_bounds__(kRnnKSplit * 3 * kRnnUnits) rnn_step_batched_k
   }
 }
 
+// The RNN step on the matrix cores (r >= 32).  Workgroup (request block, unit block) forms
+// G = W_gco[:, :2r] [s_{k-1}; e] for 32 requests x 32 units of each of the gate, candidate
+// and output rows: three 32x32 accumulators (units on M, requests on N) that share the B
+// operand.  The four waves take quarters of the 2r inputs (two of s, two of e), each
+// issuing all of its loads before its matrix chain: A is the packed [s; e] weight chunk of
+// 32 consecutive rows (one coalesced load per half-wave), B is s_{k-1} entered as hi + lo
+// bf16 terms (two MFMAs) or the bf16 row W1[x_{k-1}] (one).  The accumulators meet
+// in LDS; wave w then finishes accumulator registers 4w .. 4w + 4 (four consecutive units
+// of every request): the four quarters in order, the two h-projection halves, the
+// nonlinearities and the state update.  s is double-buffered across steps (s_in -> s_out).
+constexpr int kStepWaves = 4;
+__global__ void __launch_bounds__(kStepWaves * kWave) rnn_step_mfma_kernel(
+    int R, int gamma, int V, int r, const uint16_t* __restrict__ W1,
+    const uint4* __restrict__ Wp, const float* __restrict__ Gh, const int32_t* prev,
+    int prev_stride, uint32_t k, const float* __restrict__ s_in, float* __restrict__ s_out,
+    float* __restrict__ orow, int32_t* status) {
+  __shared__ float part[kStepWaves][3][16][kWave];
+  const int q0 = blockIdx.x * 32, u0 = blockIdx.y * 32;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5;
+  const int qn = q0 + n < R ? q0 + n : R - 1;  // this lane's request (clamped for loads)
+  const int r3 = 3 * r, cps = r / 8, per = r / 32;
+  // the finishing step's operands first (they depend on nothing computed here): the two
+  // h-projection halves and s_{k-1} of this lane's four units (accumulator registers
+  // 4 wave .. 4 wave + 4: units u0 + 8 wave + 4 h .. + 4 of request q0 + n)
+  const int ub = u0 + 8 * wave + 4 * h;
+  const float* gh0 = Gh + ((size_t)qn * gamma + (k - 1)) * r3;
+  const float* gh1 = gh0 + (size_t)R * gamma * r3;  // the second K half
+  float4 gp[3][2];
+#pragma unroll
+  for (int g = 0; g < 3; ++g) {
+    gp[g][0] = *reinterpret_cast<const float4*>(gh0 + g * r + ub);
+    gp[g][1] = *reinterpret_cast<const float4*>(gh1 + g * r + ub);
+  }
+  const float4 sp = *reinterpret_cast<const float4*>(s_in + (size_t)qn * r + ub);
+
+  // k-steps (16 inputs) over [s; e]: r / 16 in each part; r >= 32 makes their count a
+  // multiple of 4, so waves 0 and 1 take s and waves 2 and 3 take e, per = r / 32 each;
+  // every load of the wave goes out first (clamped k-steps past `per`), then its chain
+  constexpr int kMaxPer = 8;  // r <= 256
+  const int ks0 = (wave & 1) * per;  // k-step inside the wave's part
+  f32x16 acc[3];
+#pragma unroll
+  for (int g = 0; g < 3; ++g)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[g][j] = 0.0f;
+  uint4 a[kMaxPer][3];
+  const int kbase = wave < 2 ? 0 : cps;  // chunk offset of the wave's part in [s; e]
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int c8 = 2 * (ks0 + (i < per ? i : 0)) + h;  // chunk inside the part
+#pragma unroll
+    for (int g = 0; g < 3; ++g) a[i][g] = Wp[(size_t)(kbase + c8) * r3 + g * r + u0 + n];
+  }
+  if (wave < 2) {  // s_{k-1} as hi + lo bf16 terms
+    float4 xs[kMaxPer][2];
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int c8 = 2 * (ks0 + (i < per ? i : 0)) + h;
+      xs[i][0] = *reinterpret_cast<const float4*>(s_in + (size_t)qn * r + 8 * c8);
+      xs[i][1] = *reinterpret_cast<const float4*>(s_in + (size_t)qn * r + 8 * c8 + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      if (i < per) {
+        const float x[8] = {xs[i][0].x, xs[i][0].y, xs[i][0].z, xs[i][0].w,
+                            xs[i][1].x, xs[i][1].y, xs[i][1].z, xs[i][1].w};
+        uint4 hi, lo;
+        split8(x, hi, lo);
+#pragma unroll
+        for (int g = 0; g < 3; ++g) {
+          acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][g]), as_bf16x8(hi), acc[g], 0, 0, 0);
+          acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][g]), as_bf16x8(lo), acc[g], 0, 0, 0);
+        }
+      }
+    }
+  } else {  // the bf16 row W1[x_{k-1}]
+    const int32_t tk = checked_token(prev[(size_t)qn * prev_stride], V, status);
+    const uint16_t* erow = W1 + (size_t)tk * r;
+    uint4 ev[kMaxPer];
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int c8 = 2 * (ks0 + (i < per ? i : 0)) + h;
+      ev[i] = *reinterpret_cast<const uint4*>(erow + 8 * c8);
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      if (i < per) {
+#pragma unroll
+        for (int g = 0; g < 3; ++g)
+          acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i][g]), as_bf16x8(ev[i]), acc[g], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 3; ++g)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) part[wave][g][j][lane] = acc[g][j];
+  __syncthreads();
+  const int q = q0 + n;
+  if (q >= R) return;
+  float G[3][4];
+#pragma unroll
+  for (int g = 0; g < 3; ++g) {
+    const float b[4] = {gp[g][0].x + gp[g][1].x, gp[g][0].y + gp[g][1].y,
+                        gp[g][0].z + gp[g][1].z, gp[g][0].w + gp[g][1].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float v = b[t];
+#pragma unroll
+      for (int w = 0; w < kStepWaves; ++w) v += part[w][g][4 * wave + t][lane];
+      G[g][t] = v;
+    }
+  }
+  const float sv[4] = {sp.x, sp.y, sp.z, sp.w};
+  float so[4], oo[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float gt = 1.0f / (1.0f + expf(-G[0][t]));
+    so[t] = gt * sv[t] + (1.0f - gt) * tanhf(G[1][t]);
+    oo[t] = tanhf(G[2][t]);
+  }
+  *reinterpret_cast<float4*>(s_out + (size_t)q * r + ub) = make_float4(so[0], so[1], so[2], so[3]);
+  *reinterpret_cast<float4*>(orow + (size_t)q * r + ub) = make_float4(oo[0], oo[1], oo[2], oo[3]);
+}
+
 // ---------------------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------------------
@@ -656,7 +781,14 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
   for (int k = 1; k <= gamma; ++k) {
     const int32_t* prev = (k == 1) ? x0 : x + (k - 2);
     const int ps = (k == 1) ? 1 : gamma;
-    if (rnn && BF) {
+    if (rnn && BF && r >= 32) {
+      float* s_in = (k & 1) ? ws.s : ws.s2;  // s_0 sits in ws.s
+      float* s_out = (k & 1) ? ws.s2 : ws.s;
+      const dim3 grid((R + 31) / 32, r / 32);
+      rnn_step_mfma_kernel<<<grid, kStepWaves * kWave, 0, stream>>>(
+          R, gamma, V, r, reinterpret_cast<const uint16_t*>(W1), ws.wpack, ws.Gh, prev, ps,
+          (uint32_t)k, s_in, s_out, ws.orow, status);
+    } else if (rnn && BF) {
       const int U = r < kRnnUnits ? r : kRnnUnits;
       const size_t sh = sizeof(float) * kRnnReq * (2 * r + kRnnKSplit * 3 * U);
       const dim3 grid((R + kRnnReq - 1) / kRnnReq, r / U);
