@@ -68,3 +68,34 @@ def test_schedule_single_request(ora, ds):
         g = ds.schedule(T(c), T(sps), 1, mode)
         assert np.array_equal(N(g["ell"]), ref["ell"]), mode
         assert np.array_equal(N(g["a"]), ref["a"].astype(np.float32))
+
+
+def test_empty_batch(ds):
+    """R = 0 is a no-op for every entry point of the hot path: no launch, no error, empty
+    outputs (include/dspark.h, size limits)."""
+    import torch
+    dev, bf = "cuda:0", torch.bfloat16
+    V, r, d, G = 1024, 32, 64, 4
+    U = torch.zeros((0, G, V), dtype=bf, device=dev)
+    h = torch.zeros((0, G, d), dtype=bf, device=dev)
+    W1 = torch.zeros((V, r), dtype=bf, device=dev)
+    W2t = torch.zeros((V, r), dtype=bf, device=dev)
+    w = torch.zeros(d + r, dtype=torch.float32, device=dev)
+    x0 = torch.zeros(0, dtype=torch.int32, device=dev)
+    o = ds.draft_markov(U, h, W1, W2t, w, x0, 0, 0)
+    assert tuple(o["x"].shape) == (0, G)
+    Wg = torch.zeros((3 * r, 2 * r + d), dtype=bf, device=dev)
+    o = ds.draft_rnn(U, h, W1, W2t, Wg, w, x0, 0, 0)
+    assert tuple(o["bias_rows"].shape) == (0, G, r)
+    c = torch.zeros((0, G), dtype=torch.float32, device=dev)
+    sps = torch.ones(8, dtype=torch.float32, device=dev)
+    s = ds.schedule(c, sps, 0, ds.SYNC_BREAK)
+    assert s["ell"].numel() == 0
+    target = torch.zeros((0, G + 1, V), dtype=bf, device=dev)
+    v = ds.verify(target, U, W2t, torch.zeros((0, G, r), dtype=bf, device=dev),
+                  torch.zeros((0, G), dtype=torch.int32, device=dev),
+                  torch.zeros((0, G), dtype=torch.float32, device=dev),
+                  torch.zeros((0, G), dtype=torch.float32, device=dev),
+                  torch.zeros(0, dtype=torch.int32, device=dev))
+    assert v["n_acc"].numel() == 0
+    torch.cuda.synchronize()

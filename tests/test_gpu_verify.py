@@ -35,6 +35,8 @@ def _inputs(ora, cfg, cycle, ell_kind, rnn=False):
         ell = s["ell"]
     elif ell_kind == "full":
         ell = np.full(cfg.R, cfg.gamma, np.int32)
+    elif ell_kind == "zero":  # nothing verified: every request draws from its row 1
+        ell = np.zeros(cfg.R, np.int32)
     else:
         ell = rng.integers(0, cfg.gamma + 1, cfg.R).astype(np.int32)
         ell[0] = 0
@@ -69,6 +71,7 @@ CASES = [
     ("c1-random", "c1", dict(R=9, V=1000), "random"),
     ("c2-random", "c2", dict(R=48, gamma=5, V=6000, d=256), "random"),
     ("c2-full", "c2", dict(R=33, gamma=4, V=4096, d=128, r=128), "full"),
+    ("c2-zero", "c2", dict(R=21, gamma=4, V=3000, d=128), "zero"),
     ("c2-sched", "c2", dict(R=64, gamma=4, V=8192, d=256), "sched"),
     ("c3-law", "c3", dict(R=40, gamma=6, V=16384, d=256), "random"),
 ]
