@@ -346,7 +346,11 @@ int dspark_train_forward(int R, int gamma, int V, int r, int d, dspark_dtype dt,
   p.lse = wsl.lse;
   p.status = dev_status;
   p.bpack = wsl.bpack;
-  const SweepGeom g = make_geom(rows, V, r, static_cast<const uint16_t*>(W2t), nranges);
+  SweepGeom g = make_geom(rows, V, r, static_cast<const uint16_t*>(W2t), nranges);
+  // one workgroup per (range, row group): the dispatch order runs a range's groups together on
+  // one XCD, so each W2t tile comes from HBM about once and from that XCD's L2 for the rest,
+  // and one workgroup's start overlaps another's sweep instead of following it
+  g.gsplit = g.ngroups;
   train_pack_kernel<<<(rows * (r / 8) + 255) / 256, 256, 0, stream>>>(p, wsl.bpack);
   launch_sweep<false, TrainLseEpi>(g, p, stream);
   train_merge_kernel<<<(rows + kTrainMergeRows - 1) / kTrainMergeRows, 64 * kTrainMergeRows, 0,
