@@ -172,6 +172,11 @@ def cpu_baseline(cfg, I, target_seconds):
                 cpu_model=cpu_model(), nproc=len(os.sched_getaffinity(0)))
 
 
+def sweep_bytes_of(R: int, V: int, r: int) -> int:
+    """Algorithmic bytes of one draft sweep: U_k rows, all of W2, the gathered W1 rows."""
+    return R * V * 2 + V * r * 2 + R * r * 2
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -204,6 +209,7 @@ def traffic_from(fetch_csv: str, write_csv: str) -> None:
                 copy.append(v)
         if not sweep or not copy:
             raise SystemExit(f"{path}: no {counter} rows for the draft sweep and the copy probe")
+        copy = [v for v in copy if v >= 0.9 * max(copy)]  # the probe copies are the largest
         return sum(sweep) / len(sweep), sum(copy) / len(copy), len(sweep)
 
     f_sweep, f_copy, n = per_kernel(fetch_csv, "FETCH_SIZE")
@@ -347,6 +353,22 @@ def main():
     t_sched = np.mean([e[1].elapsed_time(e[2]) for e in sev])
     t_ver = np.mean([e[2].elapsed_time(e[3]) for e in sev])
     cycle_median = float(np.median([e[0].elapsed_time(e[3]) for e in sev]))
+    # a plain device copy of the sweep's byte count (read + write), the practical HBM rate
+    # beside the spec peak; outside the timed region (not in counter runs, whose copies are
+    # the scaling probe)
+    copy_gbs = None
+    if not args.copy_probe:
+        cbuf = torch.empty(sweep_bytes_of(R, V, r) // 2, dtype=torch.bfloat16, device=dev)
+        cdst = torch.empty_like(cbuf)
+        cdst.copy_(cbuf)
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ce[0].record()
+        for _ in range(10):
+            cdst.copy_(cbuf)
+        ce[1].record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * cbuf.numel() * 2 * 10 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+        del cbuf, cdst
     if args.copy_probe:
         # a plain device copy of known size, for scaling the HBM byte counters
         a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
@@ -361,7 +383,7 @@ def main():
     emitted = int(n_acc.sum()) + R
 
     # algorithmic bytes of one draft sweep launch: U_k rows, all of W2, the gathered W1 rows
-    sweep_bytes = R * V * 2 + V * r * 2 + R * r * 2
+    sweep_bytes = sweep_bytes_of(R, V, r)
     achieved = sweep_bytes / (sweep_ms * 1e-3) / 1e9
     n_a, n_b = int(ell.sum()) + R, int(ell.sum())
     cycle_bytes = (G * sweep_bytes + R * G * d * 2) + (n_a * V * 2 + n_b * V * 2 + V * r * 2)
@@ -400,6 +422,7 @@ def main():
         "emitted_tokens_per_s": emitted / (ms_per_step * 1e-3),
         "stage_ms": {"draft": t_draft, "schedule": t_sched, "verify": t_ver},
         "cycle_ms_median": cycle_median,
+        "hbm_copy_gbs": copy_gbs,
         "draft_hbm_frac_w2_once": draft_bytes_w2_once / (t_draft * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "cycle_hbm_frac": cycle_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "verified_rows": n_b, "accepted": int(n_acc.sum()), "mean_ell": float(ell.mean()),
