@@ -72,7 +72,7 @@ static VerifyWs carve_verify(void* ws, int R, int gamma, int V, int r) {
 // ---------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) verify_prep_kernel(int R, int gamma, const int32_t* ell_in,
                                                            VerifyWs ws, int32_t* status) {
-  __shared__ int totA[1024], totB[1024];
+  __shared__ int totA[1024 / kWave], totB[1024 / kWave];
   const int per = (R + 1023) / 1024;
   const int lo = threadIdx.x * per, hi = min(R, lo + per);
   int sa = 0, sb = 0;
@@ -85,19 +85,41 @@ __global__ void __launch_bounds__(1024) verify_prep_kernel(int R, int gamma, con
     sa += L + 1;
     sb += L;
   }
-  totA[threadIdx.x] = sa;
-  totB[threadIdx.x] = sb;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int va = threadIdx.x >= off ? totA[threadIdx.x - off] : 0;
-    const int vb = threadIdx.x >= off ? totB[threadIdx.x - off] : 0;
-    __syncthreads();
-    totA[threadIdx.x] += va;
-    totB[threadIdx.x] += vb;
-    __syncthreads();
+  // exclusive prefix sums of the per-thread totals: inclusive scans inside each wave, then a
+  // scan of the 16 wave totals (two barriers)
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int ia = sa, ib = sb;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int ua = __shfl_up(ia, o, kWave), ub = __shfl_up(ib, o, kWave);
+    if (lane >= o) {
+      ia += ua;
+      ib += ub;
+    }
   }
-  int oa = threadIdx.x > 0 ? totA[threadIdx.x - 1] : 0;
-  int ob = threadIdx.x > 0 ? totB[threadIdx.x - 1] : 0;
+  if (lane == kWave - 1) {
+    totA[wave] = ia;
+    totB[wave] = ib;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int xa = lane < 1024 / kWave ? totA[lane] : 0, xb = lane < 1024 / kWave ? totB[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 1024 / kWave; o <<= 1) {
+      const int ua = __shfl_up(xa, o, kWave), ub = __shfl_up(xb, o, kWave);
+      if (lane >= o) {
+        xa += ua;
+        xb += ub;
+      }
+    }
+    if (lane < 1024 / kWave) {
+      totA[lane] = xa;  // inclusive totals through wave `lane`
+      totB[lane] = xb;
+    }
+  }
+  __syncthreads();
+  int oa = ia - sa + (wave > 0 ? totA[wave - 1] : 0);
+  int ob = ib - sb + (wave > 0 ? totB[wave - 1] : 0);
   for (int q = lo; q < hi; ++q) {
     int L = ell_in[q];
     L = L < 0 ? 0 : (L > gamma ? gamma : L);
@@ -109,15 +131,16 @@ __global__ void __launch_bounds__(1024) verify_prep_kernel(int R, int gamma, con
     ob += L;
   }
   if (threadIdx.x == 1023) {
-    ws.hdr[0] = totA[1023];
-    ws.hdr[1] = totB[1023];
+    ws.hdr[0] = totA[1024 / kWave - 1];
+    ws.hdr[1] = totB[1024 / kWave - 1];
   }
 }
 
 __device__ __forceinline__ int clamp_len(int L, int gamma) { return L < 0 ? 0 : (L > gamma ? gamma : L); }
 
 // ---------------------------------------------------------------------------------------
-// lse: (max, sum exp) of 256 blocks of a list-A row (+ first level of the bonus sample)
+// lse: (max, sum exp) of every 4096-id wave item of the list-A rows (+ first level of the
+// bonus sample)
 // ---------------------------------------------------------------------------------------
 // reductions over the 8 lanes 8k .. 8k+7 on the DPP network (xor 1, xor 2, then the
 // half-row mirror, which pairs the two quads)
