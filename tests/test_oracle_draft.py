@@ -133,6 +133,58 @@ def test_rnn_zero_output_gate_weights_reduce_to_U(ora):
                                atol=1e-12)
 
 
+def test_rnn_output_rows_on_e_reduce_to_markov(ora):
+    """eq. (6) with W_o = [0 | c I | 0]: the output rows read only the embedding block of z, so
+    o_k = tanh(c W1[x_{k-1}]) whatever the state, and the RNN head must draw exactly what the
+    Markov head (pinned above) draws with rows tanh(c W1).  The confidence's embedding weights
+    are zero so c_k depends on h alone in both.  Pins the block order of z and of W_gco's rows
+    and the use of o_k as the bias row."""
+    cfg = _small("rnn", R=4, gamma=5, V=96, r=8, d=6)
+    I = synth.inputs(cfg)
+    r, d, cs = cfg.r, cfg.d, 1.75  # exact in float32
+    Wg = I["W_gco"].copy()
+    Wg[2 * r:] = 0
+    Wg[2 * r:, r:2 * r] = cs * np.eye(r, dtype=np.float32)
+    w = I["w"].copy()
+    w[d:] = 0
+    out = ora.draft_rnn(I["U"], I["h"], I["W1"], I["W2"], Wg, w, I["x0"], 5, 3)
+    W1t = np.tanh(cs * I["W1"].astype(np.float64)).astype(np.float32)
+    ref = ora.draft_markov(I["U"], I["h"], W1t, I["W2"], w, I["x0"], 5, 3)
+    assert np.array_equal(out["x"], ref["x"])
+    np.testing.assert_allclose(out["lse"], ref["lse"], atol=1e-6)
+    np.testing.assert_allclose(out["logit_x"], ref["logit_x"], atol=1e-6)
+    np.testing.assert_allclose(out["c"], ref["c"], atol=1e-12)
+    np.testing.assert_allclose(out["bias_rows"], ref["bias_rows"], atol=1e-7)
+
+
+def test_rnn_state_recurrence_geometric_sum(ora):
+    """eq. (6) with a constant gate and a candidate that reads only e: h = 1 and
+    W_g = [0 | 0 | (a/d) 1] make every gate g = sigmoid(a); W_c = [0 | I | 0] makes the
+    candidate tanh(W1[x_{k-1}]); W_o = [b I | 0 | 0] outputs tanh(b s_{k-1}).  From s_0 = 0 the
+    state is the discounted sum s_k = (1 - g) sum_{i<=k} g^(k-i) tanh(W1[x_{i-1}]), so
+    o_k = tanh(b s_{k-1}).  Swapping g and 1 - g, the z or row blocks, or s_k and s_{k-1}
+    fails this."""
+    cfg = _small("rnn", R=3, gamma=6, V=80, r=4, d=5)
+    I = synth.inputs(cfg)
+    r, d, a, b = cfg.r, cfg.d, 1.25, 0.875  # a / d = 0.25 and b exact in float32
+    h = np.ones_like(I["h"])
+    Wg = np.zeros_like(I["W_gco"])
+    Wg[:r, 2 * r:] = a / d
+    Wg[r:2 * r, r:2 * r] = np.eye(r, dtype=np.float32)
+    Wg[2 * r:, :r] = b * np.eye(r, dtype=np.float32)
+    out = ora.draft_rnn(I["U"], h, I["W1"], I["W2"], Wg, I["w"], I["x0"], 2, 1)
+    g = special.expit(a)  # the gate's pre-activation: d entries of h = 1 times a / d
+    W1 = I["W1"].astype(np.float64)
+    for q in range(cfg.R):
+        toks = np.concatenate([[I["x0"][q]], out["x"][q, :-1]])  # x_0 .. x_{gamma-1}
+        for k in range(1, cfg.gamma + 1):
+            # s_{k-1} = (1 - g) sum_{i=1}^{k-1} g^{k-1-i} tanh(W1[x_{i-1}])
+            s_prev = np.zeros(r)
+            for i in range(1, k):
+                s_prev += (1 - g) * g ** (k - 1 - i) * np.tanh(W1[toks[i - 1]])
+            np.testing.assert_allclose(out["bias_rows"][q, k - 1], np.tanh(b * s_prev), atol=1e-12)
+
+
 def test_draft_rejects_bad_anchor(ora):
     cfg = _small(V=64)
     I = synth.inputs(cfg)
