@@ -48,12 +48,6 @@ inline int device_cus() {
   return cached_device_attribute(cache, hipDeviceAttributeMultiprocessorCount, 256);
 }
 
-// LDS the current device allows one workgroup
-inline size_t device_max_lds() {
-  static std::atomic<int> cache[64];
-  return (size_t)cached_device_attribute(cache, hipDeviceAttributeMaxSharedMemoryPerBlock, 65536);
-}
-
 // Raises a kernel's dynamic-LDS ceiling to `bytes` on the current device, once per device
 // (`done` is the kernel's own set of devices already raised).
 inline void ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done) {

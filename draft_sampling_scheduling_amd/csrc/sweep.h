@@ -16,8 +16,8 @@
 //   - Per 32-id tile the workgroup stages in LDS the tile's W2t rows (32 x r bf16, shared by
 //     all waves) and every wave's 32 x 32 slice of each streamed operand (U, and the target
 //     logits in verification).  Staging is asynchronous: the loads go straight to LDS
-//     (global_load_lds_dwordx4), three stages deep when two workgroups still fit a CU, so
-//     each tile's HBM traffic is issued two tiles ahead of its use and the matrix-core and
+//     (global_load_lds_dwordx4), two stages deep, so each tile's HBM traffic is issued one
+//     tile ahead of its use (while the CU's other workgroup computes) and the matrix-core and
 //     epilogue work of the current tile hides the memory latency.  The waits on those
 //     loads are explicit vmcnt waits.
 //   - MFMA 32x32x16 bf16 with A = W2t tile (vocabulary on M) and B = B^T (rows on N):
@@ -504,15 +504,14 @@ inline void launch_sweep_nks(const SweepGeom& g, const typename Epi::Params& p, 
     kern<<<g.nranges * g.gsplit, kSweepThreads, sh, s>>>(g, p);
 }
 
-// launch with NKS = r / 16 fixed at compile time (r in {16, 32, 64, 128, 256}) and three
-// pipeline stages when two workgroups still fit one CU's LDS, else two
+// launch with NKS = r / 16 fixed at compile time (r in {16, 32, 64, 128, 256}) and two
+// pipeline stages.  A third stage still fits two one-stream workgroups in a CU's LDS, but the
+// draft sweep at R = 256, V = 151936, r = 256 ran 32.4-35.4 us with three against
+// 29.8-31.8 us with two (interleaved runs on one device).
 template <int NKS, bool SPLIT, class Epi>
 inline void launch_sweep_stages(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s,
                                 hipEvent_t ev0, hipEvent_t ev1) {
-  if (2 * sweep_lds_bytes(g.r, Epi::kStreams, 3) <= device_max_lds())
-    launch_sweep_nks<NKS, SPLIT, 3, Epi>(g, p, s, ev0, ev1);
-  else
-    launch_sweep_nks<NKS, SPLIT, 2, Epi>(g, p, s, ev0, ev1);
+  launch_sweep_nks<NKS, SPLIT, 2, Epi>(g, p, s, ev0, ev1);
 }
 
 template <bool SPLIT, class Epi>
