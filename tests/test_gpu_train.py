@@ -46,6 +46,9 @@ CASES = [
     ("c2-R150-r64", "c2", dict(R=150, gamma=3, V=3000, r=64, d=256)),
     ("c2-r16-g1", "c2", dict(R=3, gamma=1, V=1024, r=16, d=64)),
     ("c4-law-g16", "c4", dict(R=9, gamma=16, V=4104, r=128, d=0)),
+    # 640 rows = 5 row groups: the sweeps take about 4 x CUs / 5 vocabulary ranges (200 on a
+    # 256-CU device), between the one-group and the many-group settings; V % 64 = 32
+    ("c3-rows640", "c3", dict(R=80, gamma=8, V=20000, r=64, d=256)),
 ]
 
 
