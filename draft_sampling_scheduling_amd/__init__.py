@@ -22,6 +22,7 @@ FIXED, THRESHOLD = 3, 4  # decode-driver length policies beyond the scheduler's 
 OK, EINVAL, ERANGE, EWORKSPACE, EDEVICE = 0, -1, -2, -3, -4
 FAULT_TOKEN, FAULT_CONF, FAULT_LEN = 1, 2, 4
 EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov", "dspark_draft_markov_timed",
+           "dspark_draft_markov_noalloc_max_bytes", "dspark_draft_markov_noalloc",
            "dspark_draft_rnn_workspace_bytes", "dspark_draft_rnn",
            "dspark_schedule_workspace_bytes", "dspark_schedule",
            "dspark_verify_workspace_bytes", "dspark_verify",
@@ -63,6 +64,10 @@ def lib():
         L.dspark_draft_markov.restype = i
         L.dspark_draft_markov_timed.argtypes = L.dspark_draft_markov.argtypes + [vp, vp]
         L.dspark_draft_markov_timed.restype = i
+        L.dspark_draft_markov_noalloc_max_bytes.argtypes = []
+        L.dspark_draft_markov_noalloc_max_bytes.restype = sz
+        L.dspark_draft_markov_noalloc.argtypes = [i] * 6 + [vp] * 7 + [u64, u64] + [vp] * 8
+        L.dspark_draft_markov_noalloc.restype = i
         L.dspark_draft_rnn.argtypes = ([i] * 6 + [vp] * 8 + [u64, u64] + [vp] * 7 +
                                        [vp, sz, vp])
         L.dspark_draft_rnn.restype = i
@@ -222,6 +227,45 @@ def draft_markov(U, h, W1, W2t, w, x0, seed=0, cycle=0, *, temps=None, out=None,
     the timed variant."""
     return _draft(False, U, h, W1, W2t, w, x0, seed, cycle, temps=temps, out=out, ws=ws,
                   status=status, events=events)
+
+
+def draft_markov_noalloc(U, h, W1, W2t, w, x0, seed=0, cycle=0, *, temps=None, out=None,
+                         status=None):
+    """dspark_draft_markov_noalloc: the Markov-head draft with the library's own device
+    workspace (no workspace argument; calls that overlap on one GPU race).  Same results
+    as draft_markov."""
+    torch = _torch()
+    _chk(U, "U")
+    R, gamma, V = U.shape
+    dt = _dt(U)
+    r = W1.shape[1]
+    d = h.shape[2]
+    _chk(h, "h", (R, gamma, d), U.dtype)
+    _chk(W1, "W1", (V, r), U.dtype)
+    _chk(W2t, "W2t", (V, r), U.dtype)
+    _chk(w, "w", (d + r,), torch.float32)
+    _chk(x0, "x0", (R,), torch.int32)
+    if temps is not None:
+        _chk(temps, "temps", (gamma,), torch.float32)
+    dev = U.device
+    if out is None:
+        out = dict(
+            x=torch.empty((R, gamma), dtype=torch.int32, device=dev),
+            c=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+            z=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+            lse=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+            logit_x=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+            bias_rows=torch.empty((R, gamma, r), dtype=U.dtype, device=dev))
+    rc = lib().dspark_draft_markov_noalloc(
+        R, gamma, V, r, d, dt, _p(U), _p(h), _p(W1), _p(W2t), _p(w), _p(temps), _p(x0), seed,
+        cycle, _p(out["x"]), _p(out["c"]), _p(out.get("z")), _p(out["lse"]),
+        _p(out["logit_x"]), _p(out["bias_rows"]), _p(status), _stream())
+    _raise("dspark_draft_markov_noalloc", rc)
+    return out
+
+
+def draft_markov_noalloc_max_bytes() -> int:
+    return int(lib().dspark_draft_markov_noalloc_max_bytes())
 
 
 def draft_rnn(U, h, W1, W2t, W_gco, w, x0, seed=0, cycle=0, *, temps=None, out=None, ws=None,

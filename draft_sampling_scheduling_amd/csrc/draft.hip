@@ -885,9 +885,53 @@ static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_d
                           x, c, z, lse, logit_x, bias_rows, status, lay, stream, evb, eve);
 }
 
+// ---------------------------------------------------------------------------------------
+// allocation-free variant: the workspace is a library-owned device array, one per GPU
+// (each device's code object holds its own copy until the process ends).  In host code the
+// array's name is only a stand-in for the symbol, so its device address is looked up once
+// per device with hipGetSymbolAddress and that address is what the kernels receive.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// the scratch array's device address on the current device (null on failure); the first
+// call on a device looks it up, later calls read the per-device cache (concurrent first
+// calls both look it up and store the same address)
+static void* scratch_on_device() {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  addr[dev].store(q, std::memory_order_release);
+  return q;
+}
+
 }  // namespace dspark
 
 extern "C" {
+
+size_t dspark_draft_markov_noalloc_max_bytes(void) { return dspark::kNoAllocScratchBytes; }
+
+int dspark_draft_markov_noalloc(int R, int gamma, int V, int r, int d, dspark_dtype dt,
+                                const void* U, const void* h, const void* W1, const void* W2t,
+                                const float* w, const float* temps, const int32_t* x0,
+                                uint64_t seed, uint64_t cycle, int32_t* x, float* c, float* z,
+                                float* lse, float* logit_x, void* bias_rows,
+                                int32_t* dev_status, hipStream_t stream) {
+  using namespace dspark;
+  if (!dims_ok(R, gamma, V, r, d)) return DSPARK_EINVAL;
+  if (carve_draft(nullptr, R, gamma, V, r, d, false).bytes > kNoAllocScratchBytes)
+    return DSPARK_ERANGE;
+  if (R == 0) return DSPARK_OK;
+  void* ws = scratch_on_device();
+  if (!ws) return DSPARK_EDEVICE;
+  return draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, temps, x0, seed,
+                     cycle, x, c, z, lse, logit_x, bias_rows, dev_status, ws,
+                     kNoAllocScratchBytes, stream);
+}
 
 size_t dspark_draft_workspace_bytes(int R, int gamma, int V, int r, int d) {
   if (!dspark::dims_ok(R, gamma, V, r, d)) return 0;

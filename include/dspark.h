@@ -132,6 +132,25 @@ int dspark_draft_markov_timed(int R, int gamma, int V, int r, int d, dspark_dtyp
                               void *ws, size_t ws_bytes, hipStream_t stream,
                               hipEvent_t *ev_begin, hipEvent_t *ev_end);
 
+/* Allocation-free variant of dspark_draft_markov, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments and results are those of dspark_draft_markov without
+ * ws / ws_bytes: the workspace is a library-owned device array of
+ * dspark_draft_markov_noalloc_max_bytes() bytes (16 MiB), one per GPU, which that GPU holds
+ * until the process ends.  The call allocates nothing.  DSPARK_ERANGE if the shapes need
+ * more than that (dspark_draft_workspace_bytes(...) larger than the maximum; R = 512,
+ * V = 151936, r = 256 needs about 8.3 MiB).  Every call on one GPU shares its array:
+ * calls that overlap on one GPU (different streams, or host threads) race and must be
+ * serialised by the caller; calls on one stream are ordered and safe. */
+size_t dspark_draft_markov_noalloc_max_bytes(void);
+
+int dspark_draft_markov_noalloc(int R, int gamma, int V, int r, int d, dspark_dtype dt,
+                                const void *U, const void *h, const void *W1, const void *W2t,
+                                const float *w, const float *temps, const int32_t *x0,
+                                uint64_t seed, uint64_t cycle, int32_t *x, float *c, float *z,
+                                float *lse, float *logit_x, void *bias_rows,
+                                int32_t *dev_status, hipStream_t stream);
+
 /* RNN head, eq. (6): W_gco [3r][2r + d] dt stacks the gate, candidate and output
  * projections (row blocks in that order; columns ordered [s ; W1 row ; h]; no biases);
  * s_0 = 0.  The bias row of step k is tanh(W_o z_k) with z_k holding s_{k-1}; c uses eq.

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(ds):
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(ds.lib(), n), n
     assert set(names) == set(ds.EXPORTS)
@@ -63,6 +63,24 @@ def test_draft_rejects_bad_arguments(ds):
     assert call(ws_bytes=ws - 1) == ds.EWORKSPACE
     assert call(cycle=1 << 28) == ds.EINVAL
     assert call(R=0) == ds.OK  # empty batch: nothing to do
+
+
+def test_draft_noalloc_rejects_before_launch(ds):
+    L = ds.lib()
+    assert ds.draft_markov_noalloc_max_bytes() == 16 << 20
+
+    def call(R=4, gamma=4, V=1024, r=16, d=64):
+        return L.dspark_draft_markov_noalloc(R, gamma, V, r, d, ds.BF16, FAKE, FAKE, FAKE, FAKE,
+                                             FAKE, None, FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE,
+                                             FAKE, FAKE, None, None)
+
+    assert call(V=1001) == ds.EINVAL
+    assert call(r=24) == ds.EINVAL
+    # the shapes need more than the library's scratch array
+    assert ds.draft_workspace_bytes(1100, 8, 151936, 256, 4096) > 16 << 20
+    assert call(R=1100, gamma=8, V=151936, r=256, d=4096) == ds.ERANGE
+    assert ds.draft_workspace_bytes(512, 16, 151936, 256, 5120) <= 16 << 20
+    assert call(R=0) == ds.OK
 
 
 def test_schedule_rejects_bad_arguments(ds):
