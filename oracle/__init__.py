@@ -61,6 +61,9 @@ def lib():
         L.ora_schedule.argtypes = [C.c_int, C.c_int, f32p, f32p, C.c_int, f32p, C.c_int,
                                    C.c_int, C.c_int, i32p, f32p, f64p, f64p]
         L.ora_schedule.restype = C.c_int
+        L.ora_schedule_literal.argtypes = [C.c_int, C.c_int, f32p, f32p, C.c_int, C.c_int,
+                                           C.c_int, i32p, f64p]
+        L.ora_schedule_literal.restype = C.c_int
         L.ora_verify.argtypes = ([C.c_int] * 5 + [vp, vp, vp, f64p, i32p, i32p, i32p, C.c_uint64,
                                  C.c_uint64, i32p, i32p, f64p, f64p, f64p, f64p, f64p])
         L.ora_verify.restype = C.c_int
@@ -304,6 +307,22 @@ def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, trace=False):
     if rc != 0:
         raise ValueError(f"oracle schedule rejected its arguments (rc={rc})")
     return dict(ell=ell, a=a, stats=stats, theta=theta)
+
+
+def schedule_literal(c, sps, sps_B0, brk=True):
+    """Algorithm 1 with single-precision running sums (the literal reading).  Returns
+    dict(ell, theta) with theta the float Theta of every prefix (NaN past |E|)."""
+    c = _c(c, np.float32)
+    R, gamma = c.shape
+    sps = _c(sps, np.float32)
+    ell = np.zeros(R, np.int32)
+    theta = np.zeros(R * gamma + 1)
+    rc = lib().ora_schedule_literal(R, gamma, _p(c, C.c_float), _p(sps, C.c_float), sps_B0,
+                                    sps.size, 1 if brk else 0, _p(ell, C.c_int32),
+                                    _p(theta, C.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle schedule_literal rejected its arguments (rc={rc})")
+    return dict(ell=ell, theta=theta)
 
 
 def schedule_rc(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None) -> int:

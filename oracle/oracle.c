@@ -698,6 +698,44 @@ int ora_schedule(int R, int gamma, const float *c, const float *c_lag, int R_lag
   return 0;
 }
 
+/* The same walk with single-precision running sums, as Algorithm 1 prints them:
+ * tau <- tau + a (float), Theta = tau * SPS(B) (float), the comparison Theta > Theta_best. */
+int ora_schedule_literal(int R, int gamma, const float *c, const float *sps, int sps_B0,
+                         int sps_len, int brk, int32_t *ell, double *theta_trace) {
+  if (R < 1 || gamma < 1 || !c || !sps || !ell || sps_len < 1) return -1;
+  if (sps_B0 > R || sps_B0 + sps_len - 1 < R * (1 + gamma)) return -2;
+  size_t N = (size_t)R * (size_t)gamma;
+  float *aa = (float *)malloc(sizeof(float) * N);
+  cand_t *E = (cand_t *)malloc(sizeof(cand_t) * (N ? N : 1));
+  int n_cand = build_candidates(R, gamma, c, aa, E);
+  if (n_cand < 0) {
+    free(aa); free(E);
+    return -1;
+  }
+  if (theta_trace)
+    for (size_t n = 0; n <= N; ++n) theta_trace[n] = NAN;
+  volatile float tau = (float)R;
+  volatile float best = tau * sps[R - sps_B0];
+  if (theta_trace) theta_trace[0] = best;
+  int n_adm = 0;
+  for (int n = 1; n <= n_cand; ++n) {
+    tau = tau + E[n - 1].a;
+    volatile float theta = tau * sps[R + n - sps_B0];
+    if (theta_trace) theta_trace[n] = theta;
+    if (theta > best) {
+      best = theta;
+      n_adm = n;
+    } else if (brk) {
+      break;
+    }
+  }
+  for (int r = 0; r < R; ++r) ell[r] = 0;
+  for (int n = 0; n < n_adm; ++n) ell[E[n].r] += 1;
+  free(aa);
+  free(E);
+  return 0;
+}
+
 /* ------------------------------------------------------------------------------------
  * Verification.  For request r with scheduled length l = ell[r], positions j = 1..l:
  *   p_j = softmax(target row j), q_j = softmax(U_j + bias_j W2) (recomputed here),

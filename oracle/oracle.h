@@ -168,6 +168,16 @@ int ora_schedule(int R, int gamma, const float *c, const float *c_lag, int R_lag
                  const float *sps, int sps_B0, int sps_len, int mode, int32_t *ell,
                  float *a, double *stats, double *theta_trace);
 
+/* Algorithm 1 with its running sums taken literally in single precision (digest, Module E:
+ * tau* <- tau* + a and Theta = tau* x SPS(B) as float operations, tau* starting at R), on
+ * the same candidate order as ora_schedule.  brk != 0: the early-stop break (SYNC_BREAK);
+ * brk == 0: no break, the first largest Theta (GLOBAL).  Used to measure how often the
+ * exact fixed-point reading of ora_schedule decides differently (only where two Theta
+ * values lie within the single-precision rounding of each other).  theta_trace [R*gamma+1]
+ * (nullable) receives the float Theta_n of every prefix (NaN past |E|). */
+int ora_schedule_literal(int R, int gamma, const float *c, const float *sps, int sps_B0,
+                         int sps_len, int brk, int32_t *ell, double *theta_trace);
+
 /* Lossless verification of the scheduled prefixes ([digest] overall cycle step 3,
  * [explainer] section 06 rule, eq. (8) for c*).
  *   target [R][gamma+1][V] (dt): target logits for draft positions 1..gamma and the

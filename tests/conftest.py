@@ -18,3 +18,14 @@ def ora():
     import oracle
     oracle.lib()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """The session's near-tie tally (printed also under -q)."""
+    from tests.gpu_util import TALLY
+    n, e = TALLY["compared"], TALLY["excused"]
+    if n:
+        terminalreporter.write_line(
+            f"parity tally: {e} near-tie mismatches excused of {n} tokens and acceptance "
+            f"decisions compared ({100.0 * e / n:.4f} %, budget 0.1 %) over "
+            f"{len(TALLY['cases'])} cases")

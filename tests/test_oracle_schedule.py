@@ -183,3 +183,50 @@ def test_error_codes(ora):
     bad[1, 1] = 1.5
     assert ora.schedule_rc(bad, sps, 4) == -1
     assert ora.schedule_rc(c, sps, 4, ASYNC) == -1         # no lagged confidences
+
+
+@pytest.mark.parametrize("brk", [True, False], ids=["sync-break", "global"])
+def test_literal_running_sum_differs_only_at_theta_near_ties(ora, brk):
+    """Reading of Algorithm 1's precision (digest, Module E): the oracle keeps tau exactly
+    (2^-32 fixed point) and Theta in double; the page's loop read literally keeps tau and
+    Theta in single precision.  Wherever the two admit different counts, the decision that
+    differs compares two Theta values closer than the single-precision summation error
+    ((n + 2) 2^-24 relative after n additions).  The disagreement count is printed."""
+    from tests.sched_sets import _conf_sets, _sps
+    u = 2.0 ** -24
+    differ = []
+    sets = [(name, c, *_sps(kind, *c.shape)) for name, c, _, kind in _conf_sets()]
+    # a flat Theta: every a = 0.7 and SPS(B) = 1 / (R + 0.7 (B - R)) rounded to float, so
+    # Theta_n = 1 up to rounding and every decision is a near-tie
+    Rf = 3000
+    cf = np.tile(np.array([0.7, 1.0], np.float32), (Rf, 1))
+    Bf = np.arange(Rf, 3 * Rf + 1, dtype=np.float64)
+    sets.append(("flat-theta", cf, (1.0 / (Rf + 0.7 * (Bf - Rf))).astype(np.float32), Rf))
+    for name, c, sps, B0 in sets:
+        R, gamma = c.shape
+        ex = ora.schedule(c, sps, B0, SYNC if brk else GLOBAL, trace=True)
+        lit = ora.schedule_literal(c, sps, B0, brk=brk)
+        th, thl = ex["theta"], lit["theta"]
+        n_cand = int(np.sum(np.isfinite(th))) - 1
+        tol = lambda m: (m + 2) * u * th[m] * 1.01  # noqa: E731
+        n_ex, n_lit = int(ex["stats"][3]), int(lit["ell"].sum())
+        # the single-precision Theta stays within its error bound of the exact one
+        fin = np.isfinite(thl)
+        m = np.nonzero(fin)[0]
+        assert np.all(np.abs(thl[fin] - th[fin]) <= np.array([tol(k) for k in m])), name
+        if n_ex == n_lit:
+            assert np.array_equal(ex["ell"], lit["ell"]), name
+            continue
+        differ.append((name, n_ex, n_lit))
+        if brk:
+            # first step whose improve/stop decision differs
+            k = 1
+            while k <= n_cand and (th[k] > th[k - 1]) == (thl[k] > thl[k - 1]) and th[k] > th[k - 1]:
+                k += 1
+            assert abs(th[k] - th[k - 1]) <= tol(k) + tol(k - 1), (name, k, th[k], th[k - 1])
+        else:
+            assert th[n_ex] - th[n_lit] <= tol(n_ex) + tol(n_lit), (name, n_ex, n_lit)
+    if not brk:  # without the break the flat case's argmax is decided by rounding alone
+        assert any(d[0] == "flat-theta" for d in differ)
+    print(f"literal single-precision sums: {len(differ)} of {len(sets)} confidence "
+          f"sets admit a different count ({'break' if brk else 'no break'}): {differ}")
