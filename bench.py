@@ -6,11 +6,13 @@ draft positions, V=151936, r=256, d=4096, bf16 operands with fp32 softmax):
   dspark_draft_markov  (gamma vocabulary sweeps + combines)
   dspark_schedule      (Algorithm 1 with the early-stop break)
   dspark_verify        (rejection sampling of the scheduled prefixes, c*)
-All inputs are seeded synthetic tensors already resident in device memory.  The target
-logits that verification reads are a synthetic stand-in for the target model (the drafted
-logits plus noise, plus a fresh bonus row), built once before timing for the cycle's drafted
-tokens; every timed step redoes the whole cycle on the same inputs and seed, so the drafted
-tokens and the target stay consistent.
+  next anchors         (each request's last emitted token starts its next cycle)
+All inputs are seeded synthetic tensors already resident in device memory.  Cycle t uses
+random-counter cycle t and the anchors cycle t-1 emitted, so the drafted tokens and the
+scheduled lengths change from cycle to cycle.  The target logits that verification reads are
+a synthetic stand-in for the target model (the drafted logits plus noise, plus a fresh bonus
+row), built for every cycle on an untimed first pass over the same chain of cycles; the
+timed pass reproduces that chain token for token (checked).
 
 Printed: one JSON line with the metric, the roofline of the dominant kernel (the draft
 sweep, timed live with HIP events around each of its launches), and the CPU oracle timed on
@@ -251,7 +253,14 @@ def main():
         return bench_decode(args)
     if args.workload == "rnn":
         return bench_rnn(args)
+    return bench_cycle(args)
 
+
+def bench_cycle(args):
+    """The decode cycle, advanced as the method runs it: cycle t drafts from the anchors
+    that cycle t-1 emitted (its last token per request), with random-counter cycle t; the
+    target stand-in of every cycle is built beforehand (untimed) on a first pass over the
+    same cycles, and the timed pass must reproduce that pass's emitted tokens exactly."""
     import numpy as np
     import torch
 
@@ -272,8 +281,8 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    U, h, W1, w, x0 = T(I["U"]), T(I["h"]), T(I["W1"]), T(I["w"]), T(I["x0"])
-    W2t = T(np.ascontiguousarray(I["W2"].T))
+    U, h, W1, w, x0_first = T(I["U"]), T(I["h"]), T(I["W1"]), T(I["w"]), T(I["x0"])
+    W2t = ds.w2_relayout(T(I["W2"]))  # the pages' [r][V] -> [V][r]
     sps = T(synth.sps_table(cfg))
     R, G, V, r, d = cfg.R, cfg.gamma, cfg.V, cfg.r, cfg.d
     gen_s = time.perf_counter() - t_gen
@@ -294,20 +303,12 @@ def main():
     dws = torch.empty(ds.draft_workspace_bytes(R, G, V, r, d), dtype=torch.uint8, device=dev)
     vws = torch.empty(ds.verify_workspace_bytes(R, G, V, r), dtype=torch.uint8, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-
-    # the cycle's drafted tokens, then the target stand-in for them
-    ds.draft_markov(U, h, W1, W2t, w, x0, SEED, CYCLE, out=dout, ws=dws, status=status)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(1234)
-    target = make_target(torch, cfg, U, W2t, dout, gen)
-    torch.cuda.synchronize()
-    log("target stand-in built")
+    x0 = torch.empty_like(x0_first)
 
     nsteps = args.warmup + args.steps
-    # one sweep launch per step is bracketed by events (draft position k = step mod gamma,
+    # one sweep launch per cycle is bracketed by events (draft position k = cycle mod gamma,
     # so every position is sampled); the other positions run unbracketed
     hip, evs = hip_events(2 * nsteps)
-    null = C.c_void_p()
 
     def ev_arrays(i):
         k = i % G
@@ -317,42 +318,66 @@ def main():
 
     ev_args = [ev_arrays(i) for i in range(nsteps)]
 
-    def step(i=None, stage_ev=None):
-        e = stage_ev
-        if e: e[0].record()
-        ds.draft_markov(U, h, W1, W2t, w, x0, SEED, CYCLE, out=dout, ws=dws, status=status,
-                        events=ev_args[i] if i is not None else None)
-        if e: e[1].record()
-        ds.schedule(dout["c"], sps, cfg.sps_B0, ds.SYNC_BREAK, out=sout, status=status)
-        if e: e[2].record()
-        ds.verify(target, U, W2t, dout["bias_rows"], dout["x"], dout["lse"], dout["logit_x"],
-                  sout["ell"], SEED, CYCLE, out=vout, ws=vws, status=status)
-        if e: e[3].record()
+    def next_anchors():
+        # the last emitted token of every request: y[q][n_acc[q]]
+        x0.copy_(vout["y"].gather(1, vout["n_acc"].long()[:, None])[:, 0])
 
-    for i in range(args.warmup):
-        step(i)
+    # first pass (untimed): the chain of cycles, each cycle's target stand-in built for the
+    # tokens it drafted; the emitted tokens are kept to check the timed pass
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    targets, emitted_ref, ells = [], [], []
+    x0.copy_(x0_first)
+    for t in range(nsteps):
+        ds.draft_markov(U, h, W1, W2t, w, x0, SEED, t, out=dout, ws=dws, status=status)
+        targets.append(make_target(torch, cfg, U, W2t, dout, gen))
+        ds.schedule(dout["c"], sps, cfg.sps_B0, ds.SYNC_BREAK, out=sout, status=status)
+        ds.verify(targets[t], U, W2t, dout["bias_rows"], dout["x"], dout["lse"],
+                  dout["logit_x"], sout["ell"], SEED, t, out=vout, ws=vws, status=status)
+        emitted_ref.append(vout["y"].clone())
+        ells.append(sout["ell"].clone())
+        next_anchors()
+    torch.cuda.synchronize()
+    log(f"{nsteps} cycles drafted once and their target stand-ins built")
+
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nsteps)]
+
+    def cycle(t):
+        e = sev[t]
+        e[0].record()
+        ds.draft_markov(U, h, W1, W2t, w, x0, SEED, t, out=dout, ws=dws, status=status,
+                        events=ev_args[t])
+        e[1].record()
+        ds.schedule(dout["c"], sps, cfg.sps_B0, ds.SYNC_BREAK, out=sout, status=status)
+        e[2].record()
+        ds.verify(targets[t], U, W2t, dout["bias_rows"], dout["x"], dout["lse"],
+                  dout["logit_x"], sout["ell"], SEED, t, out=vout, ws=vws, status=status)
+        e[3].record()
+        next_anchors()
+
+    x0.copy_(x0_first)
+    for t in range(args.warmup):
+        cycle(t)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.warmup, nsteps):
-        step(i)
+    for t in range(args.warmup, nsteps):
+        cycle(t)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"{args.steps} timed cycles: {wall * 1e3 / args.steps:.3f} ms each")
     if int(status.item()) != 0:
         raise SystemExit(f"device fault bits set: {int(status.item())}")
+    # the last timed cycle reproduces the first pass (same anchors, seeds and counters)
+    if not torch.equal(vout["y"], emitted_ref[-1]):
+        raise SystemExit("the timed cycles did not reproduce the first pass's tokens")
     timed = range(args.warmup, nsteps)
-    sweep_ms = np.mean([elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in timed])
+    sweep_ms = float(np.mean([elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in timed]))
+    t_draft = float(np.mean([sev[t][0].elapsed_time(sev[t][1]) for t in timed]))
+    t_sched = float(np.mean([sev[t][1].elapsed_time(sev[t][2]) for t in timed]))
+    t_ver = float(np.mean([sev[t][2].elapsed_time(sev[t][3]) for t in timed]))
+    cycle_median = float(np.median([sev[t][0].elapsed_time(sev[t][3]) for t in timed]))
+    ell_all = torch.stack([ells[t] for t in timed]).cpu().numpy()
 
-    # stage breakdown, outside the timed region (its events add gaps of their own)
-    nb = min(20, args.steps)
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
-    for i in range(nb):
-        step(None, sev[i])
-    torch.cuda.synchronize()
-    t_draft = np.mean([e[0].elapsed_time(e[1]) for e in sev])
-    t_sched = np.mean([e[1].elapsed_time(e[2]) for e in sev])
-    t_ver = np.mean([e[2].elapsed_time(e[3]) for e in sev])
-    cycle_median = float(np.median([e[0].elapsed_time(e[3]) for e in sev]))
     # a plain device copy of the sweep's byte count (read + write), the practical HBM rate
     # beside the spec peak; outside the timed region (not in counter runs, whose copies are
     # the scaling probe)
@@ -378,15 +403,18 @@ def main():
         torch.cuda.synchronize()
         log("copy probe: 3 device copies of 512 MiB")
     ms_per_step = wall * 1000.0 / args.steps
-    n_acc = vout["n_acc"].cpu().numpy()
-    ell = sout["ell"].cpu().numpy()
-    emitted = int(n_acc.sum()) + R
+    n_acc_sum = sum(int((emitted_ref[t] >= 0).sum()) for t in timed)  # emitted tokens
 
     # algorithmic bytes of one draft sweep launch: U_k rows, all of W2, the gathered W1 rows
     sweep_bytes = sweep_bytes_of(R, V, r)
     achieved = sweep_bytes / (sweep_ms * 1e-3) / 1e9
-    n_a, n_b = int(ell.sum()) + R, int(ell.sum())
-    cycle_bytes = (G * sweep_bytes + R * G * d * 2) + (n_a * V * 2 + n_b * V * 2 + V * r * 2)
+    # the Markov step (gather, bias contraction, logits, normaliser, sample, confidence) per
+    # position: U_k, W2, h_k and the gathered W1 rows; gamma positions per cycle
+    step_bytes = R * V * 2 + V * r * 2 + R * d * 2 + R * r * 2
+    draft_bytes = G * step_bytes
+    n_b = float(ell_all.sum(axis=1).mean())
+    n_a = n_b + R
+    cycle_bytes = draft_bytes + (n_a * V * 2 + n_b * V * 2 + V * r * 2)
     # the stricter view of the draft: W2 counted once per cycle (the last-level cache can
     # hold it), so only U_k, the W1 rows and h count per step
     draft_bytes_w2_once = G * (R * V * 2 + R * r * 2) + V * r * 2 + R * G * d * 2
@@ -413,19 +441,30 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: Markov head R={R} gamma={G} V={V} r={r} d={d}, "
-                               "bf16 operands, fp32 softmax; draft + schedule (early stop) + verify",
+                               "bf16 operands, fp32 softmax; draft + schedule (early stop) + "
+                               "verify, anchors from the previous cycle's last emitted tokens",
                    "R": R, "gamma": G, "V": V, "r": r, "d": d},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": f"draft sweep (sweep_kernel<{r // 16}, false, *, DraftEpi<false>>)",
                      "bytes_per_launch": sweep_bytes, "launch_us": sweep_ms * 1e3},
-        "emitted_tokens_per_s": emitted / (ms_per_step * 1e-3),
+        "markov_step_roofline": {
+            "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "achieved": draft_bytes / (t_draft * 1e-3) / 1e9,
+            "frac": draft_bytes / (t_draft * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_cycle": draft_bytes, "draft_us_per_cycle": t_draft * 1e3,
+            "us_per_step": t_draft * 1e3 / G,
+            "what": "the whole draft call (gamma positions: gather, bias contraction, logits, "
+                    "normaliser, two-level sample, confidence) against U_k + W2 + h_k + W1 rows "
+                    "per position"},
+        "emitted_tokens_per_s": n_acc_sum / len(timed) / (ms_per_step * 1e-3),
         "stage_ms": {"draft": t_draft, "schedule": t_sched, "verify": t_ver},
         "cycle_ms_median": cycle_median,
         "hbm_copy_gbs": copy_gbs,
         "draft_hbm_frac_w2_once": draft_bytes_w2_once / (t_draft * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "cycle_hbm_frac": cycle_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
-        "verified_rows": n_b, "accepted": int(n_acc.sum()), "mean_ell": float(ell.mean()),
+        "mean_verified_rows": n_b, "mean_ell": float(ell_all.mean()),
+        "ell_per_cycle": [int(v) for v in ell_all.sum(axis=1)],
         "input_gen_s": gen_s,
     }
     if not args.no_cpu_baseline:
@@ -476,7 +515,7 @@ def bench_train(args):
         return torch.from_numpy(a).to(dev)
 
     U, h, W1, w, x0 = T(I["U"]), T(I["h"]), T(I["W1"]), T(I["w"]), T(I["x0"])
-    W2t = T(np.ascontiguousarray(I["W2"].T))
+    W2t = ds.w2_relayout(T(I["W2"]))  # the pages' [r][V] -> [V][r]
     target, xstar = T(B["target"]), T(B["xstar"])
     R, G, V, r, d = cfg.R, cfg.gamma, cfg.V, cfg.r, cfg.d
     gen_s = time.perf_counter() - t_gen

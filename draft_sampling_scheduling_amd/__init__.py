@@ -29,7 +29,8 @@ EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov", "dspark_draft_
            "dspark_sts_workspace_bytes", "dspark_sts_fit",
            "dspark_train_forward_workspace_bytes", "dspark_train_forward",
            "dspark_decode_workspace_bytes", "dspark_decode_run",
-           "dspark_sps_profile", "dspark_sps_interpolate", "dspark_version")
+           "dspark_sps_profile", "dspark_sps_interpolate", "dspark_w2_relayout",
+           "dspark_version")
 
 _lib = None
 
@@ -100,6 +101,8 @@ def lib():
         L.dspark_sps_profile.restype = i
         L.dspark_sps_interpolate.argtypes = [i, vp, vp, i, i, vp]
         L.dspark_sps_interpolate.restype = i
+        L.dspark_w2_relayout.argtypes = [i, i, i, vp, vp, vp]
+        L.dspark_w2_relayout.restype = i
         L.dspark_version.restype = C.c_char_p
         _lib = L
     return _lib
@@ -166,6 +169,20 @@ def _raise(fn, rc):
 # ----------------------------------------------------------------------------------------
 # entry points (same names as the C ABI without the prefix)
 # ----------------------------------------------------------------------------------------
+def w2_relayout(W2, *, out=None):
+    """W2 [r][V] (the pages' layout) -> W2t [V][r], the layout the draft, verify, training
+    and decode calls take (dspark_w2_relayout; device tensors, same dtype)."""
+    torch = _torch()
+    _chk(W2, "W2")
+    r, V = W2.shape
+    dt = _dt(W2)
+    if out is None:
+        out = torch.empty((V, r), dtype=W2.dtype, device=W2.device)
+    _chk(out, "W2t", (V, r), W2.dtype)
+    _raise("dspark_w2_relayout", lib().dspark_w2_relayout(V, r, dt, _p(W2), _p(out), _stream()))
+    return out
+
+
 def draft_workspace_bytes(R, gamma, V, r, d) -> int:
     return int(lib().dspark_draft_workspace_bytes(R, gamma, V, r, d))
 
@@ -457,10 +474,11 @@ def decode_run(Ub, Hb, W1, W2t, w, Tb, x0, ncycles, policy=SYNC_BREAK, threshold
 
 
 def sps_profile(target, U, W2t, bias_rows, x, lse, logit_x, B_list, reps=10, *, ws=None,
-                status=None):
+                status=None, ell=None):
     """SPS(B) at the profiled batches B_list: the verification pass timed as the stand-in
     engine (steps/s).  Operands as verify(); returns a numpy float32 array [len(B_list)].
-    Synchronises with the current stream."""
+    ell: optional [R] int32 device tensor that receives the lengths of the last profiled
+    batch.  Synchronises with the current stream."""
     import numpy as np
     torch = _torch()
     _chk(U, "U")
@@ -472,7 +490,9 @@ def sps_profile(target, U, W2t, bias_rows, x, lse, logit_x, B_list, reps=10, *, 
     bl = np.ascontiguousarray(np.asarray(B_list, dtype=np.int32))
     sps = np.zeros(bl.size, np.float32)
     dev = U.device
-    ell = torch.empty(R, dtype=torch.int32, device=dev)
+    if ell is None:
+        ell = torch.empty(R, dtype=torch.int32, device=dev)
+    _chk(ell, "ell", (R,), torch.int32)
     n_acc = torch.empty(R, dtype=torch.int32, device=dev)
     y = torch.empty((R, gamma + 1), dtype=torch.int32, device=dev)
     cs = torch.empty((R, gamma), dtype=torch.float32, device=dev)

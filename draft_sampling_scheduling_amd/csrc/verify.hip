@@ -743,7 +743,14 @@ __global__ void __launch_bounds__(kFinalThreads) verify_final_kernel(
       }
       int idx = v;
       wave_argmax(score, idx);
-      token = idx;
+      // The block was chosen from the sweep's residual masses; recomputed here in another
+      // order, every rho of a block with rounding-level mass can come out <= 0.  No id of
+      // it may be emitted then (its residual probability is zero): the draw falls back to
+      // the target row, as for a zero residual mass.  The whole wave holds the same score.
+      token = score > -INFINITY
+                  ? idx
+                  : sample_row_wave<T>(trow, V, rng, kStreamResidBlk, kStreamResidIn,
+                                       (uint32_t)q, (uint32_t)js);
     } else {
       // the residual mass is zero in floating point: draw from the target row instead
       token = sample_row_wave<T>(trow, V, rng, kStreamResidBlk, kStreamResidIn, (uint32_t)q,

@@ -75,6 +75,20 @@ enum {
 enum { DSPARK_FAULT_TOKEN = 1, DSPARK_FAULT_CONF = 2, DSPARK_FAULT_LEN = 4 };
 
 /* ------------------------------------------------------------------------------------
+ * W2 re-layout (digest, Module B eq. (5): the Markov head's bias is W1[x] W2 with
+ * W2 in R^{r x V}).  The pages' W2 is [r][V] (row i holds coordinate i of every id); the
+ * draft, verify, training and decode calls read it transposed, W2t [V][r] (row v holds
+ * column v of W2, so a tile of consecutive ids is one contiguous run).  This call writes
+ *   W2t[v][i] = W2[i][v]   for v < V, i < r
+ * into caller memory (device pointers, V * r elements of dt each, not overlapping),
+ * asynchronously on `stream`.  Once per weight load; exact (a copy).
+ * DSPARK_EINVAL for V % 8 != 0, r outside {16,32,64,128,256}, a bad dt, a NULL or
+ * aliased pointer.
+ * ------------------------------------------------------------------------------------ */
+int dspark_w2_relayout(int V, int r, dspark_dtype dt, const void *W2, void *W2t,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * Draft (digest, Module B eq. (4) with the Markov head of eq. (5) or the RNN head of
  * eq. (6); confidence head eq. (7)).
  *
@@ -95,7 +109,8 @@ enum { DSPARK_FAULT_TOKEN = 1, DSPARK_FAULT_CONF = 2, DSPARK_FAULT_LEN = 4 };
  *   h   [R][gamma][d] dt   hidden states h_1..h_gamma
  *   W1  [V][r] dt          token embedding table (the low-rank factor W_1)
  *   W2t [V][r] dt          W_2 transposed: row v holds column v of W_2 in R^{r x V}
- *                          (the usual storage of an output projection)
+ *                          (the usual storage of an output projection; from the pages'
+ *                          [r][V] layout by dspark_w2_relayout)
  *   w   [d + r] float      confidence weights, ordered [h part ; W1-row part]
  *   temps [gamma] float    per-position temperatures (> 0), or NULL; a value that is not
  *                          > 0 sets DSPARK_FAULT_CONF and that position uses 1

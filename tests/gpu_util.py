@@ -29,12 +29,21 @@ def dev():
 
 
 def T(a):
-    """numpy -> device tensor (uint16 arrays are bf16 bit patterns)."""
+    """numpy -> device tensor (uint16 arrays are bf16 bit patterns); device tensors pass."""
     import torch
+    if isinstance(a, torch.Tensor):
+        return a
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(dev()).view(torch.bfloat16)
     return torch.from_numpy(a).to(dev())
+
+
+def W2T(W2):
+    """The pages' W2 [r][V] (numpy) on the device, re-laid out to W2t [V][r] by the
+    library's dspark_w2_relayout (the layout the hot-path calls take)."""
+    import draft_sampling_scheduling_amd as ds
+    return ds.w2_relayout(T(W2))
 
 
 def N(t):

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(ds):
     names = _declared()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(ds.lib(), n), n
     assert set(names) == set(ds.EXPORTS)
@@ -81,6 +81,16 @@ def test_draft_noalloc_rejects_before_launch(ds):
     assert call(R=1100, gamma=8, V=151936, r=256, d=4096) == ds.ERANGE
     assert ds.draft_workspace_bytes(512, 16, 151936, 256, 5120) <= 16 << 20
     assert call(R=0) == ds.OK
+
+
+def test_w2_relayout_rejects_bad_arguments(ds):
+    L = ds.lib()
+    other = C.c_void_p(0x2000)
+    assert L.dspark_w2_relayout(1001, 16, ds.BF16, FAKE, other, None) == ds.EINVAL
+    assert L.dspark_w2_relayout(1024, 48, ds.BF16, FAKE, other, None) == ds.EINVAL
+    assert L.dspark_w2_relayout(1024, 16, 5, FAKE, other, None) == ds.EINVAL
+    assert L.dspark_w2_relayout(1024, 16, ds.F32, None, other, None) == ds.EINVAL
+    assert L.dspark_w2_relayout(1024, 16, ds.F32, FAKE, FAKE, None) == ds.EINVAL  # aliased
 
 
 def test_schedule_rejects_bad_arguments(ds):

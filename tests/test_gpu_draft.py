@@ -5,14 +5,14 @@ import numpy as np
 import pytest
 
 from draft_sampling_scheduling_amd import synth
-from tests.gpu_util import N, T, compare_draft
+from tests.gpu_util import N, T, compare_draft, W2T
 
 pytestmark = pytest.mark.gpu
 
 
 def _run(ora, ds, cfg, seed=0, cycle=0, rnn=False):
     I = synth.inputs(cfg)
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     if rnn:
         o = ora.draft_rnn(I["U"], I["h"], I["W1"], I["W2"], I["W_gco"], I["w"], I["x0"], seed, cycle)
         g = ds.draft_rnn(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["W_gco"]), T(I["w"]),
@@ -79,7 +79,7 @@ def test_rnn_parity(ora, ds, name, base, kw):
 def test_deterministic(ds):
     cfg = synth.scaled(synth.CONFIGS["c2"], R=100, gamma=3, V=4096, d=256)
     I = synth.inputs(cfg)
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     args = [T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(I["x0"])]
     runs = [{k: N(v) for k, v in ds.draft_markov(*args, 3, 9).items()} for _ in range(3)]
     for r in runs[1:]:
@@ -94,6 +94,6 @@ def test_bad_anchor_sets_fault_bit(ds):
     x0 = I["x0"].copy()
     x0[3] = cfg.V + 5
     status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     ds.draft_markov(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(x0), status=status)
     assert int(N(status)[0]) & ds.FAULT_TOKEN

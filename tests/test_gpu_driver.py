@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from draft_sampling_scheduling_amd import synth
-from tests.gpu_util import N, T
+from tests.gpu_util import N, T, W2T
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def _both(ora, ds, C, ncycles, policy, threshold=0.0, temps=None):
     o = ora.decode_run(C["Ub"], C["Hb"], C["W1"], C["W2"], C["w"], C["Tb"], C["x0"], ncycles,
                        policy=policy, threshold=threshold, sps=C["sps"], sps_B0=C["sps_B0"],
                        seed=11, temps=temps)
-    W2t = np.ascontiguousarray(C["W2"].T)
+    W2t = W2T(C["W2"])
     g = ds.decode_run(T(C["Ub"]), T(C["Hb"]), T(C["W1"]), T(W2t), T(C["w"]), T(C["Tb"]),
                       T(C["x0"]), ncycles, policy=policy, threshold=threshold, sps=T(C["sps"]),
                       sps_B0=C["sps_B0"], seed=11, temps=None if temps is None else T(temps))
@@ -70,7 +70,7 @@ def test_decode_parity_wider(ora, ds):
 def test_decode_zero_cycles_and_bad_anchor(ds):
     import torch
     C = synth.toy_chain(V=512, gamma=2, r=16, d=8, R=4, seed=4)
-    W2t = np.ascontiguousarray(C["W2"].T)
+    W2t = W2T(C["W2"])
     args = [T(C["Ub"]), T(C["Hb"]), T(C["W1"]), T(W2t), T(C["w"]), T(C["Tb"])]
     g = ds.decode_run(*args, T(C["x0"]), 0, policy=3)
     assert N(g["n_emitted"]).sum() == 0 and N(g["stats"]).sum() == 0

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from draft_sampling_scheduling_amd import synth
-from tests.gpu_util import N, T, compare_draft, compare_verify
+from tests.gpu_util import N, T, compare_draft, compare_verify, W2T
 from tests.test_gpu_verify import _inputs
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +30,7 @@ def test_draft_and_verify_edge(ora, ds, name, base, kw):
     cfg = synth.scaled(synth.CONFIGS[base], **kw)
     print(f"{name}: draft", flush=True)
     I = synth.inputs(cfg)
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     o = ora.draft_markov(I["U"], I["h"], I["W1"], I["W2"], I["w"], I["x0"], 1, 2)
     g = ds.draft_markov(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(I["x0"]), 1, 2)
     g = {k: N(v) for k, v in g.items()}

@@ -46,3 +46,17 @@ def test_confidence_fault_bit(ds):
     sps = np.ones(16, np.float32)
     ds.schedule(T(c), T(sps), 1, 0, status=status)
     assert int(N(status)[0]) & ds.FAULT_CONF
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_schedule_deterministic(ds, mode):
+    """Three runs on the same confidences give bit-identical lengths, survival and stats."""
+    name, c, _, kind = _conf_sets()[4]  # the largest set (512 x 16)
+    R, gamma = c.shape
+    sps, B0 = _sps(kind, R, gamma)
+    c_lag = c if mode == 2 else None
+    runs = []
+    for _ in range(3):
+        g = ds.schedule(T(c), T(sps), B0, mode, c_lag=None if c_lag is None else T(c_lag))
+        runs.append({k: N(v).tobytes() for k, v in g.items()})
+    assert runs[0] == runs[1] == runs[2], name

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from draft_sampling_scheduling_amd import synth
-from tests.gpu_util import N, T, compare_draft
+from tests.gpu_util import N, T, compare_draft, W2T
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +30,7 @@ def test_draft_with_temperatures(ora, ds, rnn):
         cfg = synth.scaled(synth.CONFIGS["c2"], R=37, gamma=4, V=5000, d=512)
     I = synth.inputs(cfg)
     temps = np.array([0.5, 1.7, 3.0, 0.9], np.float32)[:cfg.gamma]
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     if rnn:
         o = ora.draft_rnn(I["U"], I["h"], I["W1"], I["W2"], I["W_gco"], I["w"], I["x0"], 2, 4,
                           temps=temps)
@@ -52,7 +52,7 @@ def test_nonpositive_temperature_sets_fault_bit(ds):
     cfg = synth.scaled(synth.CONFIGS["c2"], R=8, gamma=2, V=1024, d=64)
     I = synth.inputs(cfg)
     status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     ds.draft_markov(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(I["x0"]),
                     temps=T(np.array([1.0, 0.0], np.float32)), status=status)
     assert int(N(status)[0]) & ds.FAULT_CONF
@@ -88,7 +88,7 @@ def test_sts_fit_deterministic_and_feeds_draft(ora, ds):
     assert np.array_equal(N(a["T"]), N(b["T"])) and np.array_equal(N(a["ece"]), N(b["ece"]))
     cfg = synth.scaled(synth.CONFIGS["c2"], R=16, gamma=4, V=2048, d=128)
     I = synth.inputs(cfg)
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     Tfit = N(a["T"])
     o = ora.draft_markov(I["U"], I["h"], I["W1"], I["W2"], I["w"], I["x0"], 0, 1, temps=Tfit)
     g = ds.draft_markov(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(I["x0"]), 0, 1,

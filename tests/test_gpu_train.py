@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from draft_sampling_scheduling_amd import synth
-from tests.gpu_util import N, T, TOL_P
+from tests.gpu_util import N, T, TOL_P, W2T
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def _compare(o, g, rows, label):
 
 
 def _gpu(ds, I, B, alpha=ALPHA):
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     g = ds.train_forward(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(B["target"]),
                          T(I["x0"]), T(B["xstar"]), alpha)
     return {k: N(v) for k, v in g.items()}
@@ -76,7 +76,7 @@ def test_train_forward_alpha_and_fault(ora, ds):
     xs = B["xstar"].copy()
     xs[2, 1] = cfg.V
     status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     ds.train_forward(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(B["target"]),
                      T(I["x0"]), T(xs), status=status)
     assert int(N(status)[0]) & ds.FAULT_TOKEN

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from draft_sampling_scheduling_amd import synth
-from tests.gpu_util import N, T, compare_verify
+from tests.gpu_util import N, T, compare_verify, W2T
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,7 @@ def test_verify_parity(ora, ds, name, base, kw, ell_kind):
     I, d, target, ell = _inputs(ora, cfg, cycle, ell_kind)
     o = ora.verify(target, I["U"], I["W2"], d["bias_rows"], d["x"], ell, seed=0, cycle=cycle)
     brows = synth.encode(cfg, d["bias_rows"].astype(np.float32))  # exact: rows of W1
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     g = ds.verify(T(target), T(I["U"]), T(W2t), T(brows), T(d["x"]),
                   T(d["lse"].astype(np.float32)), T(d["logit_x"].astype(np.float32)), T(ell),
                   seed=0, cycle=cycle)
@@ -76,7 +76,7 @@ def test_verify_rnn_float_bias_rows(ora, ds):
     cycle = 2
     I, d, target, ell = _inputs(ora, cfg, cycle, "random", rnn=True)
     o = ora.verify(target, I["U"], I["W2"], d["bias_rows"], d["x"], ell, seed=0, cycle=cycle)
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     g = ds.verify(T(target), T(I["U"]), T(W2t), T(d["bias_rows"].astype(np.float32)), T(d["x"]),
                   T(d["lse"].astype(np.float32)), T(d["logit_x"].astype(np.float32)), T(ell),
                   seed=0, cycle=cycle)
@@ -91,8 +91,24 @@ def test_length_fault_bit(ora, ds):
     ell = ell.copy()
     ell[1] = 9
     status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    W2t = np.ascontiguousarray(I["W2"].T)
+    W2t = W2T(I["W2"])
     brows = synth.encode(cfg, d["bias_rows"].astype(np.float32))
     ds.verify(T(target), T(I["U"]), T(W2t), T(brows), T(d["x"]), T(d["lse"].astype(np.float32)),
               T(d["logit_x"].astype(np.float32)), T(ell), status=status)
     assert int(N(status)[0]) & ds.FAULT_LEN
+
+
+def test_verify_deterministic(ora, ds):
+    """Three verifications of the same drafted block (same seed and cycle) give
+    bit-identical accepted counts, tokens and c*."""
+    cfg = synth.scaled(synth.CONFIGS["c3"], R=40, gamma=6, V=16384, d=256)
+    I, d, target, ell = _inputs(ora, cfg, 5, "random")
+    W2t = W2T(I["W2"])
+    brows = synth.encode(cfg, d["bias_rows"].astype(np.float32))
+    runs = []
+    for _ in range(3):
+        g = ds.verify(T(target), T(I["U"]), W2t, T(brows), T(d["x"]),
+                      T(d["lse"].astype(np.float32)), T(d["logit_x"].astype(np.float32)),
+                      T(ell), seed=0, cycle=5)
+        runs.append({k: N(v).tobytes() for k, v in g.items()})
+    assert runs[0] == runs[1] == runs[2]
