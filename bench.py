@@ -205,7 +205,7 @@ def traffic_from(fetch_csv: str, write_csv: str) -> None:
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"])
-            if "DraftEpi<false>" in r["Kernel_Name"]:
+            if "DraftEpi<false, true>" in r["Kernel_Name"]:
                 sweep.append(v)
             elif "copyBuffer" in r["Kernel_Name"] and v > COPY_PROBE_BYTES / 1024 / 8:
                 copy.append(v)
@@ -219,7 +219,7 @@ def traffic_from(fetch_csv: str, write_csv: str) -> None:
     f_scale = COPY_PROBE_BYTES / 1024 / f_copy
     w_scale = COPY_PROBE_BYTES / 1024 / w_copy
     out = {
-        "kernel": "draft sweep (sweep_kernel<16, false, *, DraftEpi<false>>), R=256 V=151936 r=256",
+        "kernel": "draft sweep (sweep_kernel<16, false, 2, DraftEpi<false, true>>), R=256 V=151936 r=256",
         "kernel_source_sha": kernel_sha(),
         "dispatches": n,
         "fetch_kib_per_dispatch": f_sweep, "write_kib_per_dispatch": w_sweep,
@@ -310,6 +310,8 @@ def bench_cycle(args):
     # so every position is sampled); the other positions run unbracketed
     hip, evs = hip_events(2 * nsteps)
 
+    # one sweep launch per cycle is bracketed by events (draft position k = cycle mod gamma,
+    # so every position is sampled); the other positions run unbracketed
     def ev_arrays(i):
         k = i % G
         evb, eve = (C.c_void_p * G)(), (C.c_void_p * G)()
@@ -371,7 +373,25 @@ def bench_cycle(args):
     if not torch.equal(vout["y"], emitted_ref[-1]):
         raise SystemExit("the timed cycles did not reproduce the first pass's tokens")
     timed = range(args.warmup, nsteps)
-    sweep_ms = float(np.mean([elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in timed]))
+    kern_ms = float(np.mean([elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in timed]))
+
+    # the cost of the sequential head: the same draft without it (the parallel block's own
+    # sampling from U_k), timed on the same inputs after the cycles
+    def draft_time(fn, n=10):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(n):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+    x0.copy_(x0_first)
+    t_markov = draft_time(lambda: ds.draft_markov(U, h, W1, W2t, w, x0, SEED, 0, out=dout,
+                                                  ws=dws, status=status))
+    t_parallel = draft_time(lambda: ds.draft_parallel(U, h, W1, w, x0, SEED, 0, out=dout,
+                                                      ws=dws, status=status))
     t_draft = float(np.mean([sev[t][0].elapsed_time(sev[t][1]) for t in timed]))
     t_sched = float(np.mean([sev[t][1].elapsed_time(sev[t][2]) for t in timed]))
     t_ver = float(np.mean([sev[t][2].elapsed_time(sev[t][3]) for t in timed]))
@@ -405,13 +425,14 @@ def bench_cycle(args):
     ms_per_step = wall * 1000.0 / args.steps
     n_acc_sum = sum(int((emitted_ref[t] >= 0).sum()) for t in timed)  # emitted tokens
 
-    # algorithmic bytes of one draft sweep launch: U_k rows, all of W2, the gathered W1 rows
-    sweep_bytes = sweep_bytes_of(R, V, r)
-    achieved = sweep_bytes / (sweep_ms * 1e-3) / 1e9
     # the Markov step (gather, bias contraction, logits, normaliser, sample, confidence) per
     # position: U_k, W2, h_k and the gathered W1 rows; gamma positions per cycle
     step_bytes = R * V * 2 + V * r * 2 + R * d * 2 + R * r * 2
     draft_bytes = G * step_bytes
+    # the timed kernel: one vocabulary sweep, U_k rows, all of W2, the gathered W1 rows
+    kern_bytes = sweep_bytes_of(R, V, r)
+    kern_name = f"draft sweep (sweep_kernel<{r // 16}, false, 2, DraftEpi<false, true>>)"
+    achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     n_b = float(ell_all.sum(axis=1).mean())
     n_a = n_b + R
     cycle_bytes = draft_bytes + (n_a * V * 2 + n_b * V * 2 + V * r * 2)
@@ -446,8 +467,13 @@ def bench_cycle(args):
                    "R": R, "gamma": G, "V": V, "r": r, "d": d},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": f"draft sweep (sweep_kernel<{r // 16}, false, *, DraftEpi<false>>)",
-                     "bytes_per_launch": sweep_bytes, "launch_us": sweep_ms * 1e3},
+                     "kernel": kern_name, "bytes_per_launch": kern_bytes,
+                     "launch_us": kern_ms * 1e3},
+        "sequential_head_cost": {
+            "draft_markov_us": t_markov * 1e3, "draft_parallel_us": t_parallel * 1e3,
+            "ratio": t_markov / t_parallel,
+            "what": "the draft call with the Markov head against the parallel block's own "
+                    "sampling from U_k (dspark_draft_parallel), same inputs, 10 calls each"},
         "markov_step_roofline": {
             "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS,
             "achieved": draft_bytes / (t_draft * 1e-3) / 1e9,

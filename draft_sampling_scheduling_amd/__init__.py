@@ -23,6 +23,7 @@ OK, EINVAL, ERANGE, EWORKSPACE, EDEVICE = 0, -1, -2, -3, -4
 FAULT_TOKEN, FAULT_CONF, FAULT_LEN = 1, 2, 4
 EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov", "dspark_draft_markov_timed",
            "dspark_draft_markov_noalloc_max_bytes", "dspark_draft_markov_noalloc",
+           "dspark_draft_parallel",
            "dspark_draft_rnn_workspace_bytes", "dspark_draft_rnn",
            "dspark_schedule_workspace_bytes", "dspark_schedule",
            "dspark_verify_workspace_bytes", "dspark_verify",
@@ -69,6 +70,9 @@ def lib():
         L.dspark_draft_markov_noalloc_max_bytes.restype = sz
         L.dspark_draft_markov_noalloc.argtypes = [i] * 6 + [vp] * 7 + [u64, u64] + [vp] * 8
         L.dspark_draft_markov_noalloc.restype = i
+        L.dspark_draft_parallel.argtypes = ([i] * 6 + [vp] * 6 + [u64, u64] + [vp] * 7 +
+                                            [vp, sz, vp])
+        L.dspark_draft_parallel.restype = i
         L.dspark_draft_rnn.argtypes = ([i] * 6 + [vp] * 8 + [u64, u64] + [vp] * 7 +
                                        [vp, sz, vp])
         L.dspark_draft_rnn.restype = i
@@ -192,7 +196,7 @@ def draft_rnn_workspace_bytes(R, gamma, V, r, d) -> int:
 
 
 def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, temps=None, out=None, ws=None,
-           status=None, events=None):
+           status=None, events=None, parallel=False):
     torch = _torch()
     _chk(U, "U")
     R, gamma, V = U.shape
@@ -201,7 +205,8 @@ def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, temps=None, out=N
     d = h.shape[2]
     _chk(h, "h", (R, gamma, d), U.dtype)
     _chk(W1, "W1", (V, r), U.dtype)
-    _chk(W2t, "W2t", (V, r), U.dtype)
+    if not parallel:
+        _chk(W2t, "W2t", (V, r), U.dtype)
     _chk(w, "w", (d + r,), torch.float32)
     _chk(x0, "x0", (R,), torch.int32)
     if temps is not None:
@@ -222,14 +227,19 @@ def _draft(rnn, U, h, W1, W2t, w, x0, seed, cycle, W_gco=None, temps=None, out=N
     if nbytes == 0 and R > 0:
         raise DsparkError("dspark_draft_workspace_bytes", EINVAL)
     ws = _ws(nbytes, dev, ws)
-    args = [R, gamma, V, r, d, dt, _p(U), _p(h), _p(W1), _p(W2t)]
+    args = [R, gamma, V, r, d, dt, _p(U), _p(h), _p(W1)]
+    if not parallel:
+        args.append(_p(W2t))
     if rnn:
         args.append(_p(W_gco))
     args += [_p(w), _p(temps), _p(x0), seed, cycle, _p(out["x"]), _p(out["c"]),
              _p(out.get("z")), _p(out["lse"]), _p(out["logit_x"]), _p(out["bias_rows"]), _p(status), _p(ws),
              ws.numel() * ws.element_size(), _stream()]
-    fn = "dspark_draft_rnn" if rnn else "dspark_draft_markov"
+    fn = "dspark_draft_rnn" if rnn else ("dspark_draft_parallel" if parallel else
+                                         "dspark_draft_markov")
     if events is not None:  # (begin, end): ctypes arrays of gamma hipEvent_t each
+        if parallel:
+            raise ValueError("the timed hook is the Markov head's")
         fn = "dspark_draft_markov_timed"
         args += [C.cast(events[0], C.c_void_p), C.cast(events[1], C.c_void_p)]
     _raise(fn, getattr(lib(), fn)(*args))
@@ -244,6 +254,14 @@ def draft_markov(U, h, W1, W2t, w, x0, seed=0, cycle=0, *, temps=None, out=None,
     the timed variant."""
     return _draft(False, U, h, W1, W2t, w, x0, seed, cycle, temps=temps, out=out, ws=ws,
                   status=status, events=events)
+
+
+def draft_parallel(U, h, W1, w, x0, seed=0, cycle=0, *, temps=None, out=None, ws=None,
+                   status=None):
+    """The parallel block's drafter without the sequential head: x_k from softmax(U_k);
+    same outputs as draft_markov (bf16 operands)."""
+    return _draft(False, U, h, W1, None, w, x0, seed, cycle, temps=temps, out=out, ws=ws,
+                  status=status, parallel=True)
 
 
 def draft_markov_noalloc(U, h, W1, W2t, w, x0, seed=0, cycle=0, *, temps=None, out=None,

@@ -122,35 +122,45 @@ __global__ void __launch_bounds__(64) draft_sweep_f32_kernel(
 // combine: one workgroup per request
 // ---------------------------------------------------------------------------------------
 constexpr int kCombineThreads = 256;
+constexpr int kCombineWaves = kCombineThreads / kWave;
 
-template <class T, bool RNN>
-__global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
-    int R, int gamma, int V, int r, int d, const T* __restrict__ U, const T* __restrict__ W1,
-    const T* __restrict__ W2t, const float* __restrict__ w, const float* __restrict__ temps,
-    const float* __restrict__ zh, const int32_t* prev, int prev_stride,
-    const float* __restrict__ orow, const float4* __restrict__ partials, int nranges,
-    uint32_t k, uint64_t seed, uint64_t cycle, int32_t* x, float* c, float* zout, float* lse,
-    float* logit_x, void* bias_rows, uint4* bpack, int32_t* status) {
-  constexpr int kWaves = kCombineThreads / kWave;
-  __shared__ float4 red[kWaves];
-  __shared__ float dotp[kWaves][kWave];
-  __shared__ float zred[kWaves];
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+struct CombineLds {
+  float4 red[kCombineWaves];
+  float dotp[kCombineWaves][kWave];
+  float zred[kCombineWaves];
+};
+
+// The combine of request q at position k, for a workgroup of kCombineThreads threads.  It
+// first does the work that depends on x_{k-1} only (the embedding part of the confidence,
+// and the bias row verification reuses), while the first range partial is in flight; then
+// it merges the vocabulary ranges' partials (normaliser and winning block), recomputes the
+// winning block's 64 logits, draws x_k inside it (second level of the sampler), and writes
+// x, c, z, lse, logit_x (and W1[x_k] in the next sweep's packed order when bpack is set).
+// BIAS = false: the logits are U_k (the parallel block's own sampling).
+template <class T, bool RNN, bool BIAS>
+__device__ void combine_request(CombineLds& sm, int q, int R, int gamma, int V, int r, int d,
+                               const T* __restrict__ U, const T* __restrict__ W1,
+                               const T* __restrict__ W2t, const float* __restrict__ w,
+                               const float* __restrict__ temps, const float* zh,
+                               int32_t tprev, const float* __restrict__ orow,
+                               const float4* partials, int nranges, uint32_t k, uint64_t seed,
+                               uint64_t cycle, int32_t* x, float* c, float* zout, float* lse,
+                               float* logit_x, void* bias_rows, uint4* bpack, int32_t* status) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t rk = (size_t)q * gamma + (k - 1);
-  // this thread's first range partial and the previous token, loaded before anything waits
-  const float4* prow = partials + (size_t)q * nranges;
-  const float4 pr0 =
-      tid < nranges ? prow[tid] : make_float4(0.0f, 0.0f, 0.0f, __int_as_float(0x7fffffff));
-  // the previous token's embedding row (independent of the partials)
-  const int32_t tprev = checked_token(prev[(size_t)q * prev_stride], V, status);
   const T* e = W1 + (size_t)tprev * r;
-  // confidence head, embedding part: w_e . W1[x_{k-1}], and the bias row this step used
-  // (for verification): both depend on x_{k-1} only, so they overlap the partials' loads
+  // this thread's first range partial is loaded before anything else, so it is in flight
+  // with the x_{k-1} work
+  const float4* prow = partials + (size_t)q * nranges;
+  const float4 pr0 = tid < nranges ? prow[tid]
+                                   : make_float4(0.0f, 0.0f, 0.0f, __int_as_float(0x7fffffff));
+  // confidence head, embedding part: w_e . W1[x_{k-1}], and the bias row this step used (for
+  // verification): both depend on x_{k-1} only
   {
     float ze = 0.0f;
     for (int i = tid; i < r; i += kCombineThreads) ze = fmaf(w[d + i], ld<T>(e, i), ze);
     ze = wave_sum(ze);
-    if (lane == 0) zred[wave] = ze;
+    if (lane == 0) sm.zred[wave] = ze;
     if (RNN) {
       float* br = static_cast<float*>(bias_rows) + rk * r;
       for (int i = tid; i < r; i += kCombineThreads) br[i] = orow[(size_t)q * r + i];
@@ -160,8 +170,8 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
     }
   }
 
-  // first level: normaliser and winning block over the ranges' partials (per wave: the
-  // largest reference, then one rescale per lane and a plain sum)
+  // the range partials: per wave the largest reference, one rescale per lane and a plain
+  // sum
   float M = -INFINITY, S = 0.0f, G = -INFINITY;
   int Bk = 0x7fffffff;
   for (int i = tid; i < nranges; i += kCombineThreads) {
@@ -181,14 +191,14 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
     M = Mw;
   }
   wave_argmax(G, Bk);
-  if (lane == 0) red[wave] = make_float4(M, S, G, __int_as_float(Bk));
+  if (lane == 0) sm.red[wave] = make_float4(M, S, G, __int_as_float(Bk));
   __syncthreads();
   {
-    const float4 r0 = red[0];
+    const float4 r0 = sm.red[0];
     M = r0.x; S = r0.y; G = r0.z; Bk = __float_as_int(r0.w);
 #pragma unroll
-    for (int i = 1; i < kWaves; ++i) {
-      const float4 ri = red[i];
+    for (int i = 1; i < kCombineWaves; ++i) {
+      const float4 ri = sm.red[i];
       lse_merge(M, S, ri.x, ri.y);
       const int bi = __float_as_int(ri.w);
       if (ri.z > G || (ri.z == G && bi < Bk)) {
@@ -203,37 +213,41 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
   // second level: the winning block's 64 logits, the k sum split over the waves in
   // 8-element chunks
   const int v = Bk * kVB + lane;
-  const float u = (wave == 0 && v < V) ? ld<T>(U, (size_t)q * gamma * V + (size_t)(k - 1) * V + v) : 0.0f;
+  const float u = (wave == 0 && v < V) ? ld<T>(U, rk * V + v) : 0.0f;
   float part = 0.0f;
   float gn = 0.0f;  // in-block Gumbel noise (wave 0), formed while the block's rows load
   if (v < V) {
-    const T* wr = W2t + (size_t)v * r;
-    // r <= 256: at most 8 chunks per wave, all loads in flight together
-    float a[8][8], bv[8][8];
+    if (BIAS) {
+      const T* wr = W2t + (size_t)v * r;
+      // r <= 256: at most 8 chunks per wave, all loads in flight together
+      float a[8][8], bv[8][8];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int ch = wave + kWaves * it < r / 8 ? wave + kWaves * it : 0;
-      ld8<T>(wr + ch * 8, a[it]);
-      if (RNN) {
+      for (int it = 0; it < 8; ++it) {
+        const int ch = wave + kCombineWaves * it < r / 8 ? wave + kCombineWaves * it : 0;
+        ld8<T>(wr + ch * 8, a[it]);
+        if (RNN) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bv[it][j] = orow[(size_t)q * r + ch * 8 + j];
-      } else {
-        ld8<T>(e + ch * 8, bv[it]);
+          for (int j = 0; j < 8; ++j) bv[it][j] = orow[(size_t)q * r + ch * 8 + j];
+        } else {
+          ld8<T>(e + ch * 8, bv[it]);
+        }
       }
+      if (wave == 0) gn = gumbel_of(Rng(seed, cycle).word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v));
+#pragma unroll
+      for (int it = 0; it < 8; ++it)
+        if (wave + kCombineWaves * it < r / 8)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) part = fmaf(bv[it][j], a[it][j], part);
+    } else if (wave == 0) {
+      gn = gumbel_of(Rng(seed, cycle).word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v));
     }
-    if (wave == 0) gn = gumbel_of(Rng(seed, cycle).word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v));
-#pragma unroll
-    for (int it = 0; it < 8; ++it)
-      if (wave + kWaves * it < r / 8)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) part = fmaf(bv[it][j], a[it][j], part);
   }
-  dotp[wave][lane] = part;
+  sm.dotp[wave][lane] = part;
   __syncthreads();
   if (wave == 0) {
     float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) acc += dotp[i][lane];
+    for (int i = 0; i < kCombineWaves; ++i) acc += sm.dotp[i][lane];
     const float l = (v < V) ? u + acc : -INFINITY;
     float score = (v < V) ? l + gn : -INFINITY;
     int idx = v;
@@ -245,7 +259,7 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
     const float lx = __shfl(l, idx - Bk * kVB, kWave);
     float z = zh[rk];
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) z += zred[i];
+    for (int i = 0; i < kCombineWaves; ++i) z += sm.zred[i];
     if (lane == 0) {
       // the position's STS temperature (Module D); a non-positive one is a data fault
       float Tk = temps ? temps[k - 1] : 1.0f;
@@ -260,6 +274,22 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
       logit_x[rk] = lx;
     }
   }
+}
+
+template <class T, bool RNN, bool BIAS = true>
+__global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
+    int R, int gamma, int V, int r, int d, const T* __restrict__ U, const T* __restrict__ W1,
+    const T* __restrict__ W2t, const float* __restrict__ w, const float* __restrict__ temps,
+    const float* __restrict__ zh, const int32_t* prev, int prev_stride,
+    const float* __restrict__ orow, const float4* __restrict__ partials, int nranges,
+    uint32_t k, uint64_t seed, uint64_t cycle, int32_t* x, float* c, float* zout, float* lse,
+    float* logit_x, void* bias_rows, uint4* bpack, int32_t* status) {
+  __shared__ CombineLds sm;
+  const int q = blockIdx.x;
+  const int32_t tprev = checked_token(prev[(size_t)q * prev_stride], V, status);
+  combine_request<T, RNN, BIAS>(sm, q, R, gamma, V, r, d, U, W1, W2t, w, temps, zh, tprev,
+                                orow, partials, nranges, k, seed, cycle, x, c, zout, lse,
+                                logit_x, bias_rows, bpack, status);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -716,8 +746,11 @@ static DraftWs carve_draft(void* ws, int R, int gamma, int V, int r, int d, bool
   return w;
 }
 
+// Launches the single-launch draft when its grid can be resident at once and every
+// workgroup has at most kMaxCombinesPerWg requests to combine; returns false (nothing
+// enqueued) otherwise.  ev0/ev1 (nullable) are recorded around the kernel.
 template <class T>
-static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void* U_,
+static int draft_run(bool rnn, bool bias, int R, int gamma, int V, int r, int d, const void* U_,
                      const void* h_, const void* W1_, const void* W2t_, const void* Wg_,
                      const float* w, const float* temps, const int32_t* x0, uint64_t seed,
                      uint64_t cycle, int32_t* x, float* c, float* z, float* lse, float* logit_x,
@@ -825,8 +858,10 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
       p.status = status;
       if (rnn)
         launch_sweep<true, DraftEpi<true>>(g, p, stream, e0, e1);
-      else
+      else if (bias)
         launch_sweep<false, DraftEpi<false>>(g, p, stream, e0, e1);
+      else
+        launch_sweep<false, DraftEpi<false, false>>(g, p, stream, e0, e1);
     } else {
       const int nblocks = (V + kVB - 1) / kVB;
       dim3 grid(nranges, R);
@@ -842,8 +877,13 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
           R, gamma, V, r, d, U, W1, W2t, w, temps, ws.zh, prev, ps, ws.orow, ws.partials,
           nranges, (uint32_t)k, seed, cycle, x, c, z, lse, logit_x, bias_rows, nullptr,
           status);
-    else
+    else if (bias)
       draft_combine_kernel<T, false><<<R, kCombineThreads, 0, stream>>>(
+          R, gamma, V, r, d, U, W1, W2t, w, temps, ws.zh, prev, ps, nullptr, ws.partials,
+          nranges, (uint32_t)k, seed, cycle, x, c, z, lse, logit_x, bias_rows,
+          k < gamma ? bpack : nullptr, status);
+    else
+      draft_combine_kernel<T, false, false><<<R, kCombineThreads, 0, stream>>>(
           R, gamma, V, r, d, U, W1, W2t, w, temps, ws.zh, prev, ps, nullptr, ws.partials,
           nranges, (uint32_t)k, seed, cycle, x, c, z, lse, logit_x, bias_rows,
           k < gamma ? bpack : nullptr, status);
@@ -851,7 +891,7 @@ static int draft_run(bool rnn, int R, int gamma, int V, int r, int d, const void
   return launch_status();
 }
 
-static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_dtype dt,
+static int draft_entry(bool rnn, bool bias, int R, int gamma, int V, int r, int d, dspark_dtype dt,
                        const void* U, const void* h, const void* W1, const void* W2t,
                        const void* Wg, const float* w, const float* temps, const int32_t* x0,
                        uint64_t seed, uint64_t cycle, int32_t* x, float* c, float* z,
@@ -861,10 +901,12 @@ static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_d
   if (!dims_ok(R, gamma, V, r, d) || (dt != DSPARK_F32 && dt != DSPARK_BF16)) return DSPARK_EINVAL;
   if (cycle >= ((uint64_t)1 << 28)) return DSPARK_EINVAL;
   if (R == 0) return DSPARK_OK;
-  if (!U || !W1 || !W2t || !w || !x0 || !x || !c || !lse || !logit_x || !bias_rows || !ws)
+  if (!U || !W1 || (bias && !W2t) || !w || !x0 || !x || !c || !lse || !logit_x || !bias_rows ||
+      !ws)
     return DSPARK_EINVAL;
   if (d > 0 && !h) return DSPARK_EINVAL;
   if (rnn && !Wg) return DSPARK_EINVAL;
+  if (!bias && (rnn || dt != DSPARK_BF16)) return DSPARK_EINVAL;  // the parallel drafter: bf16
   // the bf16 h projection addresses h with 32-bit byte offsets
   if (rnn && dt == DSPARK_BF16 && (uint64_t)R * gamma * d * 2 >= ((uint64_t)1 << 32))
     return DSPARK_EINVAL;
@@ -878,10 +920,10 @@ static int draft_entry(bool rnn, int R, int gamma, int V, int r, int d, dspark_d
   if (!aligned16(ws)) return DSPARK_EINVAL;
   const DraftWs lay = carve_draft(ws, R, gamma, V, r, d, rnn);
   if (dt == DSPARK_BF16)
-    return draft_run<uint16_t>(rnn, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, temps, x0, seed,
+    return draft_run<uint16_t>(rnn, bias, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, temps, x0, seed,
                                cycle, x, c, z, lse, logit_x, bias_rows, status, lay, stream,
                                evb, eve);
-  return draft_run<float>(rnn, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, temps, x0, seed, cycle,
+  return draft_run<float>(rnn, bias, R, gamma, V, r, d, U, h, W1, W2t, Wg, w, temps, x0, seed, cycle,
                           x, c, z, lse, logit_x, bias_rows, status, lay, stream, evb, eve);
 }
 
@@ -928,7 +970,7 @@ int dspark_draft_markov_noalloc(int R, int gamma, int V, int r, int d, dspark_dt
   if (R == 0) return DSPARK_OK;
   void* ws = scratch_on_device();
   if (!ws) return DSPARK_EDEVICE;
-  return draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, temps, x0, seed,
+  return draft_entry(false, true, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, temps, x0, seed,
                      cycle, x, c, z, lse, logit_x, bias_rows, dev_status, ws,
                      kNoAllocScratchBytes, stream);
 }
@@ -949,7 +991,7 @@ int dspark_draft_markov(int R, int gamma, int V, int r, int d, dspark_dtype dt, 
                         int32_t* x, float* c, float* z, float* lse, float* logit_x,
                         void* bias_rows, int32_t* dev_status, void* ws, size_t ws_bytes,
                         hipStream_t stream) {
-  return dspark::draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, temps, x0,
+  return dspark::draft_entry(false, true, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, temps, x0,
                              seed, cycle, x, c, z, lse, logit_x, bias_rows, dev_status, ws,
                              ws_bytes, stream);
 }
@@ -962,9 +1004,19 @@ int dspark_draft_markov_timed(int R, int gamma, int V, int r, int d, dspark_dtyp
                               void* ws, size_t ws_bytes, hipStream_t stream,
                               hipEvent_t* ev_begin, hipEvent_t* ev_end) {
   if (!ev_begin || !ev_end) return DSPARK_EINVAL;
-  return dspark::draft_entry(false, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, temps, x0,
+  return dspark::draft_entry(false, true, R, gamma, V, r, d, dt, U, h, W1, W2t, nullptr, w, temps, x0,
                              seed, cycle, x, c, z, lse, logit_x, bias_rows, dev_status, ws,
                              ws_bytes, stream, ev_begin, ev_end);
+}
+
+int dspark_draft_parallel(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void* U,
+                          const void* h, const void* W1, const float* w, const float* temps,
+                          const int32_t* x0, uint64_t seed, uint64_t cycle, int32_t* x, float* c,
+                          float* z, float* lse, float* logit_x, void* bias_rows,
+                          int32_t* dev_status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return dspark::draft_entry(false, false, R, gamma, V, r, d, dt, U, h, W1, nullptr, nullptr, w,
+                             temps, x0, seed, cycle, x, c, z, lse, logit_x, bias_rows, dev_status,
+                             ws, ws_bytes, stream);
 }
 
 int dspark_draft_rnn(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void* U,
@@ -973,7 +1025,7 @@ int dspark_draft_rnn(int R, int gamma, int V, int r, int d, dspark_dtype dt, con
                      uint64_t cycle, int32_t* x, float* c, float* z, float* lse, float* logit_x,
                      float* bias_rows, int32_t* dev_status, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
-  return dspark::draft_entry(true, R, gamma, V, r, d, dt, U, h, W1, W2t, W_gco, w, temps, x0,
+  return dspark::draft_entry(true, true, R, gamma, V, r, d, dt, U, h, W1, W2t, W_gco, w, temps, x0,
                              seed, cycle, x, c, z, lse, logit_x, bias_rows, dev_status, ws,
                              ws_bytes, stream);
 }

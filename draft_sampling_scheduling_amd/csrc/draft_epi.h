@@ -27,9 +27,12 @@ struct DraftSweepParams {
   int32_t* status;
 };
 
-template <bool RNN>
+// BIAS = false: the sampling of the parallel block alone (logits U_k, no head bias), the
+// drafter the sequential head is measured against
+template <bool RNN, bool BIAS = true>
 struct DraftEpi {
   static constexpr int kStreams = 1;  // U_k
+  static constexpr bool kNoBias = !BIAS;
   using Params = DraftSweepParams;
   // Row state, kept alike in the row's two lanes except for the partial sums: one running
   // reference ref (log2 units: the largest l * log2(e) seen so far), so each tile's

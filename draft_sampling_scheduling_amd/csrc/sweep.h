@@ -28,6 +28,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "dev.h"
 #include "host.h"
 
@@ -176,8 +178,9 @@ __device__ __forceinline__ void half_lse(float& m, float& s) {
   lse_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
 }
 
-// The sweep kernel.  Lane (n, h) of wave w works on row = group*128 + 32w + n; the lanes
-// with h == 0 own the row's running state.  Epi provides:
+// The sweep of one row group over one vocabulary range.  Lane (n, h) of wave w works on
+// row = group*128 + 32w + n; the lanes with h == 0 own the row's running state.  Epi
+// provides:
 //   static constexpr int kStreams;       streamed operands: 1 (U) or 2 (U, target)
 //   struct Params; struct State;
 //   static bool group_live(const Params&, int row0)         rows exist in this group
@@ -201,64 +204,129 @@ __device__ __forceinline__ void half_lse(float& m, float& s) {
 // NKS = r / 16 (compile time: the k loop is fully unrolled over register operands).
 // SPLIT: B rows are float and enter as hi + lo bf16 terms (two MFMAs each).
 // Host guarantees: every stream array is smaller than 4 GiB (32-bit byte offsets).
-template <int NKS, bool SPLIT, int NSTAGE, class Epi>
-__global__ void __launch_bounds__(kSweepThreads, 2)
-    sweep_kernel(SweepGeom g, typename Epi::Params ep) {
-  constexpr int CH = 2 * NKS;
-  constexpr int RS = CH + 1;                 // W2t tile row stride (chunks)
-  constexpr int NI = w2_copies(CH);          // W2t copies per tile
-  constexpr int W2_MAX = (NI + kSweepWaves - 1) / kSweepWaves;
-  constexpr int NS = Epi::kStreams;
-  constexpr int SCH = stage_chunks(CH, NS);
-  constexpr int D = NSTAGE - 1;              // prefetch distance in tiles
-  extern __shared__ uint4 lds[];
+//
+// An epilogue may declare `static constexpr bool kNoBias = true`: the logits are then the
+// first streamed operand alone (no W2t tiles are copied and no matrix-core chain runs), the
+// sampling of the parallel block without the sequential head.
+template <class E, class = void>
+struct epi_has_bias : std::true_type {};
+template <class E>
+struct epi_has_bias<E, std::void_t<decltype(E::kNoBias)>>
+    : std::integral_constant<bool, !E::kNoBias> {};
 
-  // task -> (vocabulary range, first row group); the gsplit workgroups of one range are
-  // dispatched to the same XCD (round-robin dispatch over 8 XCDs) so its W2t tiles come
-  // from HBM once and from that XCD's L2 after
-  int range, g0;
-  {
-    const int bid = blockIdx.x, G = g.gsplit;
-    if ((g.nranges & 7) == 0) {
-      const int slot = bid >> 3;
-      range = (slot / G) * 8 + (bid & 7);
-      g0 = slot - (slot / G) * G;
+// The work comes in two parts: prepare() fixes the per-lane copy offsets and issues the
+// first tile into stage 0 (it reads nothing the B rows or the epilogue state need); run()
+// loads the B rows, streams the range and hands the result to the epilogue.
+template <int NKS, bool SPLIT, int NSTAGE, class Epi>
+struct SweepTask {
+  static constexpr int CH = 2 * NKS;
+  static constexpr int RS = CH + 1;                 // W2t tile row stride (chunks)
+  static constexpr int NI = w2_copies(CH);          // W2t copies per tile
+  static constexpr int W2_MAX = (NI + kSweepWaves - 1) / kSweepWaves;
+  static constexpr int NS = Epi::kStreams;
+  static constexpr int SCH = stage_chunks(CH, NS);
+  static constexpr int D = NSTAGE - 1;              // prefetch distance in tiles
+  static constexpr bool BIAS = epi_has_bias<Epi>::value;
+  // copies one tile puts in flight for a wave (W2t copies: W2_MAX or W2_MAX - 1)
+  static constexpr int OPS_BIG = (BIAS ? W2_MAX : 0) + 2 * NS;
+  static constexpr int OPS_SMALL = (BIAS ? W2_MAX - 1 : 0) + 2 * NS;
+
+  const SweepGeom& g;
+  const typename Epi::Params& ep;
+  uint4* lds;
+  int range, group_row0, lane, wave, n, h, nrows, row;
+  bool live, owner, big;
+  uint32_t w2off[W2_MAX];
+  uint32_t soff[NS][2];
+  int sx[2];
+  const uint16_t* sb[NS];
+  uint32_t lds0;
+  int a_idx, s_idx0, s_idx1;
+  int b0, b1, bp1, t0, t1;
+  bool ragged;
+
+  __device__ __forceinline__ SweepTask(const SweepGeom& g_, const typename Epi::Params& ep_,
+                                       uint4* lds_)
+      : g(g_), ep(ep_), lds(lds_) {}
+
+  // copies of full tile t into stage stg (scalar bases; per-lane offsets fixed)
+  __device__ __forceinline__ void issue(int t, int stg) {
+    const uint32_t base = lds0 + 16u * stg * SCH;
+    const uint16_t* w2b = g.W2t + (size_t)kTile * t * g.r;
+#pragma unroll
+    for (int i = 0; i < W2_MAX; ++i) {
+      const int I = wave + kSweepWaves * i;
+      if (BIAS && I < NI) dma16s(w2b, w2off[i], base + 16u * 64u * I);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        dma16s(sb[s] + kTile * t, soff[s][k],
+               base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
+  }
+  // the same for the short last tile: clamp each lane's source into the arrays
+  __device__ __forceinline__ void issue_ragged(int t, int stg) {
+    const uint32_t base = lds0 + 16u * stg * SCH;
+#pragma unroll
+    for (int i = 0; i < W2_MAX; ++i) {
+      const int I = wave + kSweepWaves * i;
+      const int P = 64 * I + lane;
+      const int m = P / RS, c = P - m * RS;
+      int v = kTile * t + (m < 32 ? tile_row_of_vocab(m) : 0);
+      if (v >= g.V) v = g.V - 1;
+      const uint32_t off = (m < 32 && c < CH) ? (uint32_t)(v * g.r + 8 * c) * 2u : 0u;
+      if (BIAS && I < NI) dma16s(g.W2t, off, base + 16u * 64u * I);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        int v = kTile * t + sx[k];
+        if (v > g.V - 8) v = g.V - 8;
+        dma16s(sb[s], soff[s][k] + (uint32_t)(v - sx[k]) * 2u,
+               base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
+      }
+  }
+  // wait until at most `left` (0 .. D-1) tiles' copies are still in flight (loads complete
+  // in order)
+  __device__ __forceinline__ void wait_tiles(int left) {
+    if (left <= 0) {
+      vm_wait<0>();
+    } else if (left == 1 || D < 3) {
+      if (big) vm_wait<OPS_BIG>(); else vm_wait<OPS_SMALL>();
     } else {
-      range = bid / G;
-      g0 = bid - range * G;
+      if (big) vm_wait<2 * OPS_BIG>(); else vm_wait<2 * OPS_SMALL>();
     }
   }
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 31, h = lane >> 5;
-  const int nrows = Epi::nrows(ep);
-  for (int group = g0; Epi::group_live(ep, group * kRowsPerGroup); group += g.gsplit) {
+
+  // the per-lane copy offsets of row group `group` and the first tile's copies
+  __device__ __forceinline__ void prepare(int range_, int group) {
+    range = range_;
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    n = lane & 31;
+    h = lane >> 5;
+    nrows = Epi::nrows(ep);
     // values derived from the group are recomputed per group rather than hoisted out of
     // the group loop and held (the scalar register file is the tight resource here)
-    int group_row0 = group * kRowsPerGroup;
+    group_row0 = group * kRowsPerGroup;
     asm volatile("" : "+s"(group_row0));
-    const int row = group_row0 + wave * 32 + n;
-    const bool live = row < nrows;
-    const bool owner = live && h == 0;
-
-    bf16x8 bh[NKS];  // B operand (filled once the first tiles are in flight)
-    bf16x8 bl[SPLIT ? NKS : 1];
-    typename Epi::State st;
+    row = group_row0 + wave * 32 + n;
+    live = row < nrows;
+    owner = live && h == 0;
 
     // per-lane byte offsets of the copies (constant over tiles)
     //   W2t copy i (index I = wave + 8i): lane -> padded position P = 64I + lane -> tile row
     //   m = P / RS, chunk c = P % RS; the pad chunk and positions past the tile read row 0
     //   stream copy k: lane -> chunk lane & 3 (xor-permuted) of the wave's row 16k + lane/4;
     //   rows past the end read the last live row
-    uint32_t w2off[W2_MAX];
 #pragma unroll
     for (int i = 0; i < W2_MAX; ++i) {
       const int P = 64 * (wave + kSweepWaves * i) + lane;
       const int m = P / RS, c = P - m * RS;
       w2off[i] = (m < 32 && c < CH) ? (uint32_t)(tile_row_of_vocab(m) * g.r + 8 * c) * 2u : 0u;
     }
-    uint32_t soff[NS][2];
-    int sx[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int rl = 16 * k + (lane >> 2);
@@ -268,108 +336,65 @@ __global__ void __launch_bounds__(kSweepThreads, 2)
 #pragma unroll
       for (int s = 0; s < NS; ++s) soff[s][k] = (Epi::srow(ep, s, rr) + (uint32_t)sx[k]) * 2u;
     }
-    const uint16_t* sb[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) sb[s] = Epi::sbase(ep, s);
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+    lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
     // LDS chunk indices this lane reads (stage 0): A fragments at a_idx + 2*ks, stream chunks
-    const int a_idx = n * RS + h;
-    const int s_idx0 = w2_tile_chunks(CH) + wave * 128 + stream_pos(n, h);
-    const int s_idx1 = w2_tile_chunks(CH) + wave * 128 + stream_pos(n, 2 + h);
+    a_idx = n * RS + h;
+    s_idx0 = w2_tile_chunks(CH) + wave * 128 + stream_pos(n, h);
+    s_idx1 = w2_tile_chunks(CH) + wave * 128 + stream_pos(n, 2 + h);
+    big = wave < NI - kSweepWaves * (W2_MAX - 1);
 
-    // copies of full tile t into stage stg (scalar bases; per-lane offsets fixed)
-    auto issue = [&](int t, int stg) {
-      const uint32_t base = lds0 + 16u * stg * SCH;
-      const uint16_t* w2b = g.W2t + (size_t)kTile * t * g.r;
-#pragma unroll
-      for (int i = 0; i < W2_MAX; ++i) {
-        const int I = wave + kSweepWaves * i;
-        if (I < NI) dma16s(w2b, w2off[i], base + 16u * 64u * I);
-      }
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-          dma16s(sb[s] + kTile * t, soff[s][k],
-                 base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
-    };
-    // the same for the short last tile: clamp each lane's source into the arrays
-    auto issue_ragged = [&](int t, int stg) {
-      const uint32_t base = lds0 + 16u * stg * SCH;
-#pragma unroll
-      for (int i = 0; i < W2_MAX; ++i) {
-        const int I = wave + kSweepWaves * i;
-        const int P = 64 * I + lane;
-        const int m = P / RS, c = P - m * RS;
-        int v = kTile * t + (m < 32 ? tile_row_of_vocab(m) : 0);
-        if (v >= g.V) v = g.V - 1;
-        const uint32_t off = (m < 32 && c < CH) ? (uint32_t)(v * g.r + 8 * c) * 2u : 0u;
-        if (I < NI) dma16s(g.W2t, off, base + 16u * 64u * I);
-      }
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          int v = kTile * t + sx[k];
-          if (v > g.V - 8) v = g.V - 8;
-          dma16s(sb[s], soff[s][k] + (uint32_t)(v - sx[k]) * 2u,
-                 base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
-        }
-    };
-    // loads one tile puts in flight for this wave
-    constexpr int OPS_BIG = W2_MAX + 2 * NS, OPS_SMALL = W2_MAX - 1 + 2 * NS;
-    const bool big = wave < NI - kSweepWaves * (W2_MAX - 1);
-    // wait until at most `left` (0 .. D-1) tiles' copies are still in flight (loads complete
-    // in order)
-    auto wait_tiles = [&](int left) {
-      if (left <= 0) {
-        vm_wait<0>();
-      } else if (left == 1 || D < 3) {
-        if (big) vm_wait<OPS_BIG>(); else vm_wait<OPS_SMALL>();
-      } else {
-        if (big) vm_wait<2 * OPS_BIG>(); else vm_wait<2 * OPS_SMALL>();
-      }
-    };
-
-    // matrix-core chain of the tile in stage stg, seeded with its U slice
-    auto mma = [&](int stg, f32x16& acc, uint4 (&x)[2]) {
-      const uint4* sl = lds + stg * SCH;
-      float u[16];
-      widen8(sl[s_idx0], u);
-      widen8(sl[s_idx1], u + 8);
-      if (NS == 2) {
-        x[0] = sl[s_idx0 + stream_tile_chunks()];
-        x[1] = sl[s_idx1 + stream_tile_chunks()];
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] = u[j];
-      const uint4* ab = sl + a_idx;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = as_bf16x8(ab[2 * ks]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc, 0, 0, 0);
-        if (SPLIT) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[SPLIT ? ks : 0], acc, 0, 0, 0);
-      }
-    };
-
-    int b0, b1;
     int rg = range + (group_row0 & 0);
     asm volatile("" : "+s"(rg));
     range_blocks(g, rg, b0, b1);
     // the last block of the vocabulary is short when V % 64 != 0: it leaves the pipeline
-    const bool ragged = (b1 * kVB > g.V);
-    const int bp1 = ragged ? b1 - 1 : b1;  // pipelined blocks [b0, bp1)
-    const int t0 = 2 * b0, t1 = 2 * bp1;
-
+    ragged = (b1 * kVB > g.V);
+    bp1 = ragged ? b1 - 1 : b1;  // pipelined blocks [b0, bp1)
+    t0 = 2 * b0;
+    t1 = 2 * bp1;
     // the first tile goes out before anything else (it depends on nothing the B rows or
     // the epilogue state need); the rest of the pipeline fills once they are in, so the
     // first step waits for one tile rather than D
     if (t0 < t1) issue(t0, 0);
+  }
+
+  // matrix-core chain of the tile in stage stg, seeded with its U slice
+  __device__ __forceinline__ void mma(int stg, f32x16& acc, uint4 (&x)[2], const bf16x8 (&bh)[NKS],
+                                      const bf16x8 (&bl)[SPLIT ? NKS : 1]) {
+    const uint4* sl = lds + stg * SCH;
+    float u[16];
+    widen8(sl[s_idx0], u);
+    widen8(sl[s_idx1], u + 8);
+    if (NS == 2) {
+      x[0] = sl[s_idx0 + stream_tile_chunks()];
+      x[1] = sl[s_idx1 + stream_tile_chunks()];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = u[j];
+    if (!BIAS) return;
+    const uint4* ab = sl + a_idx;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 a = as_bf16x8(ab[2 * ks]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc, 0, 0, 0);
+      if (SPLIT) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[SPLIT ? ks : 0], acc, 0, 0, 0);
+    }
+  }
+
+  // the B rows, the streamed tiles and the epilogue of the prepared group
+  __device__ __forceinline__ void run() {
+    bf16x8 bh[NKS];  // B operand (filled once the first tiles are in flight)
+    bf16x8 bl[SPLIT ? NKS : 1];
+    typename Epi::State st;
 
     // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row; from the packed
     // copy when the epilogue has one (coalesced; rows past the end read padding)
     const uint4* bpk = SPLIT ? nullptr : Epi::bpack(ep);
-    if (bpk) {
+    if (!BIAS) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) bh[ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    } else if (bpk) {
       const uint4* src = bpk + (size_t)(group_row0 / 32 + wave) * (NKS * kWave) + lane;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) bh[ks] = as_bf16x8(src[ks * kWave]);
@@ -415,12 +440,12 @@ __global__ void __launch_bounds__(kSweepThreads, 2)
       wait_tiles(min(D - 1, t1 - 1 - t0));
       stage_barrier();
       if (t0 + D < t1) issue(t0 + D, ahead(stg));
-      mma(stg, accA, xA);
+      mma(stg, accA, xA, bh, bl);
       stg = next_stage(stg);
       wait_tiles(min(D - 1, t1 - 2 - t0));
       stage_barrier();
       if (t0 + 1 + D < t1) issue(t0 + 1 + D, ahead(stg));
-      mma(stg, accB, xB);
+      mma(stg, accB, xB, bh, bl);
       Epi::template tile<0, false>(ep, st, accA, xA, t0 >> 1, row, owner);
       stg = next_stage(stg);
     }
@@ -431,14 +456,14 @@ __global__ void __launch_bounds__(kSweepThreads, 2)
       wait_tiles(min(D - 1, t1 - 1 - t));
       stage_barrier();
       if (t + D < t1) issue(t + D, ahead(stg));
-      mma(stg, accA, xA);
+      mma(stg, accA, xA, bh, bl);
       Epi::template tile<1, false>(ep, st, accB, xB, b - 1, row, owner);
       stg = next_stage(stg);
       // -- tile t + 1 (half 1); epilogue of tile t (half 0 of block b)
       wait_tiles(min(D - 1, t1 - 2 - t));
       stage_barrier();
       if (t + 1 + D < t1) issue(t + 1 + D, ahead(stg));
-      mma(stg, accB, xB);
+      mma(stg, accB, xB, bh, bl);
       Epi::template tile<0, false>(ep, st, accA, xA, b, row, owner);
       stg = next_stage(stg);
     }
@@ -454,14 +479,44 @@ __global__ void __launch_bounds__(kSweepThreads, 2)
       issue_ragged(2 * b + 1, 1);
       vm_wait<0>();
       __syncthreads();
-      mma(0, accA, xA);
+      mma(0, accA, xA, bh, bl);
       Epi::template tile<0, true>(ep, st, accA, xA, b, row, owner);
-      mma(1, accB, xB);
+      mma(1, accB, xB, bh, bl);
       Epi::refresh(ep, st, b, row);
       Epi::template tile<1, true>(ep, st, accB, xB, b, row, owner);
     }
     vm_wait<0>();
     Epi::finish(ep, st, row, owner, range);
+  }
+};
+
+// task -> (vocabulary range, first row group); the gsplit workgroups of one range are
+// dispatched to the same XCD (round-robin dispatch over 8 XCDs) so its W2t tiles come from
+// HBM once and from that XCD's L2 after
+__device__ __forceinline__ void sweep_task_of(const SweepGeom& g, int bid, int& range, int& g0) {
+  const int G = g.gsplit;
+  if ((g.nranges & 7) == 0) {
+    const int slot = bid >> 3;
+    range = (slot / G) * 8 + (bid & 7);
+    g0 = slot - (slot / G) * G;
+  } else {
+    range = bid / G;
+    g0 = bid - range * G;
+  }
+}
+
+// The sweep kernel: workgroup (range, g0) sweeps row groups g0, g0 + gsplit, ... over its
+// range.
+template <int NKS, bool SPLIT, int NSTAGE, class Epi>
+__global__ void __launch_bounds__(kSweepThreads, 2)
+    sweep_kernel(SweepGeom g, typename Epi::Params ep) {
+  extern __shared__ uint4 lds[];
+  int range, g0;
+  sweep_task_of(g, blockIdx.x, range, g0);
+  for (int group = g0; Epi::group_live(ep, group * kRowsPerGroup); group += g.gsplit) {
+    SweepTask<NKS, SPLIT, NSTAGE, Epi> task(g, ep, lds);
+    task.prepare(range, group);
+    task.run();
     __syncthreads();  // the next group reuses the stages
   }
 }

@@ -166,6 +166,20 @@ int dspark_draft_markov_noalloc(int R, int gamma, int V, int r, int d, dspark_dt
                                 float *lse, float *logit_x, void *bias_rows,
                                 int32_t *dev_status, hipStream_t stream);
 
+/* The parallel block's drafter alone, without the sequential head (the baseline the pages
+ * compare the head against; digest, Module B, and the latency analysis of the sequential
+ * module): x_k is sampled from softmax(U_k) itself (no bias; eq. (4) with the head's term
+ * removed), with the same two-level sampler, random streams and outputs as
+ * dspark_draft_markov (lse and logit_x of U_k; c and z from eq. (7) with W1[x_{k-1}];
+ * bias_rows = W1[x_{k-1}]).  bf16 operands only (DSPARK_EINVAL otherwise); workspace as
+ * dspark_draft_markov.  Timing it beside dspark_draft_markov gives the cost of the
+ * sequential head. */
+int dspark_draft_parallel(int R, int gamma, int V, int r, int d, dspark_dtype dt, const void *U,
+                          const void *h, const void *W1, const float *w, const float *temps,
+                          const int32_t *x0, uint64_t seed, uint64_t cycle, int32_t *x, float *c,
+                          float *z, float *lse, float *logit_x, void *bias_rows,
+                          int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* RNN head, eq. (6): W_gco [3r][2r + d] dt stacks the gate, candidate and output
  * projections (row blocks in that order; columns ordered [s ; W1 row ; h]; no biases);
  * s_0 = 0.  The bias row of step k is tanh(W_o z_k) with z_k holding s_{k-1}; c uses eq.

@@ -97,3 +97,25 @@ def test_bad_anchor_sets_fault_bit(ds):
     W2t = W2T(I["W2"])
     ds.draft_markov(T(I["U"]), T(I["h"]), T(I["W1"]), T(W2t), T(I["w"]), T(x0), status=status)
     assert int(N(status)[0]) & ds.FAULT_TOKEN
+
+
+PAR_CASES = [
+    ("par-c3-law", "c3", dict(R=40, gamma=4, V=8192, d=512)),
+    ("par-c2-R150", "c2", dict(R=150, gamma=3, V=3000, r=64, d=256)),
+    ("par-c2-r16", "c2", dict(R=70, gamma=3, V=1024, r=16, d=64)),
+]
+
+
+@pytest.mark.parametrize("name,base,kw", PAR_CASES, ids=[c[0] for c in PAR_CASES])
+def test_parallel_drafter_parity(ora, ds, name, base, kw):
+    """dspark_draft_parallel samples softmax(U_k) itself: the oracle's Markov draft with
+    W2 = 0 (the head's bias term removed) is the same computation."""
+    cfg = synth.scaled(synth.CONFIGS[base], **kw)
+    I = synth.inputs(cfg)
+    W2zero = np.zeros_like(I["W2"])
+    o = ora.draft_markov(I["U"], I["h"], I["W1"], W2zero, I["w"], I["x0"], 5, 2)
+    g = ds.draft_parallel(T(I["U"]), T(I["h"]), T(I["W1"]), T(I["w"]), T(I["x0"]), 5, 2)
+    g = {k: N(v) for k, v in g.items()}
+    g["bias_rows"] = synth.bf16_to_f32(g["bias_rows"])
+    compared, excused = compare_draft(o, g, name)
+    print(f"{name}: compared {compared}, near-tie mismatches {excused}")

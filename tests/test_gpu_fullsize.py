@@ -201,3 +201,18 @@ def test_c5_cycle_full(ora, ds, c5):
     target = _target(cfg, I, g["bias_rows"])
     _verify_both(ora, ds, cfg, I, target, g["x"], g["lse"], g["logit_x"],
                  np.asarray(g["bias_rows"], np.float32), ell, "c5-full")
+
+
+def test_c3_parallel_drafter_full(ora, ds):
+    """The draft without the sequential head at the headline sizes (what the head's cost
+    is measured against): the oracle's Markov draft with W2 = 0."""
+    cfg = synth.CONFIGS["c3"]
+    I = synth.inputs(cfg)
+    print("c3 parallel drafter: oracle with W2 = 0", flush=True)
+    o = ora.draft_markov(I["U"], I["h"], I["W1"], np.zeros_like(I["W2"]), I["w"], I["x0"], 0,
+                         CYCLE)
+    g = ds.draft_parallel(T(I["U"]), T(I["h"]), T(I["W1"]), T(I["w"]), T(I["x0"]), 0, CYCLE)
+    g = {k: N(v) for k, v in g.items()}
+    g["bias_rows"] = synth.bf16_to_f32(g["bias_rows"])
+    compared, excused = compare_draft(o, g, "c3-parallel-full")
+    print(f"c3 parallel drafter: compared {compared}, excused {excused}")
