@@ -303,8 +303,10 @@ __global__ void __launch_bounds__(kCombineThreads) draft_combine_kernel(
 // The inputs advance in chunks of 64 through a two-stage LDS ring, copied straight from
 // global memory with global_load_lds_dwordx4: one copy moves 8 whole 128-byte row segments
 // (8 lanes per row), and row rho of the stage keeps its 16-byte piece c in slot
-// c ^ (rho % 8), so the MFMA fragment reads (lane l: row l % 32, piece 2 ks + l / 32) of
-// 8 consecutive lanes fall on 8 different slots: conflict-free ds_read_b128.  Wave w copies
+// c ^ ((rho / 2) % 8).  A ds_read_b128 is served 16 lanes at a time over 64 four-byte
+// banks, and a 128-byte row spans half of them (even rows one half, odd rows the other),
+// so the fragment reads of 16 consecutive lanes (lane l: row l % 32, piece 2 ks + l / 32)
+// land on 8 different slots in each half: conflict-free.  Wave w copies
 // rows 8w .. 8w + 8 of every 32-row block of h and W_h.  Rows and outputs past the end are
 // clamped to the last one (their results are not stored); inputs past d occur only in the
 // last chunk, are read clamped and zeroed in registers.  Tiles that share rows are placed
@@ -316,7 +318,7 @@ constexpr int kHpSplit = 2;
 template <bool MASK>
 __device__ __forceinline__ void hproj_chunk(const uint8_t* buf, int wave, int lane, int kc,
                                             int d, f32x16 (&acc)[3]) {
-  const int rl = lane & 31, sw = lane & 7;
+  const int rl = lane & 31, sw = (rl >> 1) & 7;
 #pragma unroll
   for (int ks = 0; ks < kHpKS; ++ks) {
     const int slot = 16 * ((2 * ks + (lane >> 5)) ^ sw);
@@ -353,7 +355,7 @@ __global__ void __launch_bounds__(256, 2) rnn_hproj_bf16_kernel(
   const int lane = threadIdx.x & 63, ln = lane & 31, hh = lane >> 5;
 
   // copy lane: row 8 wave + lane / 8 of each 32-row block, piece (lane % 8) ^ (lane / 8)
-  const int crow = 8 * wave + (lane >> 3), cpiece = (lane & 7) ^ (lane >> 3);
+  const int crow = 8 * wave + (lane >> 3), cpiece = (lane & 7) ^ ((crow >> 1) & 7);
   uint32_t hoff[4], woff[3];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
