@@ -302,6 +302,7 @@ def bench_cycle(args):
                 c_star=torch.empty((R, G), dtype=torch.float32, device=dev))
     dws = torch.empty(ds.draft_workspace_bytes(R, G, V, r, d), dtype=torch.uint8, device=dev)
     vws = torch.empty(ds.verify_workspace_bytes(R, G, V, r), dtype=torch.uint8, device=dev)
+    sws = torch.empty(ds.schedule_workspace_bytes(R, G), dtype=torch.uint8, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     x0 = torch.empty_like(x0_first)
 
@@ -333,7 +334,7 @@ def bench_cycle(args):
     for t in range(nsteps):
         ds.draft_markov(U, h, W1, W2t, w, x0, SEED, t, out=dout, ws=dws, status=status)
         targets.append(make_target(torch, cfg, U, W2t, dout, gen))
-        ds.schedule(dout["c"], sps, cfg.sps_B0, ds.SYNC_BREAK, out=sout, status=status)
+        ds.schedule(dout["c"], sps, cfg.sps_B0, ds.SYNC_BREAK, out=sout, ws=sws, status=status)
         ds.verify(targets[t], U, W2t, dout["bias_rows"], dout["x"], dout["lse"],
                   dout["logit_x"], sout["ell"], SEED, t, out=vout, ws=vws, status=status)
         emitted_ref.append(vout["y"].clone())
@@ -350,7 +351,7 @@ def bench_cycle(args):
         ds.draft_markov(U, h, W1, W2t, w, x0, SEED, t, out=dout, ws=dws, status=status,
                         events=ev_args[t])
         e[1].record()
-        ds.schedule(dout["c"], sps, cfg.sps_B0, ds.SYNC_BREAK, out=sout, status=status)
+        ds.schedule(dout["c"], sps, cfg.sps_B0, ds.SYNC_BREAK, out=sout, ws=sws, status=status)
         e[2].record()
         ds.verify(targets[t], U, W2t, dout["bias_rows"], dout["x"], dout["lse"],
                   dout["logit_x"], sout["ell"], SEED, t, out=vout, ws=vws, status=status)

@@ -310,7 +310,11 @@ def draft_rnn(U, h, W1, W2t, W_gco, w, x0, seed=0, cycle=0, *, temps=None, out=N
                   ws=ws, status=status)
 
 
-def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, *, out=None, status=None):
+def schedule_workspace_bytes(R, gamma) -> int:
+    return int(lib().dspark_schedule_workspace_bytes(R, gamma))
+
+
+def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, *, out=None, ws=None, status=None):
     """Prefix scheduler; returns dict(ell, a, stats) (device tensors)."""
     torch = _torch()
     _chk(c, "c", dtype=torch.float32)
@@ -325,9 +329,11 @@ def schedule(c, sps, sps_B0, mode=SYNC_BREAK, c_lag=None, *, out=None, status=No
         out = dict(ell=torch.empty(R, dtype=torch.int32, device=dev),
                    a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
                    stats=torch.empty(4, dtype=torch.float64, device=dev))
+    ws = _ws(schedule_workspace_bytes(R, gamma), dev, ws)
     rc = lib().dspark_schedule(R, gamma, _p(c), _p(c_lag), R_lag, _p(sps), sps_B0,
                                sps.numel(), mode, _p(out["ell"]), _p(out["a"]),
-                               _p(out["stats"]), _p(status), None, 0, _stream())
+                               _p(out["stats"]), _p(status), _p(ws),
+                               ws.numel() * ws.element_size(), _stream())
     _raise("dspark_schedule", rc)
     return out
 

@@ -146,6 +146,8 @@ struct DecodeWs {
   size_t dws_bytes;
   void* vws;
   size_t vws_bytes;
+  void* sws;
+  size_t sws_bytes;
   size_t bytes;
 };
 
@@ -170,6 +172,8 @@ inline DecodeWs decode_carve(void* base, int R, int gamma, int V, int r, int d, 
   w.dws = cv.take<char>(w.dws_bytes);
   w.vws_bytes = dspark_verify_workspace_bytes(R, gamma, V, r);
   w.vws = cv.take<char>(w.vws_bytes);
+  w.sws_bytes = dspark_schedule_workspace_bytes(R, gamma);
+  w.sws = cv.take<char>(w.sws_bytes);
   w.bytes = cv.bytes();
   return w;
 }
@@ -248,8 +252,8 @@ int dspark_decode_run(int R, int gamma, int V, int r, int d, dspark_dtype dt, in
           lag ? DSPARK_SCHED_ASYNC_LAG2
               : (policy == DSPARK_DECODE_SYNC_BREAK ? DSPARK_SCHED_SYNC_BREAK : DSPARK_SCHED_GLOBAL);
       rc = dspark_schedule(R, gamma, ccur, lag ? wl.c[(cyc - 2) % 3] : nullptr, lag ? R : 0, sps,
-                           sps_B0, sps_len, mode, wl.ell, nullptr, nullptr, dev_status, nullptr,
-                           0, stream);
+                           sps_B0, sps_len, mode, wl.ell, nullptr, nullptr, dev_status, wl.sws,
+                           wl.sws_bytes, stream);
       if (rc != DSPARK_OK) break;
     } else {
       policy_lengths_kernel<<<(R + 255) / 256, 256, 0, stream>>>(

@@ -1,208 +1,254 @@
 // schedule.hip -- the hardware-aware prefix scheduler (digest page, Module E, Algorithm 1,
 // and the production variants without the break and with the two-step lag).
 //
-// The whole scheduler is one workgroup (1024 threads) working in LDS:
-//   1. prefix survival a_{q,j} = a_{q,j-1} * c_{q,j} in float, one request per thread;
-//   2. 64-bit keys (~bits(a) << 32 | q*gamma + j-1) sorted ascending (bitonic, in registers
-//      and shuffles up to a wave's span, through LDS beyond), which is
-//      descending a with ties broken by q, then j -- a is non-negative, so its bit pattern
-//      orders like its value, and the j order keeps every request's admitted set a prefix;
-//   3. an exact integer prefix sum of floor(a * 2^32): tau of every prefix of the order is
-//      then independent of summation order, so the parallel search below decides exactly
-//      as the sequential loop of Algorithm 1 would;
-//   4. Theta_n = tau_n * SPS(R + n) in double for every n, and the admitted count n:
-//      first non-improving n minus one (break), first maximiser (no break), or the
-//      capacity of the lagged batch (two-step lag);
-//   5. ell_q = number of q's entries among the first n.
-#include <type_traits>
+// Entry e = (q, j) of a batch has the prefix survival a_e = c_{q,1} * ... * c_{q,j} (float,
+// left to right) and the 64-bit key
+//     key_e = (~bits(a_e)) << 32 | (q * gamma + j - 1),
+// so ascending keys are descending a with ties broken by q, then j (a is non-negative, so
+// its bit pattern orders like its value, and the j order keeps every request's admitted set
+// a prefix).  Entries with a = 0 are not candidates.  Algorithm 1 admits the candidates in
+// that order; entry e is admitted n_e = rho_e + 1 -th, where
+//     rho_e = #{candidates f : key_f < key_e},   S_e = sum of floor(a_f * 2^32) over them,
+// and tau after it is exactly R + (S_e + floor(a_e * 2^32)) * 2^-32.  Both are dominance
+// counts over all pairs, so no sorted array is needed, and Theta_{n_e} and Theta_{n_e - 1}
+// (the break's comparison) follow from e alone.  The increments are integers, so tau never
+// depends on a summation order, and every decision is the one the sequential loop of
+// Algorithm 1 takes.
+//
+// One launch.  Every workgroup rebuilds its batch's keys in LDS; each wave takes XW entries
+// and sweeps all keys in its lanes (one 64-bit compare and one 64-bit conditional add per
+// pair: the increment carries 2^48, so the count rides in the high bits of the same sum).
+// A workgroup then publishes its decisive entry: the first key that drops Theta (break),
+// the key with the largest Theta (no break), the count n at the largest Theta (lagged batch
+// of the two-step lag), or its number of candidates (current batch of the two-step lag).
+// The last workgroup to publish (every workgroup checks whether all others have) reduces the
+// publications.  With the break or without it, that gives the first key not admitted, and
+// its LDS still holds every key: n, tau and ell_q are counts and sums over the keys below
+// it.  In the two-step-lag mode the lagged batch's workgroups run beside the current batch's
+// and the admitted set is read back from each entry's rank.
+//
+// Publication without a zeroed counter and without cache maintenance: the workspace holds an
+// epoch word; a call's workgroups read it at their start and publish with tag = epoch + 1,
+// and the finishing workgroup stores epoch + 1 back, so a replayed graph reads the epoch
+// afresh and words left by earlier calls never carry the current tag.  A publication is two
+// payload words and a check word, the tag's hash mixed with the payload words' hashes, all
+// stored at device scope (written through to the point of coherence that every XCD shares).
+// A reader that loads the three words and finds the check consistent with the current tag
+// has the current payload: a stale word changes the check by a hash difference.  A
+// workgroup waits until its own three stores are acknowledged before it loads the others'
+// words, so the owner of the last acknowledged publication sees every publication.  Two
+// workgroups that both see all of them compute and store the same results.
+#include <climits>
 
 #include "dev.h"
 #include "host.h"
 
 namespace dspark {
 
-constexpr int kSchedThreads = 1024;
+constexpr int kRankThreads = 1024;
+constexpr int kRankWaves = kRankThreads / kWave;  // 16
+constexpr int kRankUnroll = 4;                    // key rows in flight per lane
+constexpr int kRankMaxBlocks = 256;               // workgroups per batch (XW is picked to fit)
+constexpr unsigned long long kCountUnit = 1ull << 48;  // S < N * 2^32 <= 2^45 < 2^48
+constexpr unsigned long long kNoKey = ~0ull;           // non-candidates and "none"
+constexpr unsigned long long kNegInfBits = 0xFFF0000000000000ull;  // -inf as a double
+constexpr int kPubWords = 4;  // words per publication slot (payload, payload, check, unused)
 
-struct SchedShared {
-  unsigned long long* key;  // [npad]
-  unsigned long long* pre;  // [npad] inclusive prefix sums of the increments
+enum SchedEval { kEvalNone = 0, kEvalBreak = 1, kEvalArgmax = 2 };
+
+struct SchedBatch {
+  const float* c;           // [R][gamma]
+  int R;
+  int nblocks;              // workgroups of this batch
+  int eval;                 // SchedEval
+  bool lagged;              // the lagged batch (argmax publishes n instead of the key)
+  int32_t* rank;            // [R * gamma] rho_e (INT_MAX for non-candidates), or null
+  unsigned long long* tau;  // [R * gamma] tau through e in 2^-32 units, or null
+  float* a_out;             // [R][gamma] prefix survival, or null
+};
+
+struct SchedOut {
+  int mode;
+  int32_t* ell;
+  double* stats;
+  unsigned long long* epoch;  // one word
+  unsigned long long* pub;    // [b0.nblocks + b1.nblocks][kPubWords]: payload, payload, check
 };
 
 __device__ __forceinline__ double theta_of(unsigned long long tau_fx, float sps) {
   return ((double)tau_fx * 0x1p-32) * (double)sps;
 }
 
-__device__ __forceinline__ unsigned long long incr_of_key(unsigned long long key) {
-  const float a = __uint_as_float(~(uint32_t)(key >> 32));
-  return (unsigned long long)((double)a * 4294967296.0);
+// floor(a * 2^32) for a in [0, 1] from the float's fields (exact)
+__device__ __forceinline__ unsigned long long incr_of_bits(uint32_t b) {
+  const int e = (int)(b >> 23);
+  if (e == 0) return 0ull;  // zero and subnormals: a * 2^32 < 1
+  const unsigned long long m = (b & 0x7FFFFFu) | 0x800000u;
+  const int sh = e - 118;  // a * 2^32 = m * 2^(e - 150 + 32), e <= 127
+  return sh >= 0 ? m << sh : (sh > -32 ? m >> (-sh) : 0ull);
 }
 
-// smallest power of two >= x (x >= 1)
-__device__ __forceinline__ int pow2_ceil(int x) { return x <= 1 ? 1 : 1 << (32 - __clz(x - 1)); }
-
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int d) {
-  const int lo = __shfl_xor((int)(uint32_t)v, d, kWave);
-  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), d, kWave);
-  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+// 64-bit finalizer of MurmurHash3 (fmix64): a bijection that spreads every input bit
+__device__ __forceinline__ unsigned long long mix64(unsigned long long x) {
+  x ^= x >> 33;
+  x *= 0xff51afd7ed558ccdull;
+  x ^= x >> 33;
+  x *= 0xc4ceb9fe1a85ec53ull;
+  x ^= x >> 33;
+  return x;
 }
 
-// the key of lane ^ d for d < 32: a swizzle in xor mode (and-mask 31, xor-mask d) moves
-// both halves without an address operand
-template <int D>
-__device__ __forceinline__ unsigned long long swz_xor_u64(unsigned long long v) {
-  constexpr int kPat = (D << 10) | 0x1F;
-  const int lo = __builtin_amdgcn_ds_swizzle((int)(uint32_t)v, kPat);
-  const int hi = __builtin_amdgcn_ds_swizzle((int)(uint32_t)(v >> 32), kPat);
-  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+__device__ __forceinline__ unsigned long long pub_check(unsigned long long tag,
+                                                        unsigned long long w0,
+                                                        unsigned long long w1) {
+  return mix64(tag) ^ mix64(w0 ^ 0x9e3779b97f4a7c15ull) ^ mix64(w1 ^ 0x632be59bd9b4e019ull);
 }
 
-// the key of lane ^ D for D = 1, 2: a quad permutation on the DPP network (no LDS pipe)
-template <int D>
-__device__ __forceinline__ unsigned long long dpp_xor_u64(unsigned long long v) {
-  constexpr int kCtrl = D == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, kCtrl, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), kCtrl, 0xF, 0xF, false);
-  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+// s_waitcnt vmcnt(0) (gfx9 encoding; expcnt and lgkmcnt left free): every memory access
+// this wave issued has completed, stores included
+constexpr int kWaitStores = 0x0F70;
+
+__device__ __forceinline__ void st_dev(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long* p) {
+  return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// compare-exchange seen from one side: the kept key is the smaller of (x, y) when keep_min,
-// else the larger (one compare, one 64-bit select)
-__device__ __forceinline__ unsigned long long cx_keep(unsigned long long x, unsigned long long y,
-                                                      bool keep_min) {
-  return ((y < x) == keep_min) ? y : x;
+// this wave's device-scope stores are acknowledged before anything after this point issues
+__device__ __forceinline__ void stores_done() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // keeps the compiler's order
+  __builtin_amdgcn_s_waitcnt(kWaitStores);
 }
 
-// Bitonic sort of npad keys (a power of two, npad <= 1024 * KP), ascending, starting at
-// stage kstart (blocks of kstart / 2 already sorted, alternately ascending and descending).
-// Thread t holds keys t*KP .. t*KP + KP-1 in registers: partners less than KP apart are in
-// the same thread, less than 64*KP apart in the same wave (one shuffle per key), farther
-// through LDS (two buffers used in turn, so each such step needs a single barrier).
-// Threads past npad / KP hold nothing but join the barriers.
-template <int KP>
-__device__ void sched_bitonic(unsigned long long (&key)[KP], int npad, int kstart,
-                              unsigned long long* buf0, unsigned long long* buf1) {
-  const int t = threadIdx.x;
-  const int i0 = t * KP;
-  const bool active = i0 < npad;
-  int which = 0;
-  // one in-wave step at lane distance D (compile time), when the stage has it
-  auto wave_step = [&](auto dc, int k) {
-    constexpr int D = decltype(dc)::value;
-    const int j = D * KP;
-    if (j >= k) return;
-    const bool keep_min = ((i0 & j) == 0) == ((i0 & k) == 0);
-#pragma unroll
-    for (int s = 0; s < KP; ++s) {
-      const unsigned long long y = D == 32 ? shfl_xor_u64(key[s], 32)
-                                   : (D <= 2 ? dpp_xor_u64<D>(key[s]) : swz_xor_u64<D>(key[s]));
-      key[s] = cx_keep(key[s], y, keep_min);
-    }
-  };
-  for (int k = kstart; k <= npad; k <<= 1) {
-    // partners a wave or more apart: through LDS
-    for (int j = k >> 1; j >= kWave * KP; j >>= 1) {
-      unsigned long long* b = which ? buf1 : buf0;
-      if (active)
-#pragma unroll
-        for (int s = 0; s < KP; ++s) b[i0 + s] = key[s];
-      __syncthreads();
-      const bool keep_min = ((i0 & j) == 0) == ((i0 & k) == 0);
-      if (active)
-#pragma unroll
-        for (int s = 0; s < KP; ++s) key[s] = cx_keep(key[s], b[(i0 + s) ^ j], keep_min);
-      which ^= 1;
-    }
-    // partners in the same wave (j >= KP and k > j lie above the slot bits, so one
-    // direction serves all KP keys)
-    wave_step(std::integral_constant<int, 32>{}, k);
-    wave_step(std::integral_constant<int, 16>{}, k);
-    wave_step(std::integral_constant<int, 8>{}, k);
-    wave_step(std::integral_constant<int, 4>{}, k);
-    wave_step(std::integral_constant<int, 2>{}, k);
-    wave_step(std::integral_constant<int, 1>{}, k);
-    // partners in the same thread
-#pragma unroll
-    for (int j = KP / 2; j > 0; j >>= 1) {
-      if (j >= k) continue;
-#pragma unroll
-      for (int s = 0; s < KP; ++s) {
-        const int p = s ^ j;
-        if (p > s) {
-          const bool up = ((i0 + s) & k) == 0;
-          const unsigned long long x = key[s], y = key[p];
-          const bool sw = (x > y) == up;
-          key[s] = sw ? y : x;
-          key[p] = sw ? x : y;
-        }
-      }
-    }
+// a 64-bit value of the partner lane of butterfly step STEP (the DPP network of dev.h)
+template <int STEP>
+__device__ __forceinline__ unsigned long long partner64(unsigned long long v) {
+  const uint32_t lo = xlane_partner<STEP>((uint32_t)v);
+  const uint32_t hi = xlane_partner<STEP>((uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+// the values of lanes l and l ^ 32, in the order (lower half, upper half)
+__device__ __forceinline__ void halves64(unsigned long long v, unsigned long long& a,
+                                         unsigned long long& b) {
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32),
+                                                   false, false);
+  a = ((unsigned long long)hi[0] << 32) | lo[0];
+  b = ((unsigned long long)hi[1] << 32) | lo[1];
+}
+
+// sum across the wave (exact integers: every lane ends with the same total)
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+  v += partner64<0>(v);
+  v += partner64<1>(v);
+  v += partner64<2>(v);
+  v += partner64<3>(v);
+  v += partner64<4>(v);
+  unsigned long long a, b;
+  halves64(v, a, b);
+  return a + b;
+}
+
+// the published quantity of one batch: (theta, order) for the argmax (largest theta, then
+// smallest order), the smallest order for the break, the sum of counts otherwise
+struct Pub {
+  unsigned long long o;  // key or n ("none": kNoKey); candidate count for kEvalNone
+  double th;             // -inf if none
+};
+
+__device__ __forceinline__ Pub pub_none(int eval) {
+  Pub p;
+  p.o = eval == kEvalNone ? 0ull : kNoKey;
+  p.th = -INFINITY;
+  return p;
+}
+
+__device__ __forceinline__ void pub_merge(Pub& a, const Pub& b, int eval) {
+  if (eval == kEvalNone) {
+    a.o += b.o;
+  } else if (eval == kEvalBreak) {
+    a.o = b.o < a.o ? b.o : a.o;
+  } else if (b.th > a.th || (b.th == a.th && b.o < a.o)) {
+    a = b;
   }
 }
 
-template <int KP>
-__device__ void sched_sort_lds(int npad, int kstart, SchedShared sh) {
-  unsigned long long key[KP];
-  const int t = threadIdx.x;
-  const bool active = t * KP < npad;
-#pragma unroll
-  for (int s = 0; s < KP; ++s) key[s] = active ? sh.key[t * KP + s] : ~0ull;
-  __syncthreads();  // every key is in registers before the buffers are reused
-  sched_bitonic<KP>(key, npad, kstart, sh.pre, sh.key);
-  __syncthreads();
-  if (active)
-#pragma unroll
-    for (int s = 0; s < KP; ++s) sh.key[t * KP + s] = key[s];
-  __syncthreads();
+template <int STEP>
+__device__ __forceinline__ Pub partner_pub(const Pub& p) {
+  Pub q;
+  q.o = partner64<STEP>(p.o);
+  q.th = __longlong_as_double((long long)partner64<STEP>((unsigned long long)__double_as_longlong(p.th)));
+  return q;
 }
 
-// inclusive scan of v over the workgroup (wave scans, then the wave totals)
-__device__ __forceinline__ unsigned long long block_scan_u64(unsigned long long v,
-                                                             unsigned long long* wsum) {
+__device__ __forceinline__ Pub wave_pub(Pub p, int eval) {
+  pub_merge(p, partner_pub<0>(p), eval);
+  pub_merge(p, partner_pub<1>(p), eval);
+  pub_merge(p, partner_pub<2>(p), eval);
+  pub_merge(p, partner_pub<3>(p), eval);
+  pub_merge(p, partner_pub<4>(p), eval);
+  Pub lo, hi;
+  halves64(p.o, lo.o, hi.o);
+  unsigned long long tl, th;
+  halves64((unsigned long long)__double_as_longlong(p.th), tl, th);
+  lo.th = __longlong_as_double((long long)tl);
+  hi.th = __longlong_as_double((long long)th);
+  pub_merge(lo, hi, eval);
+  return lo;
+}
+
+__host__ __device__ __forceinline__ int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Workgroups [0, b0.nblocks) take batch b0 (the current batch), the rest batch b1 (the lagged
+// batch of the two-step-lag mode).  Workgroup blk of a batch owns entries [blk * XB, blk * XB
+// + XB) in request-major order; wave w of it entries blk * XB + w * XW + i, i < XW.
+// LDS: the batch's keys with their increments (+ 2^48), entry (q, j) at slot j * R + q so
+// that the threads building them write consecutive slots, padded with non-candidates; then,
+// with SPS_LDS, the table slice SPS(R .. R + N).
+template <int XW, bool SPS_LDS>
+__global__ void __launch_bounds__(kRankThreads) schedule_kernel(
+    int gamma, SchedBatch b0, SchedBatch b1, const float* __restrict__ sps, int sps_B0,
+    int npad_max, SchedOut out, int32_t* status) {
+  constexpr int XB = XW * kRankWaves;
+  extern __shared__ ulonglong2 ent[];
+  __shared__ Pub e_pub[XB];
+  __shared__ Pub s_cur, s_lag;
+  __shared__ unsigned long long s_red[kRankWaves];
+  __shared__ int s_last;
+  const bool second = (int)blockIdx.x >= b0.nblocks;
+  const SchedBatch B = second ? b1 : b0;
+  const int blk = second ? (int)blockIdx.x - b0.nblocks : (int)blockIdx.x;
+  const int R = B.R, N = R * gamma;
+  const int npad = round_up(N, kWave * kRankUnroll);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int lo = __shfl_up((int)(uint32_t)v, o, kWave);
-    const int hi = __shfl_up((int)(uint32_t)(v >> 32), o, kWave);
-    const unsigned long long up = ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
-    if (lane >= o) v += up;
-  }
-  if (lane == kWave - 1) wsum[wave] = v;
-  __syncthreads();
-  if (wave == 0) {
-    unsigned long long x = lane < kSchedThreads / kWave ? wsum[lane] : 0ull;
-#pragma unroll
-    for (int o = 1; o < kSchedThreads / kWave; o <<= 1) {
-      const int lo = __shfl_up((int)(uint32_t)x, o, kWave);
-      const int hi = __shfl_up((int)(uint32_t)(x >> 32), o, kWave);
-      const unsigned long long up = ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
-      if (lane >= o) x += up;
-    }
-    if (lane < kSchedThreads / kWave) wsum[lane] = x;
-  }
-  __syncthreads();
-  const unsigned long long base = wave > 0 ? wsum[wave - 1] : 0ull;
-  __syncthreads();  // wsum is reused by the next scan
-  return v + base;
-}
+  const int nwg = b0.nblocks + b1.nblocks;
 
-// steps 1-3 for one batch of confidences; returns the candidate count |E|.  *npad_io is the
-// sorted length on entry (the padded layout) and on return (the layout actually used).
-//
-// Each request's keys already ascend (a falls along j, ties keep j order).  When the padded
-// run layout fits, request q's keys sit at [q * P, q * P + P) with the odd runs reversed,
-// which is the state a bitonic sort reaches after its stage P, so the sort starts at 2P;
-// otherwise the keys sit at q*gamma + j - 1 and the sort starts from pairs.
-__device__ int sched_sort_scan(int R, int gamma, const float* __restrict__ c, float* a_out,
-                               int* npad_io, SchedShared sh, unsigned long long* red_u64,
-                               int* red_i, int32_t* status) {
-  const int P = pow2_ceil(gamma), Rp = pow2_ceil(R);
-  const bool runs = (long)Rp * P <= *npad_io;
-  const int npad = runs ? Rp * P : *npad_io;
-  *npad_io = npad;
-  for (int i = threadIdx.x; i < npad; i += kSchedThreads) sh.key[i] = ~0ull;
-  __syncthreads();
-  for (int q = threadIdx.x; q < R; q += kSchedThreads) {
-    const float* cq = c + (size_t)q * gamma;
+  // every load below is issued before the first one is used: one round trip to memory
+  float* lsps = reinterpret_cast<float*>(ent + npad_max);
+  const float* tsps = SPS_LDS ? lsps : sps + (R - sps_B0);  // SPS(R + n) for n = 0..N
+  constexpr int kSpsPer = SPS_LDS ? (4096 + kRankThreads) / kRankThreads : 1;  // N <= 4096
+  float sv[kSpsPer];
+  if (SPS_LDS) {
+#pragma unroll
+    for (int u = 0; u < kSpsPer; ++u) {
+      const int n = (int)threadIdx.x + u * kRankThreads;
+      sv[u] = n <= N ? sps[R - sps_B0 + n] : 0.0f;
+    }
+  }
+  const float sps_R = sps[b0.R - sps_B0];  // SPS(R) of the current batch
+  const float sps_Rl = b1.nblocks > 0 ? sps[b1.R - sps_B0] : 0.0f;
+
+  // keys of every entry of the batch
+  for (int q = threadIdx.x; q < R; q += kRankThreads) {
+    const float* cq = B.c + (size_t)q * gamma;
     float run = 1.0f;
     for (int j0 = 0; j0 < gamma; j0 += 8) {
       float cv[8];
@@ -214,179 +260,247 @@ __device__ int sched_sort_scan(int R, int gamma, const float* __restrict__ c, fl
         if (j >= gamma) break;
         float cj = cv[u];
         if (!(cj >= 0.0f && cj <= 1.0f)) {
-          raise_fault(status, DSPARK_FAULT_CONF);
+          if (blk == 0) raise_fault(status, DSPARK_FAULT_CONF);
           cj = (cj > 1.0f) ? 1.0f : 0.0f;  // NaN and negatives -> 0
         }
         run = (j == 0) ? cj : __fmul_rn(run, cj);
-        const int idx = q * gamma + j;
-        if (a_out) a_out[idx] = run;
-        const int pos = runs ? q * P + ((q & 1) ? P - 1 - j : j) : idx;
-        sh.key[pos] = (run > 0.0f)
-                          ? (((unsigned long long)(~__float_as_uint(run)) << 32) | (unsigned)idx)
-                          : ~0ull;
+        const uint32_t bits = __float_as_uint(run);
+        ent[j * R + q] = run > 0.0f
+                             ? make_ulonglong2(((unsigned long long)(~bits) << 32) |
+                                                   (unsigned)(q * gamma + j),
+                                               incr_of_bits(bits) + kCountUnit)
+                             : make_ulonglong2(kNoKey, 0ull);
       }
     }
   }
-  __syncthreads();
-  const int kstart = runs ? 2 * P : 2;
-  if (npad <= 2048)
-    sched_sort_lds<2>(npad, kstart, sh);
-  else if (npad <= 4096)
-    sched_sort_lds<4>(npad, kstart, sh);
-  else
-    sched_sort_lds<8>(npad, kstart, sh);
-
-  // |E| = index of the first padding key
-  if (threadIdx.x == 0) *red_i = npad;
-  __syncthreads();
-  for (int i = threadIdx.x; i < npad; i += kSchedThreads)
-    if (sh.key[i] == ~0ull && (i == 0 || sh.key[i - 1] != ~0ull)) atomicMin(red_i, i);
-  __syncthreads();
-  const int nE = *red_i;
-
-  // inclusive prefix sums of the increments: contiguous chunks per thread, then a scan of
-  // the per-thread totals
-  const int per = npad / kSchedThreads > 0 ? npad / kSchedThreads : 1;
-  const int lo = threadIdx.x * per;
-  unsigned long long run = 0;
-  if (lo < npad) {
-    for (int i = lo; i < lo + per; ++i) {
-      run += (i < nE) ? incr_of_key(sh.key[i]) : 0ull;
-      sh.pre[i] = run;
-    }
-  }
-  const unsigned long long incl = block_scan_u64(lo < npad ? run : 0ull, red_u64);
-  const unsigned long long base = incl - (lo < npad ? run : 0ull);
-  if (lo < npad)
-    for (int i = lo; i < lo + per; ++i) sh.pre[i] += base;
-  __syncthreads();
-  return nE;
-}
-
-__device__ __forceinline__ unsigned long long tau_at(int R, const SchedShared& sh, int n) {
-  return ((unsigned long long)R << 32) + (n > 0 ? sh.pre[n - 1] : 0ull);
-}
-
-// step 4 without the break: smallest n in [0, nE] reaching the largest Theta_n
-__device__ int sched_argmax(int R, int nE, const float* __restrict__ sps, int sps_B0,
-                            const SchedShared& sh, double* red_d, int* red_i) {
-  double best = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int n = threadIdx.x; n <= nE; n += kSchedThreads) {
-    const double t = theta_of(tau_at(R, sh, n), sps[R + n - sps_B0]);
-    if (t > best) {  // n increases within a thread: strict keeps the smallest
-      best = t;
-      bi = n;
-    }
-  }
-  // wave, then workgroup: the largest Theta, ties to the smaller n
+  for (int s = N + threadIdx.x; s < npad; s += kRankThreads) ent[s] = make_ulonglong2(kNoKey, 0ull);
+  if (SPS_LDS) {
 #pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const double t2 = __shfl_xor(best, o, kWave);
-    const int i2 = __shfl_xor(bi, o, kWave);
-    if (t2 > best || (t2 == best && i2 < bi)) {
-      best = t2;
-      bi = i2;
+    for (int u = 0; u < kSpsPer; ++u) {
+      const int n = (int)threadIdx.x + u * kRankThreads;
+      if (n <= N) lsps[n] = sv[u];
     }
   }
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  if (lane == 0) {
-    red_d[wave] = best;
-    red_i[wave] = bi;
-  }
+  // the epoch is needed only to publish: loaded after the inputs, so their waits skip it
+  const unsigned long long tag = ld_dev(out.epoch) + 1ull;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < kSchedThreads / kWave; ++w)
-      if (red_d[w] > best || (red_d[w] == best && red_i[w] < bi)) {
-        best = red_d[w];
-        bi = red_i[w];
+
+  // this wave's entries (uniform across the wave: broadcast reads)
+  const int e0 = blk * XB + wave * XW;
+  unsigned long long xk[XW];
+#pragma unroll
+  for (int i = 0; i < XW; ++i) {
+    const int e = e0 + i;
+    xk[i] = e < N ? ent[(e % gamma) * R + e / gamma].x : kNoKey;
+  }
+  unsigned long long acc[XW];
+#pragma unroll
+  for (int i = 0; i < XW; ++i) acc[i] = 0ull;
+  for (int s0 = lane; s0 < npad; s0 += kWave * kRankUnroll) {
+    ulonglong2 y[kRankUnroll];
+#pragma unroll
+    for (int u = 0; u < kRankUnroll; ++u) y[u] = ent[s0 + u * kWave];
+#pragma unroll
+    for (int u = 0; u < kRankUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < XW; ++i) acc[i] += (y[u].x < xk[i]) ? y[u].y : 0ull;
+  }
+#pragma unroll
+  for (int i = 0; i < XW; ++i) acc[i] = wave_sum_u64(acc[i]);
+
+  // lane i < XW evaluates entry e0 + i
+  if (lane < XW) {
+    const int i = lane;
+    const int e = e0 + i;
+    unsigned long long A = acc[0], key = xk[0];
+#pragma unroll
+    for (int k = 1; k < XW; ++k)
+      if (i == k) {
+        A = acc[k];
+        key = xk[k];
       }
-    red_i[0] = bi;
+    Pub p = pub_none(B.eval);
+    if (e < N) {
+      const bool valid = key != kNoKey;
+      if (B.a_out) B.a_out[e] = valid ? __uint_as_float(~(uint32_t)(key >> 32)) : 0.0f;
+      if (B.rank) st_dev(B.rank + e, valid ? (int)(A >> 48) : INT_MAX);
+      if (valid) {
+        const int rho = (int)(A >> 48);
+        const unsigned long long before = ((unsigned long long)R << 32) + (A & (kCountUnit - 1));
+        const unsigned long long through = before + incr_of_bits(~(uint32_t)(key >> 32));
+        if (B.tau) st_dev(B.tau + e, through);
+        if (B.eval == kEvalNone) {
+          p.o = 1ull;
+        } else {
+          const double t1 = theta_of(through, tsps[rho + 1]);
+          if (B.eval == kEvalArgmax) {
+            p.o = B.lagged ? (unsigned long long)(rho + 1) : key;
+            p.th = t1;
+          } else if (!(t1 > theta_of(before, tsps[rho]))) {
+            p.o = key;
+          }
+        }
+      }
+    }
+    e_pub[wave * XW + i] = p;
   }
+  // the ranks and taus that the finishing workgroup reads back (two-step lag) are
+  // acknowledged before this workgroup publishes
+  if (B.rank) stores_done();
   __syncthreads();
-  const int n = red_i[0];
-  __syncthreads();
-  return n;
-}
 
-// step 4 with the break: (first n >= 1 with Theta_n <= Theta_{n-1}) - 1, or nE
-__device__ int sched_first_drop(int R, int nE, const float* __restrict__ sps, int sps_B0,
-                                const SchedShared& sh, int* red_i) {
-  if (threadIdx.x == 0) *red_i = 0x7fffffff;
-  __syncthreads();
-  int first = 0x7fffffff;  // this thread's first drop (n increases within a thread)
-  for (int n = 1 + threadIdx.x; n <= nE; n += kSchedThreads) {
-    const double t1 = theta_of(tau_at(R, sh, n), sps[R + n - sps_B0]);
-    const double t0 = theta_of(tau_at(R, sh, n - 1), sps[R + n - 1 - sps_B0]);
-    if (!(t1 > t0)) {
-      first = n;
-      break;
+  // publish; then load every publication and check whether all are current
+  if (wave == 0) {
+    if (lane == 0) {
+      Pub p = e_pub[0];
+      for (int k = 1; k < XB; ++k) pub_merge(p, e_pub[k], B.eval);
+      const unsigned long long w1 = (unsigned long long)__double_as_longlong(p.th);
+      unsigned long long* w = out.pub + kPubWords * (size_t)blockIdx.x;
+      st_dev(w + 0, p.o);
+      st_dev(w + 1, w1);
+      st_dev(w + 2, pub_check(tag, p.o, w1));
+      stores_done();
+    }
+    Pub cur = pub_none(b0.eval), lag = pub_none(kEvalArgmax);
+    bool ok = true;
+    for (int k = lane; k < nwg; k += kWave) {
+      const unsigned long long* w = out.pub + kPubWords * (size_t)k;
+      Pub p;
+      p.o = ld_dev(w + 0);
+      // the second word is -inf unless the batch publishes a maximum
+      const bool arg = k < b0.nblocks ? b0.eval == kEvalArgmax : true;
+      const unsigned long long w1 = arg ? ld_dev(w + 1) : kNegInfBits;
+      ok &= ld_dev(w + 2) == pub_check(tag, p.o, w1);
+      p.th = __longlong_as_double((long long)w1);
+      if (k < b0.nblocks)
+        pub_merge(cur, p, b0.eval);
+      else
+        pub_merge(lag, p, kEvalArgmax);
+    }
+    const bool all = __ballot(!ok) == 0ull;
+    cur = wave_pub(cur, b0.eval);
+    lag = wave_pub(lag, kEvalArgmax);
+    if (lane == 0) {
+      s_last = all ? 1 : 0;
+      s_cur = cur;
+      s_lag = lag;
     }
   }
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o, kWave));
-  if ((threadIdx.x & (kWave - 1)) == 0 && first != 0x7fffffff) atomicMin(red_i, first);
   __syncthreads();
-  const int f = *red_i;
-  __syncthreads();
-  return f == 0x7fffffff ? nE : f - 1;
-}
+  if (!s_last) return;
 
-__global__ void __launch_bounds__(kSchedThreads) schedule_kernel(
-    int R, int gamma, const float* __restrict__ c, const float* __restrict__ c_lag, int R_lag,
-    const float* __restrict__ sps, int sps_B0, int mode, int npad, int npad_lag, int32_t* ell,
-    float* a_out, double* stats, int32_t* status) {
-  extern __shared__ unsigned long long smem[];
-  __shared__ unsigned long long red_u64[kSchedThreads];
-  __shared__ double red_d[kSchedThreads];
-  __shared__ int red_i[kSchedThreads];
-  __shared__ int red_one;
-  const int np = npad > npad_lag ? npad : npad_lag;
-  SchedShared sh{smem, smem + np};
-
-  int K = -1;  // admitted-count cap from the lagged batch
-  if (mode == DSPARK_SCHED_ASYNC_LAG2) {
-    int np_lag = npad_lag;
-    const int nEl = sched_sort_scan(R_lag, gamma, c_lag, nullptr, &np_lag, sh, red_u64,
-                                    &red_one, status);
-    const int nl = sched_argmax(R_lag, nEl, sps, sps_B0, sh, red_d, red_i);
-    const int cap = R_lag + nl;
-    K = cap - R > 0 ? cap - R : 0;
-    __syncthreads();
-  }
-  int np_cur = npad;
-  const int nE = sched_sort_scan(R, gamma, c, a_out, &np_cur, sh, red_u64, &red_one, status);
+  // ---- the finishing workgroup: the admitted count, ell and the stats ----
+  const int Rc = b0.R;
+  const Pub cur = s_cur;
   int n;
-  if (mode == DSPARK_SCHED_SYNC_BREAK)
-    n = sched_first_drop(R, nE, sps, sps_B0, sh, &red_one);
-  else if (mode == DSPARK_SCHED_GLOBAL)
-    n = sched_argmax(R, nE, sps, sps_B0, sh, red_d, red_i);
-  else
-    n = K < nE ? K : nE;
-
-  const unsigned long long tau = tau_at(R, sh, n);
-  __syncthreads();
-  // count admitted entries per request (reuse the prefix array as int counters)
-  int* cnt = reinterpret_cast<int*>(sh.pre);
-  for (int q = threadIdx.x; q < R; q += kSchedThreads) cnt[q] = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += kSchedThreads)
-    atomicAdd(&cnt[(int)(sh.key[i] & 0xffffffffull) / gamma], 1);
-  __syncthreads();
-  for (int q = threadIdx.x; q < R; q += kSchedThreads) ell[q] = cnt[q];
-  if (threadIdx.x == 0 && stats) {
-    const int B = R + n;
-    stats[0] = (double)B;
-    stats[1] = (double)tau * 0x1p-32;
-    stats[2] = theta_of(tau, sps[B - sps_B0]);
-    stats[3] = (double)n;
+  unsigned long long tau_n;
+  if (out.mode != DSPARK_SCHED_ASYNC_LAG2) {
+    // a current-batch workgroup: its LDS holds every key; the admitted entries are the keys
+    // below thr
+    unsigned long long thr;
+    if (out.mode == DSPARK_SCHED_SYNC_BREAK)
+      thr = cur.o;  // the first key that drops Theta, or kNoKey: all candidates
+    else
+      thr = (cur.o != kNoKey && cur.th > theta_of((unsigned long long)Rc << 32, sps_R))
+                ? cur.o + 1ull  // keys are distinct: the keys up to the best one
+                : 0ull;
+    unsigned long long a = 0ull;
+    for (int s = threadIdx.x; s < npad; s += kRankThreads) {
+      const ulonglong2 y = ent[s];
+      a += y.x < thr ? y.y : 0ull;
+    }
+    a = wave_sum_u64(a);
+    if (lane == 0) s_red[wave] = a;
+    for (int q = threadIdx.x; q < Rc; q += kRankThreads) {
+      int cnt = 0;
+      for (int j = 0; j < gamma; ++j) cnt += ent[j * Rc + q].x < thr ? 1 : 0;
+      out.ell[q] = cnt;
+    }
+    __syncthreads();
+    a = 0ull;
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) a += s_red[w];
+    n = (int)(a >> 48);
+    tau_n = ((unsigned long long)Rc << 32) + (a & (kCountUnit - 1));
+  } else {
+    // the lagged batch's no-break count gives the capacity; the admitted set by rank (this
+    // workgroup's LDS may hold the other batch); the entry of rank n - 1 gives tau
+    const Pub lag = s_lag;
+    const int Rl = b1.R;
+    const int nl =
+        (lag.o != kNoKey && lag.th > theta_of((unsigned long long)Rl << 32, sps_Rl)) ? (int)lag.o : 0;
+    const int K = Rl + nl - Rc;
+    const int nE = (int)cur.o;
+    n = K > 0 ? (K < nE ? K : nE) : 0;
+    tau_n = (unsigned long long)Rc << 32;
+    for (int q = threadIdx.x; q < Rc; q += kRankThreads) {
+      int cnt = 0;
+      for (int j = 0; j < gamma; ++j) {
+        const int rk = ld_dev(b0.rank + q * gamma + j);
+        cnt += rk < n ? 1 : 0;
+        if (out.stats && n > 0 && rk == n - 1) {
+          const unsigned long long t = ld_dev(b0.tau + q * gamma + j);
+          const int Bn = Rc + n;
+          out.stats[0] = (double)Bn;
+          out.stats[1] = (double)t * 0x1p-32;
+          out.stats[2] = theta_of(t, sps[Bn - sps_B0]);
+          out.stats[3] = (double)n;
+        }
+      }
+      out.ell[q] = cnt;
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (out.stats && (out.mode != DSPARK_SCHED_ASYNC_LAG2 || n == 0)) {
+      const int Bn = Rc + n;
+      out.stats[0] = (double)Bn;
+      out.stats[1] = (double)tau_n * 0x1p-32;
+      out.stats[2] = theta_of(tau_n, (SPS_LDS && !second) ? lsps[n] : sps[Bn - sps_B0]);
+      out.stats[3] = (double)n;
+    }
+    st_dev(out.epoch, tag);
   }
 }
 
-static int pow2_at_least(int n) {
-  int p = 2;
-  while (p < n) p <<= 1;
-  return p;
+// entries per wave so that a batch of N entries takes at most kRankMaxBlocks workgroups
+static int rank_xw(int N) { return N <= kRankWaves * kRankMaxBlocks ? 1 : 2; }
+
+struct SchedWs {
+  unsigned long long* epoch;
+  unsigned long long* pub;
+  unsigned long long* tau;
+  int32_t* rank;
+  size_t bytes;
+};
+
+// the epoch and the publications first, at offsets that do not depend on the shape
+static SchedWs carve_sched(void* ws, int R, int gamma) {
+  const size_t N = (size_t)R * gamma;
+  Carve cv(ws);
+  SchedWs w{};
+  w.epoch = cv.take<unsigned long long>(1);
+  w.pub = cv.take<unsigned long long>(kPubWords * 2 * kRankMaxBlocks);
+  w.tau = cv.take<unsigned long long>(N);
+  w.rank = cv.take<int32_t>(N);
+  w.bytes = cv.bytes();
+  return w;
+}
+
+// the table slice goes to LDS beside the keys up to 4096 entries (8192 keys fill 128 KB)
+template <int XW>
+static void launch_schedule(int gamma, const SchedBatch& b0, const SchedBatch& b1,
+                            const float* sps, int sps_B0, int nmax, const SchedOut& out,
+                            int32_t* status, hipStream_t stream) {
+  constexpr bool kSpsLds = XW == 1;
+  const int npad_max = round_up(nmax, kWave * kRankUnroll);
+  const size_t lds =
+      (size_t)npad_max * sizeof(ulonglong2) + (kSpsLds ? (size_t)(nmax + 1) * sizeof(float) : 0);
+  static std::atomic<uint64_t> raised{0};
+  ensure_dynamic_lds(reinterpret_cast<const void*>(schedule_kernel<XW, kSpsLds>),
+                     (int)(round_up(kMaxSchedN, kWave * kRankUnroll) * sizeof(ulonglong2)),
+                     raised);
+  schedule_kernel<XW, kSpsLds><<<b0.nblocks + b1.nblocks, kRankThreads, lds, stream>>>(
+      gamma, b0, b1, sps, sps_B0, npad_max, out, status);
 }
 
 }  // namespace dspark
@@ -394,9 +508,9 @@ static int pow2_at_least(int n) {
 extern "C" {
 
 size_t dspark_schedule_workspace_bytes(int R, int gamma) {
-  (void)R;
-  (void)gamma;
-  return 0;
+  using namespace dspark;
+  if (R < 1 || gamma < 1 || gamma > kMaxGamma || (long)R * gamma > kMaxSchedN) return 0;
+  return carve_sched(nullptr, R, gamma).bytes;
 }
 
 int dspark_schedule(int R, int gamma, const float* c, const float* c_lag, int R_lag,
@@ -404,8 +518,6 @@ int dspark_schedule(int R, int gamma, const float* c, const float* c_lag, int R_
                     int32_t* ell, float* a, double* stats, int32_t* dev_status, void* ws,
                     size_t ws_bytes, hipStream_t stream) {
   using namespace dspark;
-  (void)ws;
-  (void)ws_bytes;
   if (R < 0 || gamma < 1 || gamma > kMaxGamma || sps_len < 1) return DSPARK_EINVAL;
   if (mode != DSPARK_SCHED_SYNC_BREAK && mode != DSPARK_SCHED_GLOBAL &&
       mode != DSPARK_SCHED_ASYNC_LAG2)
@@ -418,16 +530,30 @@ int dspark_schedule(int R, int gamma, const float* c, const float* c_lag, int R_
   if (sps_B0 > R || (long)sps_B0 + sps_len - 1 < (long)R * (1 + gamma)) return DSPARK_ERANGE;
   if (lag && (sps_B0 > R_lag || (long)sps_B0 + sps_len - 1 < (long)R_lag * (1 + gamma)))
     return DSPARK_ERANGE;
-  const int npad = pow2_at_least(R * gamma);
-  const int npad_lag = lag ? pow2_at_least(R_lag * gamma) : 2;
-  const int np = npad > npad_lag ? npad : npad_lag;
-  const size_t sh = (size_t)2 * np * sizeof(unsigned long long);
-  static std::atomic<uint64_t> lds_raised{0};
-  ensure_dynamic_lds(reinterpret_cast<const void*>(schedule_kernel),
-                     (int)(2 * kMaxSchedN * sizeof(unsigned long long)), lds_raised);
-  schedule_kernel<<<1, kSchedThreads, sh, stream>>>(R, gamma, c, lag ? c_lag : nullptr,
-                                                    lag ? R_lag : 0, sps, sps_B0, (int)mode,
-                                                    npad, npad_lag, ell, a, stats, dev_status);
+  const SchedWs w = carve_sched(ws, R, gamma);
+  if (!ws || ws_bytes < w.bytes) return DSPARK_EWORKSPACE;
+
+  const int N = R * gamma, Nl = lag ? R_lag * gamma : 0;
+  const int nmax = N > Nl ? N : Nl;
+  const int xw = rank_xw(nmax);
+  const int xb = xw * kRankWaves;
+  const SchedBatch b0{c,
+                      R,
+                      (N + xb - 1) / xb,
+                      mode == DSPARK_SCHED_SYNC_BREAK
+                          ? kEvalBreak
+                          : (mode == DSPARK_SCHED_GLOBAL ? kEvalArgmax : kEvalNone),
+                      false,
+                      lag ? w.rank : nullptr,
+                      lag ? w.tau : nullptr,
+                      a};
+  const SchedBatch b1{lag ? c_lag : c, lag ? R_lag : R, lag ? (Nl + xb - 1) / xb : 0,
+                      kEvalArgmax, true, nullptr, nullptr, nullptr};
+  const SchedOut out{(int)mode, ell, stats, w.epoch, w.pub};
+  if (xw == 1)
+    launch_schedule<1>(gamma, b0, b1, sps, sps_B0, nmax, out, dev_status, stream);
+  else
+    launch_schedule<2>(gamma, b0, b1, sps, sps_B0, nmax, out, dev_status, stream);
   return launch_status();
 }
 

@@ -211,6 +211,12 @@ int dspark_draft_rnn(int R, int gamma, int V, int r, int d, dspark_dtype dt, con
  *   (and R_lag .. R_lag(1+gamma) in ASYNC_LAG2), else DSPARK_ERANGE.
  * Outputs: ell [R] int32; a [R][gamma] float (nullable);
  *   stats [4] double (nullable) = {B, tau, Theta, n admitted}.
+ * Workspace: ws of at least dspark_schedule_workspace_bytes(R, gamma) device bytes
+ *   (DSPARK_EWORKSPACE otherwise; 0 for shapes beyond R * gamma <= 8192).  It needs no
+ *   preparation (any contents on the first call) and may be captured in a graph: it holds an
+ *   epoch word that each call advances, the workgroups' publications of that call, and in
+ *   ASYNC_LAG2 each entry's admission rank and tau.  Calls sharing one workspace must not
+ *   overlap.
  * ------------------------------------------------------------------------------------ */
 size_t dspark_schedule_workspace_bytes(int R, int gamma);
 

@@ -107,6 +107,12 @@ def test_schedule_rejects_bad_arguments(ds):
     assert call(mode=ds.ASYNC_LAG2, c_lag=FAKE, R_lag=8) == ds.ERANGE  # 8*(1+3) > 16
     assert call(R=1024, gamma=9, sps_B0=1, sps_len=20000) == ds.EINVAL  # R*gamma > 8192
     assert call(gamma=0) == ds.EINVAL
+    assert call() == ds.EWORKSPACE  # no workspace
+    ws = ds.schedule_workspace_bytes(4, 3)
+    assert ws >= 4 * 3 * 12
+    assert ds.schedule_workspace_bytes(1024, 9) == 0  # R*gamma > 8192
+    assert L.dspark_schedule(4, 3, FAKE, None, 0, FAKE, 4, 13, ds.SYNC_BREAK, FAKE, None, None,
+                             None, FAKE, ws - 1, None) == ds.EWORKSPACE
 
 
 def test_verify_rejects_bad_arguments(ds):

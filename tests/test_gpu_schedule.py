@@ -60,3 +60,76 @@ def test_schedule_deterministic(ds, mode):
         g = ds.schedule(T(c), T(sps), B0, mode, c_lag=None if c_lag is None else T(c_lag))
         runs.append({k: N(v).tobytes() for k, v in g.items()})
     assert runs[0] == runs[1] == runs[2], name
+
+
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random", "reused"])
+def test_schedule_any_workspace_contents(ora, ds, fill):
+    """The workspace needs no preparation: whatever it holds (zeros, all bits set, random
+    bytes, or the state a call of another shape left), every mode gives the oracle's result,
+    also on the next call with the same workspace."""
+    import torch
+    sets = _conf_sets()
+    ws = torch.empty(ds.schedule_workspace_bytes(512, 16), dtype=torch.uint8, device="cuda:0")
+    if fill == "zeros":
+        ws.zero_()
+    elif fill == "ones":
+        ws.fill_(255)
+    elif fill == "random":
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=torch.Generator().manual_seed(5)))
+    else:
+        name, c, _, kind = sets[4]  # 512 x 16
+        sps, B0 = _sps(kind, *c.shape)
+        ds.schedule(T(c), T(sps), B0, ds.GLOBAL, ws=ws)
+    for case in (0, 6, 1):
+        name, c, _, kind = sets[case]
+        R, gamma = c.shape
+        sps, B0 = _sps(kind, R, gamma)
+        for mode in MODES:
+            c_lag = None
+            if mode == 2:
+                Rl = R if kind in ("c3", "c4") else max(1, R - 3)
+                c_lag = np.clip(c[:Rl] * 0.97, 0, 1).astype(np.float32)
+            o = ora.schedule(c, sps, B0, mode, c_lag=c_lag)
+            g = ds.schedule(T(c), T(sps), B0, mode, c_lag=None if c_lag is None else T(c_lag),
+                            ws=ws)
+            g = {k: N(v) for k, v in g.items()}
+            assert np.array_equal(g["ell"], o["ell"]), (fill, name, mode)
+            assert np.array_equal(g["stats"].view(np.uint64), o["stats"].view(np.uint64)), (fill, name, mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_schedule_graph_replays(ora, ds, mode):
+    """The call captured once in a HIP graph and replayed with new confidences copied into
+    its input between replays (eager work and synchronisation in between): every replay
+    gives the oracle's result for the confidences it saw."""
+    import torch
+    rng = np.random.default_rng(11 + mode)
+    name, c0, _, kind = _conf_sets()[0]  # 256 x 8, the workload's shape
+    R, gamma = c0.shape
+    sps, B0 = _sps(kind, R, gamma)
+    dev = torch.device("cuda:0")
+    c_buf = T(c0)
+    lag_buf = T(c0) if mode == 2 else None
+    sps_t = T(sps)
+    out = dict(ell=torch.empty(R, dtype=torch.int32, device=dev),
+               a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+               stats=torch.empty(4, dtype=torch.float64, device=dev))
+    ws = torch.empty(ds.schedule_workspace_bytes(R, gamma), dtype=torch.uint8, device=dev)
+    ds.schedule(c_buf, sps_t, B0, mode, c_lag=lag_buf, out=out, ws=ws)  # first call outside
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ds.schedule(c_buf, sps_t, B0, mode, c_lag=lag_buf, out=out, ws=ws)
+    for rep in range(4):
+        c = rng.beta(6, 1.6, (R, gamma)).astype(np.float32)
+        c_buf.copy_(T(c))
+        c_lag = None
+        if mode == 2:
+            c_lag = np.clip(c * rng.uniform(0.9, 1.0), 0, 1).astype(np.float32)
+            lag_buf.copy_(T(c_lag))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o = ora.schedule(c, sps, B0, mode, c_lag=c_lag)
+        assert np.array_equal(N(out["ell"]), o["ell"]), (mode, rep)
+        assert np.array_equal(N(out["stats"]).view(np.uint64), o["stats"].view(np.uint64)), (mode, rep)
