@@ -133,3 +133,32 @@ def test_schedule_graph_replays(ora, ds, mode):
         o = ora.schedule(c, sps, B0, mode, c_lag=c_lag)
         assert np.array_equal(N(out["ell"]), o["ell"]), (mode, rep)
         assert np.array_equal(N(out["stats"]).view(np.uint64), o["stats"].view(np.uint64)), (mode, rep)
+
+
+SHAPES = [(1, 1, None), (1, 64, None), (4096, 1, None), (4097, 1, None), (8192, 1, None),
+          (128, 64, None), (37, 7, 74), (300, 9, 5)]
+
+
+@pytest.mark.parametrize("R,gamma,R_lag", SHAPES)
+def test_schedule_shape_edges(ora, ds, R, gamma, R_lag):
+    """Shapes at the kernel's edges: one entry, one request with 64 positions, the entry
+    counts around the change from one to two entries per wave (4096 / 4097) and the largest
+    (8192, as 8192 x 1 and 128 x 64), and lagged batches larger and smaller than the current
+    one; every mode bit-exact against the oracle."""
+    rng = np.random.default_rng(R * 131 + gamma)
+    c = rng.beta(5, 1.5, (R, gamma)).astype(np.float32)
+    c[rng.random((R, gamma)) < 0.02] = 1.0
+    Rmax = max(R, R_lag or 0)
+    B = np.arange(1, Rmax * (gamma + 1) + 1, dtype=np.float64)
+    sps = (1.0 / (1.0 + 0.002 * B + 0.01 * np.floor(B / 29))).astype(np.float32)
+    modes = MODES if R_lag is not None else (0, 1)
+    for mode in modes:
+        c_lag = None
+        if mode == 2:
+            c_lag = rng.beta(5, 1.5, (R_lag, gamma)).astype(np.float32)
+        o = ora.schedule(c, sps, 1, mode, c_lag=c_lag)
+        g = ds.schedule(T(c), T(sps), 1, mode, c_lag=None if c_lag is None else T(c_lag))
+        g = {k: N(v) for k, v in g.items()}
+        assert np.array_equal(g["ell"], o["ell"]), (R, gamma, mode)
+        assert np.array_equal(g["a"].view(np.uint32), o["a"].view(np.uint32)), (R, gamma, mode)
+        assert np.array_equal(g["stats"].view(np.uint64), o["stats"].view(np.uint64)), (R, gamma, mode)
