@@ -12,7 +12,7 @@ configuration bench.py times:
     those confidences, verification with the float bias rows.
 Each stage is compared with the oracle on identical inputs (the GPU stage's inputs), so a
 near-tie upstream does not cascade; the oracle runs the whole workload on the host (seconds
-to a minute on the machine's cores)."""
+to a minute on the host's cores)."""
 import numpy as np
 import pytest
 
