@@ -231,10 +231,58 @@ __global__ void __launch_bounds__(kRankThreads) schedule_kernel(
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int nwg = b0.nblocks + b1.nblocks;
 
-  // every load below is issued before the first one is used: one round trip to memory
+  // The confidences of this thread's first request go out first and the keys are built from
+  // them; the SPS slice and the epoch are issued after the keys (loads retire in order, so
+  // the keys never wait for them) and stay in flight through the pair sweep, which reads LDS
+  // only; the slice is stored to LDS just before the evaluation.
+  const int q0 = threadIdx.x;
+  float cv0[8];
+  {
+    const float* cq = B.c + (size_t)(q0 < R ? q0 : 0) * gamma;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cv0[u] = cq[u < gamma ? u : gamma - 1];
+  }
   float* lsps = reinterpret_cast<float*>(ent + npad_max);
   const float* tsps = SPS_LDS ? lsps : sps + (R - sps_B0);  // SPS(R + n) for n = 0..N
   constexpr int kSpsPer = SPS_LDS ? (4096 + kRankThreads) / kRankThreads : 1;  // N <= 4096
+
+  // keys of every entry of the batch: chunk j0 .. j0 + 7 of request q, the running product
+  // carried in run
+  auto chunk = [&](int q, int j0, const float (&cv)[8], float& run) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      if (j >= gamma) break;
+      float cj = cv[u];
+      if (!(cj >= 0.0f && cj <= 1.0f)) {
+        if (blk == 0) raise_fault(status, DSPARK_FAULT_CONF);
+        cj = (cj > 1.0f) ? 1.0f : 0.0f;  // NaN and negatives -> 0
+      }
+      run = (j == 0) ? cj : __fmul_rn(run, cj);
+      const uint32_t bits = __float_as_uint(run);
+      ent[j * R + q] = run > 0.0f
+                           ? make_ulonglong2(((unsigned long long)(~bits) << 32) |
+                                                 (unsigned)(q * gamma + j),
+                                             incr_of_bits(bits) + kCountUnit)
+                           : make_ulonglong2(kNoKey, 0ull);
+    }
+  };
+  // the first chunk of the first request straight from the registers loaded first (no loop
+  // around it, so its wait leaves the later loads in flight)
+  float run0 = 1.0f;
+  if (q0 < R) chunk(q0, 0, cv0, run0);
+  for (int q = q0; q < R; q += kRankThreads) {
+    const float* cq = B.c + (size_t)q * gamma;
+    float run = run0;
+    for (int j0 = q == q0 ? 8 : 0; j0 < gamma; j0 += 8) {
+      float cv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cv[u] = cq[j0 + u < gamma ? j0 + u : gamma - 1];
+      chunk(q, j0, cv, run);
+    }
+  }
+  for (int s = N + threadIdx.x; s < npad; s += kRankThreads) ent[s] = make_ulonglong2(kNoKey, 0ull);
+  __builtin_amdgcn_sched_barrier(0);  // the loads below stay after the keys
   float sv[kSpsPer];
   if (SPS_LDS) {
 #pragma unroll
@@ -245,44 +293,7 @@ __global__ void __launch_bounds__(kRankThreads) schedule_kernel(
   }
   const float sps_R = sps[b0.R - sps_B0];  // SPS(R) of the current batch
   const float sps_Rl = b1.nblocks > 0 ? sps[b1.R - sps_B0] : 0.0f;
-
-  // keys of every entry of the batch
-  for (int q = threadIdx.x; q < R; q += kRankThreads) {
-    const float* cq = B.c + (size_t)q * gamma;
-    float run = 1.0f;
-    for (int j0 = 0; j0 < gamma; j0 += 8) {
-      float cv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) cv[u] = cq[j0 + u < gamma ? j0 + u : gamma - 1];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u;
-        if (j >= gamma) break;
-        float cj = cv[u];
-        if (!(cj >= 0.0f && cj <= 1.0f)) {
-          if (blk == 0) raise_fault(status, DSPARK_FAULT_CONF);
-          cj = (cj > 1.0f) ? 1.0f : 0.0f;  // NaN and negatives -> 0
-        }
-        run = (j == 0) ? cj : __fmul_rn(run, cj);
-        const uint32_t bits = __float_as_uint(run);
-        ent[j * R + q] = run > 0.0f
-                             ? make_ulonglong2(((unsigned long long)(~bits) << 32) |
-                                                   (unsigned)(q * gamma + j),
-                                               incr_of_bits(bits) + kCountUnit)
-                             : make_ulonglong2(kNoKey, 0ull);
-      }
-    }
-  }
-  for (int s = N + threadIdx.x; s < npad; s += kRankThreads) ent[s] = make_ulonglong2(kNoKey, 0ull);
-  if (SPS_LDS) {
-#pragma unroll
-    for (int u = 0; u < kSpsPer; ++u) {
-      const int n = (int)threadIdx.x + u * kRankThreads;
-      if (n <= N) lsps[n] = sv[u];
-    }
-  }
-  // the epoch is needed only to publish: loaded after the inputs, so their waits skip it
-  const unsigned long long tag = ld_dev(out.epoch) + 1ull;
+  const unsigned long long tag = ld_dev(out.epoch) + 1ull;  // needed only to publish
   __syncthreads();
 
   // this wave's entries (uniform across the wave: broadcast reads)
@@ -307,6 +318,14 @@ __global__ void __launch_bounds__(kRankThreads) schedule_kernel(
   }
 #pragma unroll
   for (int i = 0; i < XW; ++i) acc[i] = wave_sum_u64(acc[i]);
+  if (SPS_LDS) {
+#pragma unroll
+    for (int u = 0; u < kSpsPer; ++u) {
+      const int n = (int)threadIdx.x + u * kRankThreads;
+      if (n <= N) lsps[n] = sv[u];
+    }
+    __syncthreads();
+  }
 
   // lane i < XW evaluates entry e0 + i
   if (lane < XW) {
