@@ -174,6 +174,31 @@ def cpu_baseline(cfg, I, target_seconds):
                 cpu_model=cpu_model(), nproc=len(os.sched_getaffinity(0)))
 
 
+def read_probe_rate(torch, ds, dev, nbytes: int):
+    """(GB/s, grid, bytes) of dspark_read_probe: the best median over grid sizes of reads of
+    nbytes from four rotated buffers (4 x nbytes above the 256 MB last-level cache, so every
+    read finds its bytes in HBM only)."""
+    import numpy as np
+
+    n16 = (nbytes + 15) // 16 * 16
+    bufs = [torch.zeros(n16 // 4, dtype=torch.int32, device=dev) for _ in range(4)]
+    hip, ev = hip_events(2)  # attached to the probe's dispatch, as for the sweep
+    best, k = (0.0, 0, n16), 0
+    for grid in (1024, 2048, 4096):
+        sink = torch.empty(grid, dtype=torch.int32, device=dev)
+        rates = []
+        for _ in range(7):
+            ds.read_probe(bufs[k % 4], grid, sink=sink, events=(ev[0], ev[1]))
+            torch.cuda.synchronize()
+            k += 1
+            rates.append(n16 / (elapsed_ms(hip, ev[0], ev[1]) * 1e-3) / 1e9)
+        med = float(np.median(rates))
+        if med > best[0]:
+            best = (med, grid, n16)
+    del bufs
+    return best
+
+
 def sweep_bytes_of(R: int, V: int, r: int) -> int:
     """Algorithmic bytes of one draft sweep: U_k rows, all of W2, the gathered W1 rows."""
     return R * V * 2 + V * r * 2 + R * r * 2
@@ -415,6 +440,11 @@ def bench_cycle(args):
         torch.cuda.synchronize()
         copy_gbs = 2 * cbuf.numel() * 2 * 10 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
         del cbuf, cdst
+    # the rate of a kernel that only reads (dspark_read_probe) on the sweep's byte count:
+    # the practical ceiling for a read-bound kernel beside the published peak
+    read_probe = None
+    if not args.copy_probe:
+        read_probe = read_probe_rate(torch, ds, dev, sweep_bytes_of(R, V, r))
     if args.copy_probe:
         # a plain device copy of known size, for scaling the HBM byte counters
         a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
@@ -488,6 +518,14 @@ def bench_cycle(args):
         "stage_ms": {"draft": t_draft, "schedule": t_sched, "verify": t_ver},
         "cycle_ms_median": cycle_median,
         "hbm_copy_gbs": copy_gbs,
+        "hbm_read_probe": None if read_probe is None else {
+            "gbs": read_probe[0], "grid": read_probe[1], "bytes": read_probe[2],
+            "frac_of_peak": read_probe[0] / HBM_PEAK_GBS,
+            "sweep_frac_of_probe": achieved / read_probe[0],
+            "what": "dspark_read_probe (a kernel that only reads, each workgroup streaming its "
+                    "own slice) on the sweep's byte count, bytes no cache holds, timed by its "
+                    "dispatch as the sweep is; best median of 7 reads over grids of 1024, 2048 "
+                    "and 4096 workgroups"},
         "draft_hbm_frac_w2_once": draft_bytes_w2_once / (t_draft * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "cycle_hbm_frac": cycle_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "mean_verified_rows": n_b, "mean_ell": float(ell_all.mean()),

@@ -31,7 +31,7 @@ EXPORTS = ("dspark_draft_workspace_bytes", "dspark_draft_markov", "dspark_draft_
            "dspark_train_forward_workspace_bytes", "dspark_train_forward",
            "dspark_decode_workspace_bytes", "dspark_decode_run",
            "dspark_sps_profile", "dspark_sps_interpolate", "dspark_w2_relayout",
-           "dspark_version")
+           "dspark_read_probe", "dspark_version")
 
 _lib = None
 
@@ -107,6 +107,8 @@ def lib():
         L.dspark_sps_interpolate.restype = i
         L.dspark_w2_relayout.argtypes = [i, i, i, vp, vp, vp]
         L.dspark_w2_relayout.restype = i
+        L.dspark_read_probe.argtypes = [vp, sz, i, vp, vp, vp, vp]
+        L.dspark_read_probe.restype = i
         L.dspark_version.restype = C.c_char_p
         _lib = L
     return _lib
@@ -185,6 +187,23 @@ def w2_relayout(W2, *, out=None):
     _chk(out, "W2t", (V, r), W2.dtype)
     _raise("dspark_w2_relayout", lib().dspark_w2_relayout(V, r, dt, _p(W2), _p(out), _stream()))
     return out
+
+
+def read_probe(buf, grid=2048, *, sink=None, events=None):
+    """Benchmark hook: a plain streaming read of the device tensor `buf` (its bytes, a
+    multiple of 16) by `grid` workgroups; returns the [grid] int32 sink, whose XOR is the
+    XOR of buf's 32-bit words (dspark_read_probe).  events=(begin, end): raw hipEvent_t
+    handles the dispatch timestamps."""
+    torch = _torch()
+    _chk(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(grid, dtype=torch.int32, device=buf.device)
+    _chk(sink, "sink", (grid,), torch.int32)
+    ev0, ev1 = events if events is not None else (None, None)
+    _raise("dspark_read_probe",
+           lib().dspark_read_probe(_p(buf), nbytes, grid, _p(sink), _stream(), ev0, ev1))
+    return sink
 
 
 def draft_workspace_bytes(R, gamma, V, r, d) -> int:

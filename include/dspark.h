@@ -89,6 +89,21 @@ int dspark_w2_relayout(int V, int r, dspark_dtype dt, const void *W2, void *W2t,
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * Benchmark hook (a measurement, not part of the method): reads `bytes` bytes at `buf`
+ * (device memory, 16-byte aligned, bytes % 16 == 0) with `grid` workgroups of 256 threads,
+ * each streaming its own contiguous slice, asynchronously on `stream`, and writes to
+ * sink[b] (device, grid uint32 values) the XOR of the 32-bit words workgroup b read (so the
+ * XOR of all of sink is the XOR of the whole buffer).  ev_begin / ev_end (both or neither;
+ * events the caller created) are attached to the dispatch, which timestamps its own start
+ * and end: their elapsed time is the kernel's duration, the read rate this device sustains,
+ * the practical ceiling beside the published HBM peak.
+ * DSPARK_EINVAL for a NULL pointer, a misaligned buffer or size, grid outside 1..65536, or
+ * only one of the two events.
+ * ------------------------------------------------------------------------------------ */
+int dspark_read_probe(const void *buf, size_t bytes, int grid, uint32_t *sink,
+                      hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
+
+/* ------------------------------------------------------------------------------------
  * Draft (digest, Module B eq. (4) with the Markov head of eq. (5) or the RNN head of
  * eq. (6); confidence head eq. (7)).
  *

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(ds):
     names = _declared()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(ds.lib(), n), n
     assert set(names) == set(ds.EXPORTS)
@@ -91,6 +91,20 @@ def test_w2_relayout_rejects_bad_arguments(ds):
     assert L.dspark_w2_relayout(1024, 16, 5, FAKE, other, None) == ds.EINVAL
     assert L.dspark_w2_relayout(1024, 16, ds.F32, None, other, None) == ds.EINVAL
     assert L.dspark_w2_relayout(1024, 16, ds.F32, FAKE, FAKE, None) == ds.EINVAL  # aliased
+
+
+def test_read_probe_arguments(ds):
+    """The read probe's argument checks return before anything reaches the device."""
+    L = ds.lib()
+    sink = C.c_void_p(0x2000)
+    ev = C.c_void_p(0x3000)
+    assert L.dspark_read_probe(None, 1024, 4, sink, None, None, None) == ds.EINVAL
+    assert L.dspark_read_probe(FAKE, 1024, 4, None, None, None, None) == ds.EINVAL
+    assert L.dspark_read_probe(FAKE, 1000, 4, sink, None, None, None) == ds.EINVAL  # 16-byte whole
+    assert L.dspark_read_probe(C.c_void_p(0x1008), 1024, 4, sink, None, None, None) == ds.EINVAL
+    assert L.dspark_read_probe(FAKE, 1024, 0, sink, None, None, None) == ds.EINVAL
+    assert L.dspark_read_probe(FAKE, 1024, 65537, sink, None, None, None) == ds.EINVAL
+    assert L.dspark_read_probe(FAKE, 1024, 4, sink, None, ev, None) == ds.EINVAL    # one event
 
 
 def test_schedule_rejects_bad_arguments(ds):
