@@ -16,7 +16,7 @@ def ds():
     return ds
 
 
-def _inputs(ora, cfg, cycle, ell_kind, rnn=False):
+def _inputs(ora, cfg, cycle, ell_kind, rnn=False, edit_target=None):
     I = synth.inputs(cfg)
     if rnn:
         d = ora.draft_rnn(I["U"], I["h"], I["W1"], I["W2"], I["W_gco"], I["w"], I["x0"], 0, cycle)
@@ -28,6 +28,8 @@ def _inputs(ora, cfg, cycle, ell_kind, rnn=False):
     logits = U + np.einsum("qkr,rv->qkv", d["bias_rows"], W2)
     noise, fresh = synth.target_parts(cfg, range(cfg.R), cycle)
     tgt = np.concatenate([logits, fresh[:, None, :]], axis=1) + noise
+    if edit_target is not None:
+        edit_target(tgt)
     target = synth.encode(cfg, tgt.astype(np.float32))
     rng = np.random.default_rng(cycle)
     if ell_kind == "sched":
@@ -82,6 +84,40 @@ def test_verify_rnn_float_bias_rows(ora, ds):
                   seed=0, cycle=cycle)
     g = {k: N(v) for k, v in g.items()}
     excused = compare_verify(o, g, ell, "rnn")
+
+
+def _spikes(tgt):
+    """Single logits far above the rest of their row, placed where the target normaliser's
+    first estimate of a window's largest logit (each lane's first chunk: the window's first
+    512 ids) cannot see them: 100 above the row (its sums would leave the float range, so
+    that window is redone against its exact maximum), 60 above (kept: large but finite
+    sums), in the last, partial window, and on bonus rows."""
+    R, G1, V = tgt.shape
+    top = float(tgt.max())
+    for q in range(R):
+        for j in range(G1):
+            if q % 3 == 0:
+                tgt[q, j, 1000 + 37 * j] = top + 100.0
+            elif q % 3 == 1:
+                tgt[q, j, V - 5] = top + 60.0
+            elif j == G1 - 1:
+                tgt[q, j, 4096 + 600 + q] = top + 100.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_verify_logit_spikes(ora, ds, dtype):
+    base = dict(R=12, gamma=4, V=6000, d=128)
+    cfg = synth.scaled(synth.CONFIGS["c2" if dtype == "bf16" else "c1"], **base)
+    cycle = 6
+    I, d, target, ell = _inputs(ora, cfg, cycle, "random", edit_target=_spikes)
+    o = ora.verify(target, I["U"], I["W2"], d["bias_rows"], d["x"], ell, seed=0, cycle=cycle)
+    brows = synth.encode(cfg, d["bias_rows"].astype(np.float32))
+    W2t = W2T(I["W2"])
+    g = ds.verify(T(target), T(I["U"]), T(W2t), T(brows), T(d["x"]),
+                  T(d["lse"].astype(np.float32)), T(d["logit_x"].astype(np.float32)), T(ell),
+                  seed=0, cycle=cycle)
+    g = {k: N(v) for k, v in g.items()}
+    compare_verify(o, g, ell, f"spikes-{dtype}")
 
 
 def test_length_fault_bit(ora, ds):
