@@ -83,7 +83,7 @@ def lib():
         L.dspark_verify_workspace_bytes.argtypes = [i] * 4
         L.dspark_verify_workspace_bytes.restype = sz
         L.dspark_verify.argtypes = ([i] * 5 + [vp] * 4 + [i] + [vp] * 4 + [u64, u64] +
-                                    [vp] * 4 + [vp, sz, vp])
+                                    [vp] * 5 + [vp, sz, vp])
         L.dspark_verify.restype = i
         L.dspark_sts_workspace_bytes.argtypes = [i] * 3
         L.dspark_sts_workspace_bytes.restype = sz
@@ -363,7 +363,9 @@ def verify_workspace_bytes(R, gamma, V, r) -> int:
 
 def verify(target, U, W2t, bias_rows, x, lse, logit_x, ell, seed=0, cycle=0, *, out=None,
            ws=None, status=None):
-    """Verification; returns dict(n_acc, y, c_star) (device tensors)."""
+    """Verification; returns dict(n_acc, y, c_star, x_next) (device tensors).  x_next [R]
+    holds y[q][n_acc[q]], the next cycle's anchors; a caller's `out` may map it to the tensor
+    the next draft call takes as x0 (or leave it out: then it is not written)."""
     torch = _torch()
     _chk(U, "U")
     R, gamma, V = U.shape
@@ -381,14 +383,19 @@ def verify(target, U, W2t, bias_rows, x, lse, logit_x, ell, seed=0, cycle=0, *, 
     if out is None:
         out = dict(n_acc=torch.empty(R, dtype=torch.int32, device=dev),
                    y=torch.empty((R, gamma + 1), dtype=torch.int32, device=dev),
-                   c_star=torch.empty((R, gamma), dtype=torch.float32, device=dev))
+                   c_star=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+                   x_next=torch.empty(R, dtype=torch.int32, device=dev))
+    x_next = out.get("x_next")
+    if x_next is not None:
+        _chk(x_next, "x_next", (R,), torch.int32)
     nbytes = verify_workspace_bytes(R, gamma, V, r)
     if nbytes == 0 and R > 0:
         raise DsparkError("dspark_verify_workspace_bytes", EINVAL)
     ws = _ws(nbytes, dev, ws)
     rc = lib().dspark_verify(R, gamma, V, r, dt, _p(target), _p(U), _p(W2t), _p(bias_rows),
                              bdt, _p(x), _p(lse), _p(logit_x), _p(ell), seed, cycle,
-                             _p(out["n_acc"]), _p(out["y"]), _p(out["c_star"]), _p(status),
+                             _p(out["n_acc"]), _p(out["y"]), _p(out["c_star"]), _p(x_next),
+                             _p(status),
                              _p(ws), ws.numel() * ws.element_size(), _stream())
     _raise("dspark_verify", rc)
     return out

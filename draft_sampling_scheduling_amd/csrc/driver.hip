@@ -265,7 +265,7 @@ int dspark_decode_run(int R, int gamma, int V, int r, int d, dspark_dtype dt, in
         static_cast<uint4*>(wl.tg), dev_status);
     rc = dspark_verify(R, gamma, V, r, dt, wl.tg, wl.U, W2t, wl.brows, dt, wl.x, wl.lse,
                        wl.logit_x, wl.ell, seed, (uint64_t)cyc, wl.n_acc, wl.y, wl.c_star,
-                       dev_status, wl.vws, wl.vws_bytes, stream);
+                       nullptr, dev_status, wl.vws, wl.vws_bytes, stream);
     if (rc != DSPARK_OK) break;
     decode_account_kernel<<<1, kAccountThreads, 0, stream>>>(
         R, gamma, maxlen, wl.ell, wl.n_acc, wl.y, wl.anchor, tokens, n_emitted,

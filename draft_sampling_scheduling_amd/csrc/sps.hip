@@ -69,13 +69,13 @@ int dspark_sps_profile(int R, int gamma, int V, int r, dspark_dtype dt, const vo
     sps_lengths_kernel<<<(R + 255) / 256, 256, 0, stream>>>(R, gamma, B_list[i] - R, ell);
     // one untimed pass (first-touch and launch set-up), then the timed ones
     rc = dspark_verify(R, gamma, V, r, dt, target, U, W2t, bias_rows, bias_dt, x, lse, logit_x,
-                       ell, 0, 0, n_acc, y, c_star, dev_status, ws, ws_bytes, stream);
+                       ell, 0, 0, n_acc, y, c_star, nullptr, dev_status, ws, ws_bytes, stream);
     if (rc != DSPARK_OK) break;
     if (hipEventRecord(e0, stream) != hipSuccess) rc = DSPARK_EDEVICE;
     for (int k = 0; k < reps && rc == DSPARK_OK; ++k)
       rc = dspark_verify(R, gamma, V, r, dt, target, U, W2t, bias_rows, bias_dt, x, lse,
-                         logit_x, ell, 0, (uint64_t)(k + 1), n_acc, y, c_star, dev_status, ws,
-                         ws_bytes, stream);
+                         logit_x, ell, 0, (uint64_t)(k + 1), n_acc, y, c_star, nullptr,
+                         dev_status, ws, ws_bytes, stream);
     if (rc != DSPARK_OK) break;
     float ms = 0.0f;
     if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||

@@ -608,7 +608,7 @@ __global__ void __launch_bounds__(kFinalThreads) verify_final_kernel(
     int R, int gamma, int V, int r, const T* __restrict__ target, const T* __restrict__ U,
     const T* __restrict__ W2t, const BT* __restrict__ brows, const float* __restrict__ lse,
     const int32_t* ell, VerifyWs ws, int nranges, uint64_t seed, uint64_t cycle,
-    const int32_t* n_acc, int32_t* y, float* c_star) {
+    const int32_t* n_acc, int32_t* y, float* c_star, int32_t* x_next) {
   constexpr int kWaves = kFinalThreads / kWave;
   constexpr int kJ = 8;  // verified rows whose range sums are in flight together
   __shared__ float tvs[kWaves][kJ];
@@ -764,7 +764,10 @@ __global__ void __launch_bounds__(kFinalThreads) verify_final_kernel(
     wave_argmax(score, idx);
     token = idx;
   }
-  if (lane == 0) y[(size_t)q * (gamma + 1) + n_acc[q]] = token;
+  if (lane == 0) {
+    y[(size_t)q * (gamma + 1) + n_acc[q]] = token;
+    if (x_next) x_next[q] = token;  // the next cycle's anchor
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -774,8 +777,8 @@ template <class T, class BT>
 static int verify_run(int R, int gamma, int V, int r, const void* target_, const void* U_,
                       const void* W2t_, const void* brows_, const int32_t* x, const float* lse,
                       const float* logit_x, const int32_t* ell, uint64_t seed, uint64_t cycle,
-                      int32_t* n_acc, int32_t* y, float* c_star, int32_t* status,
-                      const VerifyWs& ws, hipStream_t stream) {
+                      int32_t* n_acc, int32_t* y, float* c_star, int32_t* x_next,
+                      int32_t* status, const VerifyWs& ws, hipStream_t stream) {
   const T* target = static_cast<const T*>(target_);
   const T* U = static_cast<const T*>(U_);
   const T* W2t = static_cast<const T*>(W2t_);
@@ -828,7 +831,8 @@ static int verify_run(int R, int gamma, int V, int r, const void* target_, const
         seed, cycle, nranges, nblocks);
   }
   verify_final_kernel<T, BT><<<R, kFinalThreads, 0, stream>>>(R, gamma, V, r, target, U, W2t, brows, lse,
-                                                    ell, ws, nranges, seed, cycle, n_acc, y, c_star);
+                                                    ell, ws, nranges, seed, cycle, n_acc, y, c_star,
+                                                    x_next);
   return launch_status();
 }
 
@@ -845,7 +849,8 @@ int dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, const void* t
                   const void* U, const void* W2t, const void* bias_rows, dspark_dtype bias_dt,
                   const int32_t* x, const float* lse, const float* logit_x, const int32_t* ell,
                   uint64_t seed, uint64_t cycle, int32_t* n_acc, int32_t* y, float* c_star,
-                  int32_t* dev_status, void* ws, size_t ws_bytes, hipStream_t stream) {
+                  int32_t* x_next, int32_t* dev_status, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
   using namespace dspark;
   if (!dims_ok(R, gamma, V, r, 0) || (dt != DSPARK_F32 && dt != DSPARK_BF16)) return DSPARK_EINVAL;
   if (bias_dt != DSPARK_F32 && bias_dt != dt) return DSPARK_EINVAL;
@@ -867,13 +872,14 @@ int dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, const void* t
     if (bias_dt == DSPARK_BF16)
       return verify_run<uint16_t, uint16_t>(R, gamma, V, r, target, U, W2t, bias_rows, x, lse,
                                             logit_x, ell, seed, cycle, n_acc, y, c_star,
-                                            dev_status, lay, stream);
+                                            x_next, dev_status, lay, stream);
     return verify_run<uint16_t, float>(R, gamma, V, r, target, U, W2t, bias_rows, x, lse,
-                                       logit_x, ell, seed, cycle, n_acc, y, c_star, dev_status,
-                                       lay, stream);
+                                       logit_x, ell, seed, cycle, n_acc, y, c_star, x_next,
+                                       dev_status, lay, stream);
   }
   return verify_run<float, float>(R, gamma, V, r, target, U, W2t, bias_rows, x, lse, logit_x,
-                                  ell, seed, cycle, n_acc, y, c_star, dev_status, lay, stream);
+                                  ell, seed, cycle, n_acc, y, c_star, x_next, dev_status, lay,
+                                  stream);
 }
 
 const char* dspark_version(void) { return "dspark-mi355x 0.1 (gfx950)"; }

@@ -257,7 +257,9 @@ int dspark_schedule(int R, int gamma, const float *c, const float *c_lag, int R_
  *   x, lse, logit_x [R][gamma]              draft outputs
  *   ell [R] int32                           schedule output (or any lengths in [0,gamma])
  * Outputs: n_acc [R] int32; y [R][gamma+1] int32 (first n_acc+1 valid, rest -1);
- *   c_star [R][gamma] float.
+ *   c_star [R][gamma] float; x_next [R] int32 (nullable) = y[q][n_acc[q]], the last token
+ *   emitted for q, from which q's next cycle drafts (its anchor x0; written by the kernel
+ *   that draws it, so a cycle can pass it to the next draft call with no copy).
  * ------------------------------------------------------------------------------------ */
 size_t dspark_verify_workspace_bytes(int R, int gamma, int V, int r);
 
@@ -265,8 +267,8 @@ int dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, const void *t
                   const void *U, const void *W2t, const void *bias_rows,
                   dspark_dtype bias_dt, const int32_t *x, const float *lse,
                   const float *logit_x, const int32_t *ell, uint64_t seed, uint64_t cycle,
-                  int32_t *n_acc, int32_t *y, float *c_star, int32_t *dev_status, void *ws,
-                  size_t ws_bytes, hipStream_t stream);
+                  int32_t *n_acc, int32_t *y, float *c_star, int32_t *x_next,
+                  int32_t *dev_status, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Training objective, forward (digest, Module F, eqs. (8)-(12)), Markov head, on

@@ -93,6 +93,8 @@ def compare_verify(o, g, ell, label):
     sum(ell) + R decisions.  Returns the number excused."""
     excused = 0
     R = len(ell)
+    if "x_next" in g:  # the next cycle's anchors: the last emitted token of every request
+        assert np.array_equal(g["x_next"], g["y"][np.arange(R), g["n_acc"]]), label
     for q in range(R):
         L = ell[q]
         np.testing.assert_allclose(g["c_star"][q, :L], o["c_star"][q, :L], atol=TOL_P, err_msg=label)

@@ -135,7 +135,7 @@ def test_verify_rejects_bad_arguments(ds):
 
     def call(dt=ds.BF16, bdt=ds.BF16, ws_bytes=ws, V=1024):
         return L.dspark_verify(4, 4, V, 16, dt, FAKE, FAKE, FAKE, FAKE, bdt, FAKE, FAKE, FAKE,
-                               FAKE, 0, 0, FAKE, FAKE, FAKE, None, FAKE, ws_bytes, None)
+                               FAKE, 0, 0, FAKE, FAKE, FAKE, None, None, FAKE, ws_bytes, None)
 
     assert call(dt=ds.F32, bdt=ds.BF16) == ds.EINVAL  # bias rows must be float or dt
     assert call(ws_bytes=ws - 1) == ds.EWORKSPACE
