@@ -748,9 +748,9 @@ static DraftWs carve_draft(void* ws, int R, int gamma, int V, int r, int d, bool
   return w;
 }
 
-// Launches the single-launch draft when its grid can be resident at once and every
-// workgroup has at most kMaxCombinesPerWg requests to combine; returns false (nothing
-// enqueued) otherwise.  ev0/ev1 (nullable) are recorded around the kernel.
+// Enqueues the whole draft call on `stream`: the confidence pre-projection (and the RNN
+// head's set-up), then per position [state update], sweep, combine.  evb/eve (nullable
+// arrays of gamma events) time each position's sweep; returns the launch status.
 template <class T>
 static int draft_run(bool rnn, bool bias, int R, int gamma, int V, int r, int d, const void* U_,
                      const void* h_, const void* W1_, const void* W2t_, const void* Wg_,
