@@ -20,6 +20,13 @@
 //     tile ahead of its use (while the CU's other workgroup computes) and the matrix-core and
 //     epilogue work of the current tile hides the memory latency.  The waits on those
 //     loads are explicit vmcnt waits.
+//   - Without the bias contraction (one streamed operand, no W2t tiles: the parallel block's
+//     own sampling) U is staged a whole 64-id block at a time, one block ahead, in two block
+//     buffers: 128 bytes of each row per copy.  Rows lie a position's stride apart in HBM, and
+//     64-byte pieces of them (one tile's share) come at about 3.9 TB/s where 128-byte pieces
+//     come at the 5.7 TB/s of a plain read.  With W2t tiles beside them the block buffers made
+//     the draft sweep slower (32.7 against 31.2-31.9 us), so the sweeps with a bias keep the
+//     tile's 64-byte slices.
 //   - MFMA 32x32x16 bf16 with A = W2t tile (vocabulary on M) and B = B^T (rows on N):
 //     accumulator lane (n, h) holds row n; its 16 registers are permuted (see
 //     tile_row_of_vocab) to two runs of 8 consecutive ids, which the epilogue matches with
@@ -67,13 +74,26 @@ __host__ __device__ constexpr int stream_tile_chunks() { return kSweepWaves * 32
 __host__ __device__ constexpr int stage_chunks(int CH, int nstreams) {
   return w2_tile_chunks(CH) + nstreams * stream_tile_chunks();
 }
-inline size_t sweep_lds_bytes(int r, int nstreams, int nstage) {
-  return (size_t)16 * nstage * stage_chunks(r / 8, nstreams);
+// a sweep without the bias and with one stream stages U per block: its stages hold nothing
+// (no W2t tiles), and two U block buffers of 128 rows x 8 chunks follow them
+constexpr int kUBlkChunks = kSweepWaves * 32 * 8;
+__host__ __device__ constexpr bool sweep_ublk(int nstreams, bool bias) {
+  return nstreams == 1 && !bias;
+}
+__host__ __device__ constexpr int sweep_stage_chunks(int CH, int nstreams, bool bias) {
+  return sweep_ublk(nstreams, bias) ? 0 : stage_chunks(CH, nstreams);
+}
+inline size_t sweep_lds_bytes(int r, int nstreams, int nstage, bool bias) {
+  return (size_t)16 * (nstage * sweep_stage_chunks(r / 8, nstreams, bias) +
+                       (sweep_ublk(nstreams, bias) ? 2 * kUBlkChunks : 0));
 }
 
 // 16-byte chunk c (0..3) of row n in a wave's 32 x 32 stream slice; the xor spreads the 16
 // rows of one read phase over the banks
 __device__ __forceinline__ int stream_pos(int n, int c) { return n * 4 + (c ^ ((n >> 2) & 3)); }
+// chunk c (0..7) of row n in a wave's slice of a U block buffer; the xor puts the 16 rows of
+// one read phase on distinct banks
+__device__ __forceinline__ int ublk_pos(int n, int c) { return n * 8 + (c ^ ((n >> 1) & 7)); }
 
 // Accumulator row m = 16c + 8a + 4h + t of a 32x32 tile holds vocabulary offset
 // 16c + 8h + 4a + t (bits 2 and 3 swapped; the map is its own inverse), so register
@@ -224,9 +244,12 @@ struct SweepTask {
   static constexpr int NI = w2_copies(CH);          // W2t copies per tile
   static constexpr int W2_MAX = (NI + kSweepWaves - 1) / kSweepWaves;
   static constexpr int NS = Epi::kStreams;
-  static constexpr int SCH = stage_chunks(CH, NS);
-  static constexpr int D = NSTAGE - 1;              // prefetch distance in tiles
   static constexpr bool BIAS = epi_has_bias<Epi>::value;
+  static constexpr bool UBLK = sweep_ublk(NS, BIAS);  // U staged per 64-id block
+  static constexpr int SCH = sweep_stage_chunks(CH, NS, BIAS);
+  static constexpr int UB0 = NSTAGE * SCH;          // first U block buffer (chunks)
+  static constexpr int OPS_U = 4;                   // copies of one U block per wave
+  static constexpr int D = NSTAGE - 1;              // prefetch distance in tiles
   // copies one tile puts in flight for a wave (W2t copies: W2_MAX or W2_MAX - 1)
   static constexpr int OPS_BIG = (BIAS ? W2_MAX : 0) + 2 * NS;
   static constexpr int OPS_SMALL = (BIAS ? W2_MAX - 1 : 0) + 2 * NS;
@@ -239,6 +262,8 @@ struct SweepTask {
   uint32_t w2off[W2_MAX];
   uint32_t soff[NS][2];
   int sx[2];
+  uint32_t uoff[OPS_U];  // U block copies: row 8i + lane / 8 of the wave, a 16-byte piece
+  int u_idx, u_sw;       // this lane's row in a U block buffer, and its xor
   const uint16_t* sb[NS];
   uint32_t lds0;
   int a_idx, s_idx0, s_idx1;
@@ -258,12 +283,33 @@ struct SweepTask {
       const int I = wave + kSweepWaves * i;
       if (BIAS && I < NI) dma16s(w2b, w2off[i], base + 16u * 64u * I);
     }
+    if constexpr (!UBLK) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
-        dma16s(sb[s] + kTile * t, soff[s][k],
-               base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
+        for (int k = 0; k < 2; ++k)
+          dma16s(sb[s] + kTile * t, soff[s][k],
+                 base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
+    }
+  }
+  // copies of U block b (128 bytes of each row) into block buffer ub
+  __device__ __forceinline__ void issue_u(int b, int ub) {
+    const uint32_t base = lds0 + 16u * (UB0 + ub * kUBlkChunks + wave * 256);
+    const uint16_t* src = sb[0] + (size_t)kVB * b;
+#pragma unroll
+    for (int i = 0; i < OPS_U; ++i) dma16s(src, uoff[i], base + 16u * 64u * i);
+  }
+  // the same for the short last block: each piece's ids clamped into the row
+  __device__ __forceinline__ void issue_u_ragged(int b, int ub) {
+    const uint32_t base = lds0 + 16u * (UB0 + ub * kUBlkChunks + wave * 256);
+#pragma unroll
+    for (int i = 0; i < OPS_U; ++i) {
+      const int rl = 8 * i + (lane >> 3);
+      const int c = (lane & 7) ^ ((rl >> 1) & 7);
+      int v = kVB * b + 8 * c;
+      if (v > g.V - 8) v = g.V - 8;
+      dma16s(sb[0], uoff[i] + (uint32_t)(v - 8 * c) * 2u, base + 16u * 64u * i);
+    }
   }
   // the same for the short last tile: clamp each lane's source into the arrays
   __device__ __forceinline__ void issue_ragged(int t, int stg) {
@@ -278,15 +324,17 @@ struct SweepTask {
       const uint32_t off = (m < 32 && c < CH) ? (uint32_t)(v * g.r + 8 * c) * 2u : 0u;
       if (BIAS && I < NI) dma16s(g.W2t, off, base + 16u * 64u * I);
     }
+    if constexpr (!UBLK) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        int v = kTile * t + sx[k];
-        if (v > g.V - 8) v = g.V - 8;
-        dma16s(sb[s], soff[s][k] + (uint32_t)(v - sx[k]) * 2u,
-               base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
-      }
+        for (int k = 0; k < 2; ++k) {
+          int v = kTile * t + sx[k];
+          if (v > g.V - 8) v = g.V - 8;
+          dma16s(sb[s], soff[s][k] + (uint32_t)(v - sx[k]) * 2u,
+                 base + 16u * (w2_tile_chunks(CH) + s * stream_tile_chunks() + wave * 128 + 64 * k));
+        }
+    }
   }
   // wait until at most `left` (0 .. D-1) tiles' copies are still in flight (loads complete
   // in order)
@@ -327,14 +375,29 @@ struct SweepTask {
       const int m = P / RS, c = P - m * RS;
       w2off[i] = (m < 32 && c < CH) ? (uint32_t)(tile_row_of_vocab(m) * g.r + 8 * c) * 2u : 0u;
     }
+    if constexpr (UBLK) {
+      //   U block copy i: lane -> row 8i + lane / 8 of the wave, piece (lane & 7) xor the row's
+      //   swizzle, so that the 64 lanes land on ublk_pos order in LDS
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int rl = 16 * k + (lane >> 2);
-      int rr = group_row0 + wave * 32 + rl;
-      if (rr >= nrows) rr = nrows - 1;
-      sx[k] = 8 * ((lane & 3) ^ ((rl >> 2) & 3));  // element offset inside the 32-id slice
+      for (int i = 0; i < OPS_U; ++i) {
+        const int rl = 8 * i + (lane >> 3);
+        int rr = group_row0 + wave * 32 + rl;
+        if (rr >= nrows) rr = nrows - 1;
+        const int c = (lane & 7) ^ ((rl >> 1) & 7);
+        uoff[i] = (Epi::srow(ep, 0, rr) + (uint32_t)(8 * c)) * 2u;
+      }
+      u_idx = UB0 + wave * 256 + n * 8;
+      u_sw = (n >> 1) & 7;
+    } else {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) soff[s][k] = (Epi::srow(ep, s, rr) + (uint32_t)sx[k]) * 2u;
+      for (int k = 0; k < 2; ++k) {
+        const int rl = 16 * k + (lane >> 2);
+        int rr = group_row0 + wave * 32 + rl;
+        if (rr >= nrows) rr = nrows - 1;
+        sx[k] = 8 * ((lane & 3) ^ ((rl >> 2) & 3));  // element offset inside the 32-id slice
+#pragma unroll
+        for (int s = 0; s < NS; ++s) soff[s][k] = (Epi::srow(ep, s, rr) + (uint32_t)sx[k]) * 2u;
+      }
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) sb[s] = Epi::sbase(ep, s);
@@ -356,7 +419,10 @@ struct SweepTask {
     // the first tile goes out before anything else (it depends on nothing the B rows or
     // the epilogue state need); the rest of the pipeline fills once they are in, so the
     // first step waits for one tile rather than D
-    if (t0 < t1) issue(t0, 0);
+    if (t0 < t1) {
+      issue(t0, 0);
+      if constexpr (UBLK) issue_u(b0, 0);
+    }
   }
 
   // matrix-core chain of the tile in stage stg, seeded with its U slice
@@ -382,14 +448,37 @@ struct SweepTask {
     }
   }
 
+  // the one-stream form: U from block buffer ub, half HALF of the block
+  template <int HALF>
+  __device__ __forceinline__ void mma_ublk(int stg, int ub, f32x16& acc, const bf16x8 (&bh)[NKS],
+                                           const bf16x8 (&bl)[SPLIT ? NKS : 1]) {
+    const uint4* up = lds + u_idx + ub * kUBlkChunks;
+    float u[16];
+    widen8(up[(4 * HALF + h) ^ u_sw], u);
+    widen8(up[(4 * HALF + 2 + h) ^ u_sw], u + 8);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = u[j];
+    if (!BIAS) return;
+    const uint4* ab = lds + stg * SCH + a_idx;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 a = as_bf16x8(ab[2 * ks]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc, 0, 0, 0);
+      if (SPLIT) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[SPLIT ? ks : 0], acc, 0, 0, 0);
+    }
+  }
+
   // the B rows, the streamed tiles and the epilogue of the prepared group
   __device__ __forceinline__ void run() {
-    bf16x8 bh[NKS];  // B operand (filled once the first tiles are in flight)
-    bf16x8 bl[SPLIT ? NKS : 1];
-    typename Epi::State st;
+    if constexpr (UBLK)
+      run_ublk();
+    else
+      run_tiles();
+  }
 
-    // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row; from the packed
-    // copy when the epilogue has one (coalesced; rows past the end read padding)
+  // B operand in registers: k = 16*ks + 8*h .. + 8 of this lane's row; from the packed
+  // copy when the epilogue has one (coalesced; rows past the end read padding)
+  __device__ __forceinline__ void load_b(bf16x8 (&bh)[NKS], bf16x8 (&bl)[SPLIT ? NKS : 1]) {
     const uint4* bpk = SPLIT ? nullptr : Epi::bpack(ep);
     if (!BIAS) {
 #pragma unroll
@@ -419,6 +508,76 @@ struct SweepTask {
         if (SPLIT) bl[SPLIT ? ks : 0] = as_bf16x8(lo);
       }
     }
+  }
+
+  // The sweep without the bias: block b + 1's U rows go out when block b starts (one block
+  // ahead).  A block's first half waits for its own rows; its second half lets the next
+  // block's copies stay in flight.  (The W2t calls are kept in the form the bias needs:
+  // without it they issue nothing and the matrix chain is skipped.)
+  __device__ __forceinline__ void run_ublk() {
+    bf16x8 bh[NKS];
+    bf16x8 bl[SPLIT ? NKS : 1];
+    typename Epi::State st;
+    load_b(bh, bl);
+    Epi::init(ep, st, live ? row : -1);
+    // a wait the compiler sees: the first block's copies, the B rows and the epilogue
+    // state have landed
+    __builtin_amdgcn_s_waitcnt(0);
+    f32x16 accA, accB;
+    uint4 xz[2];
+    xz[0] = xz[1] = make_uint4(0, 0, 0, 0);
+    for (int b = b0; b < bp1; ++b) {
+      const int ub = (b - b0) & 1;
+      const bool more = b + 1 < bp1;
+      // -- first half of block b (stage 0); epilogue of the second half of block b - 1
+      if (b > b0) {
+        Epi::refresh(ep, st, b - 1, row);
+        vm_wait<0>();
+      }
+      stage_barrier();
+      issue(2 * b + 1, 1);
+      if (more) issue_u(b + 1, ub ^ 1);
+      mma_ublk<0>(0, ub, accA, bh, bl);
+      if (b > b0) Epi::template tile<1, false>(ep, st, accB, xz, b - 1, row, owner);
+      // -- second half of block b (stage 1); epilogue of its first half
+      if (more)
+        vm_wait<OPS_U>();
+      else
+        vm_wait<0>();
+      stage_barrier();
+      if (more) issue(2 * b + 2, 0);
+      mma_ublk<1>(1, ub, accB, bh, bl);
+      Epi::template tile<0, false>(ep, st, accA, xz, b, row, owner);
+    }
+    if (bp1 > b0) {
+      Epi::refresh(ep, st, bp1 - 1, row);
+      Epi::template tile<1, false>(ep, st, accB, xz, bp1 - 1, row, owner);
+    }
+    if (ragged) {  // the short last block, unpipelined
+      const int b = b1 - 1;
+      vm_wait<0>();
+      __syncthreads();
+      issue_ragged(2 * b, 0);
+      issue_ragged(2 * b + 1, 1);
+      issue_u_ragged(b, 0);
+      vm_wait<0>();
+      __syncthreads();
+      mma_ublk<0>(0, 0, accA, bh, bl);
+      Epi::template tile<0, true>(ep, st, accA, xz, b, row, owner);
+      mma_ublk<1>(1, 0, accB, bh, bl);
+      Epi::refresh(ep, st, b, row);
+      Epi::template tile<1, true>(ep, st, accB, xz, b, row, owner);
+    }
+    vm_wait<0>();
+    Epi::finish(ep, st, row, owner, range);
+  }
+
+  // The sweep with per-tile streamed slices (the bias contraction, or two streams).
+  __device__ __forceinline__ void run_tiles() {
+    bf16x8 bh[NKS];  // B operand (filled once the first tiles are in flight)
+    bf16x8 bl[SPLIT ? NKS : 1];
+    typename Epi::State st;
+    load_b(bh, bl);
     Epi::init(ep, st, live ? row : -1);
 
     // a wait the compiler sees: every load issued so far (first tile, B rows, epilogue
@@ -549,7 +708,7 @@ template <int NKS, bool SPLIT, int NSTAGE, class Epi>
 inline void launch_sweep_nks(const SweepGeom& g, const typename Epi::Params& p, hipStream_t s,
                              hipEvent_t ev0, hipEvent_t ev1) {
   auto kern = sweep_kernel<NKS, SPLIT, NSTAGE, Epi>;
-  const size_t sh = sweep_lds_bytes(g.r, Epi::kStreams, NSTAGE);
+  const size_t sh = sweep_lds_bytes(g.r, Epi::kStreams, NSTAGE, epi_has_bias<Epi>::value);
   static std::atomic<uint64_t> lds_raised{0};
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)sh, lds_raised);
   if (ev0 && ev1)
