@@ -5,8 +5,9 @@ A step is one whole cycle of the hot path on the headline workload (R=256 reques
 draft positions, V=151936, r=256, d=4096, bf16 operands with fp32 softmax):
   dspark_draft_markov  (gamma vocabulary sweeps + combines)
   dspark_schedule      (Algorithm 1 with the early-stop break)
-  dspark_verify        (rejection sampling of the scheduled prefixes, c*)
-  next anchors         (each request's last emitted token starts its next cycle)
+  dspark_verify        (rejection sampling of the scheduled prefixes, c*; it also writes
+                        each request's last emitted token, the next cycle's anchor, into
+                        the x0 the next draft call reads)
 All inputs are seeded synthetic tensors already resident in device memory.  Cycle t uses
 random-counter cycle t and the anchors cycle t-1 emitted, so the drafted tokens and the
 scheduled lengths change from cycle to cycle.  The target logits that verification reads are
@@ -15,8 +16,9 @@ row), built for every cycle on an untimed first pass over the same chain of cycl
 timed pass reproduces that chain token for token (checked).
 
 Printed: one JSON line with the metric, the roofline of the dominant kernel (the draft
-sweep, timed live with HIP events around each of its launches), and the CPU oracle timed on
-a bounded sample of the same workload.
+sweep, timed live with HIP events attached to its launches), the read rate a kernel that only
+reads sustains on the same bytes (dspark_read_probe, the practical ceiling beside the
+published peak), and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
