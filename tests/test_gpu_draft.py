@@ -103,6 +103,10 @@ PAR_CASES = [
     ("par-c3-law", "c3", dict(R=40, gamma=4, V=8192, d=512)),
     ("par-c2-R150", "c2", dict(R=150, gamma=3, V=3000, r=64, d=256)),
     ("par-c2-r16", "c2", dict(R=70, gamma=3, V=1024, r=16, d=64)),
+    # below one 64-id block (only the short block, no pipelined block), and three whole
+    # blocks plus a short one
+    ("par-V40", "c2", dict(R=5, gamma=2, V=40, r=16, d=64)),
+    ("par-V200", "c2", dict(R=33, gamma=3, V=200, r=32, d=64)),
 ]
 
 
