@@ -8,9 +8,10 @@
 //   prep    one workgroup: exclusive scans of ell; list A = (q, j) for j = 1..ell_q + 1
 //           (every row whose target normaliser is needed, the bonus row included), list B
 //           = (q, j) for j = 1..ell_q (every verified position);
-//   lse     each list-A row in items of 256 blocks of 64 ids (a persistent grid walks the
-//           items; loads coalesced, 8 lanes per block): (max, sum exp) of the target
-//           logits; on the bonus row also the first level of the bonus sample (stream 5);
+//   lse     each list-A row in wave items of 64 blocks of 64 ids (a grid of at most four
+//           workgroups per CU walks the items, whose count is known on the device only;
+//           loads coalesced, 8 lanes per block): (max, sum exp) of the target logits; on
+//           the bonus row also the first level of the bonus sample (stream 5);
 //   decide  one wave per request, one lane per position: merges the lse items into the
 //           target normalisers (and the bonus block), then the acceptance tests
 //           u < p_j(x_j)/q_j(x_j) (stream 2), the first rejection j*, the accepted tokens;
@@ -19,7 +20,8 @@
 //           residual max(0, p - q) per 64-id block with its first-level Gumbel score
 //           (stream 3);
 //   final   one workgroup of four waves per request: c* for every verified row, then the
-//           second level of the correction (stream 4) or of the bonus (stream 6).
+//           second level of the correction (stream 4) or of the bonus (stream 6), written
+//           as the last emitted token (and, when asked, as the next cycle's anchor).
 #include <type_traits>
 
 #include "dev.h"
@@ -788,7 +790,7 @@ static int verify_run(int R, int gamma, int V, int r, const void* target_, const
 
   verify_prep_kernel<<<1, 1024, 0, stream>>>(R, gamma, ell, ws, status);
   {
-    // persistent grid over the items of list A (its length is known on the device only)
+    // a grid-stride walk over the items of list A (its length is known on the device only)
     const int wgs = (R * (gamma + 1) * lse_witems(V) + 3) / 4, cap = 4 * device_cus();
     verify_lse_kernel<T><<<wgs < cap ? wgs : cap, kLseThreads, 0, stream>>>(
         R, gamma, V, target, ell, ws, seed, cycle);
