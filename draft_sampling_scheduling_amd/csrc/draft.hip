@@ -213,38 +213,45 @@ __device__ void combine_request(CombineLds& sm, int q, int R, int gamma, int V, 
   // second level: the winning block's 64 logits, the k sum split over the waves in
   // 8-element chunks
   const int v = Bk * kVB + lane;
-  const float u = (wave == 0 && v < V) ? ld<T>(U, rk * V + v) : 0.0f;
+  const int vc = v < V ? v : V - 1;  // lanes past V load row V-1 and are masked below
+  // zh[rk] is independent of the block: in flight with the rest
+  const float zh_k = wave == 0 ? zh[rk] : 0.0f;
   float part = 0.0f;
   float gn = 0.0f;  // in-block Gumbel noise (wave 0), formed while the block's rows load
-  if (v < V) {
-    if (BIAS) {
-      const T* wr = W2t + (size_t)v * r;
-      // r <= 256: at most 8 chunks per wave, all loads in flight together
-      float a[8][8], bv[8][8];
+  T ur = T();       // wave 0: U_k at this lane's id, kept raw until after the barrier so
+                    // that the wait for it does not hold back the row loads issued before it
+  if (BIAS) {
+    const T* wr = W2t + (size_t)vc * r;
+    // r <= 256: at most 8 chunks per wave, all loads in flight together
+    float a[8][8], bv[8][8];
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int ch = wave + kCombineWaves * it < r / 8 ? wave + kCombineWaves * it : 0;
-        ld8<T>(wr + ch * 8, a[it]);
-        if (RNN) {
+    for (int it = 0; it < 8; ++it) {
+      const int ch = wave + kCombineWaves * it < r / 8 ? wave + kCombineWaves * it : 0;
+      ld8<T>(wr + ch * 8, a[it]);
+      if (RNN) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) bv[it][j] = orow[(size_t)q * r + ch * 8 + j];
-        } else {
-          ld8<T>(e + ch * 8, bv[it]);
-        }
+        for (int j = 0; j < 8; ++j) bv[it][j] = orow[(size_t)q * r + ch * 8 + j];
+      } else {
+        ld8<T>(e + ch * 8, bv[it]);
       }
-      if (wave == 0) gn = gumbel_of(Rng(seed, cycle).word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v));
-#pragma unroll
-      for (int it = 0; it < 8; ++it)
-        if (wave + kCombineWaves * it < r / 8)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) part = fmaf(bv[it][j], a[it][j], part);
-    } else if (wave == 0) {
+    }
+    if (wave == 0) {
+      ur = U[rk * V + vc];
       gn = gumbel_of(Rng(seed, cycle).word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v));
     }
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+      if (wave + kCombineWaves * it < r / 8)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) part = fmaf(bv[it][j], a[it][j], part);
+  } else if (wave == 0) {
+    ur = U[rk * V + vc];
+    gn = gumbel_of(Rng(seed, cycle).word(kStreamDraftIn, (uint32_t)q, k, (uint32_t)v));
   }
   sm.dotp[wave][lane] = part;
   __syncthreads();
   if (wave == 0) {
+    const float u = ld<T>(&ur, 0);
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < kCombineWaves; ++i) acc += sm.dotp[i][lane];
@@ -252,12 +259,13 @@ __device__ void combine_request(CombineLds& sm, int q, int R, int gamma, int V, 
     float score = (v < V) ? l + gn : -INFINITY;
     int idx = v;
     wave_argmax(score, idx);  // every lane of the wave holds the pick
-    if (sizeof(T) == 2 && !RNN && bpack && lane < r / 8)
-      // W1[x_k] in the next sweep's packed order, one 16-byte chunk per lane
-      bpack[bpack_index(q, lane, r / 16)] =
-          reinterpret_cast<const uint4*>(W1 + (size_t)idx * r)[lane];
+    // W1[x_k] in the next sweep's packed order, one 16-byte chunk per lane: loaded here,
+    // stored after the outputs
+    const bool pack = sizeof(T) == 2 && !RNN && bpack && lane < r / 8;
+    const uint4 prow_next = pack ? reinterpret_cast<const uint4*>(W1 + (size_t)idx * r)[lane]
+                                 : make_uint4(0, 0, 0, 0);
     const float lx = __shfl(l, idx - Bk * kVB, kWave);
-    float z = zh[rk];
+    float z = zh_k;
 #pragma unroll
     for (int i = 0; i < kCombineWaves; ++i) z += sm.zred[i];
     if (lane == 0) {
@@ -273,6 +281,7 @@ __device__ void combine_request(CombineLds& sm, int q, int R, int gamma, int V, 
       lse[rk] = M + __logf(S);
       logit_x[rk] = lx;
     }
+    if (pack) bpack[bpack_index(q, lane, r / 16)] = prow_next;
   }
 }
 
