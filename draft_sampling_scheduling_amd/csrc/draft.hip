@@ -261,8 +261,11 @@ __device__ void combine_request(CombineLds& sm, int q, int R, int gamma, int V, 
     wave_argmax(score, idx);  // every lane of the wave holds the pick
     // W1[x_k] in the next sweep's packed order, one 16-byte chunk per lane: loaded here,
     // stored after the outputs
+    // (the row index is clamped: only NaN logits can make a lane past V win, and the token
+    // itself then raises the fault bit when the next position reads it)
     const bool pack = sizeof(T) == 2 && !RNN && bpack && lane < r / 8;
-    const uint4 prow_next = pack ? reinterpret_cast<const uint4*>(W1 + (size_t)idx * r)[lane]
+    const int gidx = idx < V ? idx : V - 1;
+    const uint4 prow_next = pack ? reinterpret_cast<const uint4*>(W1 + (size_t)gidx * r)[lane]
                                  : make_uint4(0, 0, 0, 0);
     const float lx = __shfl(l, idx - Bk * kVB, kWave);
     float z = zh_k;
