@@ -268,7 +268,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (this build shows one GPU's share of the path); "
+        print(f"bench.py measures one GPU only (the path as one GPU runs its share of a batch); "
               f"--gpus {args.gpus} / WORLD_SIZE={world} is not supported", file=sys.stderr)
         sys.exit(2)
 
